@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA/HCA attention hot path on one MI355X.
+
+A step is one layer's pass over one batch of new tokens: compress the entries the
+tokens complete, write the tokens into the sliding-window cache, score and select
+entries with the lightning indexer (CSA), attend.  The headline workload is
+DeepSeek-V4-Pro CSA decode at 65,536 tokens of context: batch 32, 128 query heads
+of dim 512 on one shared KV head, 64 x 128 indexer with fp8 keys, top-1,024,
+128-token window, per-head sink.  Synthetic seeded inputs; distinct per-layer caches
+are rotated so that the 256 MB last-level cache cannot serve repeated reads.
+
+Prints one JSON line.  Extra measurements (HCA decode at 1M context, the Flash fp8
+decode at 1M, per-call times) ride in the same line under "extra".
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+METRIC = "CSA/HCA decode tokens/s + indexer HBM GB/s at 65K/1M ctx; % of roofline"
+
+
+def algorithmic_costs(wl):
+    """Bytes / flops each C-ABI call of one step must move / do at minimum.
+
+    indexer: each visible key once (Di bytes fp8 + 4-byte scale, or 2*Di bf16), the
+             indexer queries and weights, the selected indices.
+    attend:  each attended row once per query token (1 KB bf16 or 512 B + 32 B scales
+             fp8), q in (bf16) and out (bf16); flops 4 * H * rows * 512 per token.
+    compress: raw kv + logits of the new tokens (2 KB per token) and the new rows.
+    """
+    rows = wl.B * wl.Tq
+    E = wl.E
+    key_b = (wl.Di + 4) if wl.idx_dtype == "fp8" else 2 * wl.Di
+    kv_row_b = (wl.D + 4 * wl.D // wl.kv_scale_block) if wl.kv_dtype == "fp8" else 2 * wl.D
+    c = {}
+    if wl.mode == "csa":
+        c["index_bytes"] = rows * (E * key_b + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4)
+        c["index_flops"] = rows * E * wl.Hi * wl.Di * 2
+        att_rows = wl.topk + wl.W
+    else:
+        att_rows = E + wl.W
+    c["attend_bytes"] = rows * (att_rows * kv_row_b + 2 * wl.H * wl.D * 2)
+    c["attend_flops"] = rows * 4 * wl.H * att_rows * wl.D
+    new_entries = wl.E - wl.n_entries(wl.N - wl.Tq)
+    raw = (new_entries - 1) * wl.stride + wl.window if new_entries else 0
+    c["compress_bytes"] = wl.B * (raw * 2 * wl.D * 2 + new_entries * kv_row_b + wl.Tq * wl.D * 4)
+    return c
+
+
+def build_layers(wl, n_layers, device, torch, out_dtype):
+    import csa_inputs as ci
+    from compressed_attention_long_amd.step import LayerStep
+    steps = []
+    for i in range(n_layers):
+        t, meta = ci.step_tensors(wl, device, seed=ci.seed_for(wl.name) + 7919 * i)
+        steps.append(LayerStep(wl, t, meta, out_dtype=out_dtype))
+    torch.cuda.synchronize()
+    return steps
+
+
+def layer_bytes(wl):
+    kv_row_b = (wl.D + 4 * wl.D // wl.kv_scale_block) if wl.kv_dtype == "fp8" else 2 * wl.D
+    key_b = ((wl.Di + 4) if wl.idx_dtype == "fp8" else 2 * wl.Di) if wl.mode == "csa" else 0
+    return wl.B * wl.E * (kv_row_b + key_b + (4 if wl.mode == "csa" else 0))
+
+
+def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layers=30):
+    """Run `steps_n` timed steps rotating over distinct layers; return timings (ms)."""
+    n_layers = max(2, min(max_layers, math.ceil(min_cache_bytes / max(layer_bytes(wl), 1))))
+    layers = build_layers(wl, n_layers, "cuda", torch, torch.bfloat16)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        layers[i % n_layers].run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps_n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps_n):
+        L = layers[i % n_layers]
+        e = ev[i]
+        e[0].record(stream)
+        L.compress()
+        e[1].record(stream)
+        if wl.mode == "csa":
+            L.index()
+        e[2].record(stream)
+        L.attend()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps_n
+    per = {"compress": [], "index": [], "attend": [], "step_gpu": []}
+    for e in ev:
+        per["compress"].append(e[0].elapsed_time(e[1]))
+        per["index"].append(e[1].elapsed_time(e[2]))
+        per["attend"].append(e[2].elapsed_time(e[3]))
+        per["step_gpu"].append(e[0].elapsed_time(e[3]))
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    out = {k: sum(v) / len(v) for k, v in per.items()}
+    out["step_gpu_median"] = med(per["step_gpu"])
+    out["wall_ms_per_step"] = wall
+    out["layers"] = n_layers
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the same workload: whole decode steps of
+    single sequences (compress the new entry, index, select, attend), as many as fit
+    in about `budget_s` seconds of host time.  Reported in tokens/s."""
+    import numpy as np
+    import csa_inputs as ci
+    from oracle import csa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t, meta = ci.step_tensors(wl, "cpu")
+    f = O.rope_inv_freq(160000.0, wl.R)
+    E = wl.E
+    ent_pos = O.entry_positions(wl.pos0, E, wl.window, wl.stride)
+    win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
+    n_done = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b = n_done % wl.B
+        qp = int(t["q_pos"][b, 0])
+        new, _ = O.compress(t["kv_raw"][b].double().numpy(), t["z_raw"][b].double().numpy(), wl.window,
+                            wl.stride, wl.pos0 + meta["E_pre"] * wl.stride, f)
+        kv = t["kv_cache"][b].double().numpy() if wl.kv_dtype == "bf16" else O.fp8_block_dequantize(
+            t["kv_cache"][b].numpy(), t["kv_cache_scale"][b].numpy(), wl.kv_scale_block)
+        kv[meta["E_pre"]:] = new[:meta["n_new_entries"]]
+        win = t["win_cache"][b].double().numpy()
+        win[meta["win_first_new"]:] = O.rope(t["kv_raw"][b, -meta["new_tok"]:].double().numpy(),
+                                             win_pos[meta["win_first_new"]:], f)
+        if wl.mode == "csa":
+            keys = t["k_idx"][b].double().numpy() if wl.idx_dtype == "bf16" else O.fp8_block_dequantize(
+                t["k_idx"][b].numpy(), t["k_idx_scale"][b].numpy(), wl.Di)
+            O.csa_query(t["q"][b, 0].double().numpy(), qp, t["q_idx"][b, 0].double().numpy(),
+                        t["w"][b, 0].double().numpy(), kv, ent_pos, keys, win, win_pos, t["sink"].double().numpy(),
+                        wl.topk, 1 / math.sqrt(wl.D), f, wl.W)
+        else:
+            O.hca_query(t["q"][b, 0].double().numpy(), qp, kv, ent_pos, win, win_pos, t["sink"].double().numpy(),
+                        1 / math.sqrt(wl.D), f, wl.W)
+        n_done += 1
+    dt = time.perf_counter() - t0
+    return {"value": n_done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_done} single-sequence decode steps of {wl.name} (sequences cycled over the batch of "
+                      f"{wl.B}; fp64 NumPy oracle; {dt:.1f} s of host time)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v4pro_csa_decode_65k")
+    ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8",
+                    help="comma-separated extra workloads measured into 'extra' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs the path on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+    import csa_inputs as ci
+    from compressed_attention_long_amd import _lib
+    _lib.load()                       # fails loudly when the HIP library is missing
+    assert torch.cuda.is_available(), "no GPU visible"
+
+    wl = ci.WORKLOADS[args.workload]
+    print(f"[bench] workload {wl.name}: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
+          flush=True)
+    tm = time_workload(wl, args.steps, args.warmup, torch)
+    costs = algorithmic_costs(wl)
+    ms = tm["wall_ms_per_step"]
+    tokens = wl.B * wl.Tq
+    value = tokens / (ms / 1e3)
+    calls = {}
+    for name in ("compress", "index", "attend"):
+        if name == "index" and wl.mode != "csa":
+            continue
+        t_ms = tm[name]
+        d = {"ms": t_ms}
+        if f"{name}_bytes" in costs:
+            d["GB_per_s"] = costs[f"{name}_bytes"] / (t_ms * 1e-3) / 1e9
+            d["hbm_frac"] = d["GB_per_s"] / HBM_PEAK_GBS
+        if f"{name}_flops" in costs:
+            d["TFLOP_per_s"] = costs[f"{name}_flops"] / (t_ms * 1e-3) / 1e12
+            d["mfma_frac"] = d["TFLOP_per_s"] / BF16_PEAK_TFLOPS
+        calls[name] = d
+    # dominant call of the step
+    dom = max(calls, key=lambda k: calls[k]["ms"])
+    if dom == "attend":
+        roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": calls[dom]["mfma_frac"], "traffic": None,
+                "kernel": "csa_attend (k_attend + k_attend_combine)",
+                "hbm_GB_per_s": calls[dom]["GB_per_s"], "hbm_frac": calls[dom]["hbm_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": calls[dom]["hbm_frac"], "traffic": None,
+                "kernel": "csa_index_topk (k_index_scores + k_topk)" if dom == "index" else "csa_compress"}
+    extra = {"calls": calls, "step_gpu_ms": tm["step_gpu"], "step_gpu_median_ms": tm["step_gpu_median"],
+             "layers_rotated": tm["layers"], "pages_config_context": {
+                 "layers": 61, "csa_layers": 30, "hca_layers": 31, "heads": 128, "head_dim": 512,
+                 "index_topk": 1024, "sliding_window": 128}}
+    for name in [x for x in args.extra.split(",") if x]:
+        w2 = ci.WORKLOADS[name]
+        print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
+        t2 = time_workload(w2, max(10, args.steps // 2), args.warmup, torch)
+        c2 = algorithmic_costs(w2)
+        e2 = {"ms_per_step": t2["wall_ms_per_step"], "tokens_per_s": w2.B * w2.Tq / (t2["wall_ms_per_step"] / 1e3),
+              "attend_ms": t2["attend"], "attend_TFLOP_per_s": c2["attend_flops"] / (t2["attend"] * 1e-3) / 1e12,
+              "attend_GB_per_s": c2["attend_bytes"] / (t2["attend"] * 1e-3) / 1e9, "compress_ms": t2["compress"]}
+        if w2.mode == "csa":
+            e2["index_ms"] = t2["index"]
+            e2["index_GB_per_s"] = c2["index_bytes"] / (t2["index"] * 1e-3) / 1e9
+        extra[name] = e2
+    base = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        base = cpu_baseline(wl, args.cpu_budget)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; fp8 indexer keys; caches rotated over distinct layers)",
+        "config": {"workload": wl.name, "batch": wl.B, "context": wl.N, "query_heads": wl.H, "head_dim": wl.D,
+                   "index_heads": wl.Hi, "index_dim": wl.Di, "topk": wl.topk, "window": wl.W,
+                   "kv_dtype": wl.kv_dtype, "index_key_dtype": wl.idx_dtype, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": base,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+// C ABI of the CSA/HCA hot path: host-side validation, workspace carving, launches.
+// Validation never calls into HIP, so a failed call has no side effects and the
+// checks run on machines without a GPU.
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return CSA_OK;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+// Common checks of a cache descriptor.  `reads` = the call reads rows (needs n_valid).
+int check_cache(const csa_cache_t* c, const char* name, bool reads) {
+  REQUIRE(c != nullptr, CSA_EINVAL, "%s: cache descriptor is NULL", name);
+  REQUIRE(c->data != nullptr, CSA_EINVAL, "%s: data is NULL", name);
+  REQUIRE(c->pos0 != nullptr, CSA_EINVAL, "%s: pos0 is NULL", name);
+  REQUIRE(!reads || c->n_valid != nullptr, CSA_EINVAL, "%s: n_valid is NULL", name);
+  REQUIRE(c->cap >= 1, CSA_EINVAL, "%s: cap must be >= 1 (got %d)", name, c->cap);
+  REQUIRE(c->C >= 1, CSA_EINVAL, "%s: C must be >= 1 (got %d)", name, c->C);
+  REQUIRE(c->window >= 1 && c->stride >= 1, CSA_EINVAL, "%s: window and stride must be >= 1 (got %d, %d)",
+          name, c->window, c->stride);
+  REQUIRE(c->dtype == CSA_BF16 || c->dtype == CSA_FP8_E4M3, CSA_ENOTSUP, "%s: dtype %d not supported", name,
+          c->dtype);
+  REQUIRE(aligned(c->data, 16), CSA_EINVAL, "%s: data must be 16-byte aligned", name);
+  if (c->dtype == CSA_FP8_E4M3) {
+    REQUIRE(c->scales != nullptr, CSA_EINVAL, "%s: fp8 cache needs scales", name);
+    REQUIRE(c->scale_block >= 1 && c->C % c->scale_block == 0, CSA_EINVAL,
+            "%s: scale_block %d must divide C %d", name, c->scale_block, c->C);
+  }
+  return CSA_OK;
+}
+
+int check_rope(const double* inv_freq, int rope_dim, int C) {
+  REQUIRE(rope_dim >= 0 && rope_dim % 2 == 0 && rope_dim <= C, CSA_EINVAL,
+          "rope_dim must be even and in [0, %d] (got %d)", C, rope_dim);
+  REQUIRE(rope_dim == 0 || inv_freq != nullptr, CSA_EINVAL, "inv_freq is NULL");
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+int csa_abi_version(void) { return 1; }
+
+int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_seq, int B, int T_raw,
+                 int first_row, int n_new, const csa_cache_t* out, const double* inv_freq, int rope_dim,
+                 hipStream_t stream) {
+  int rc = check_cache(out, "out", false);
+  if (rc) return rc;
+  REQUIRE(B >= 0 && n_new >= 0, CSA_EINVAL, "B and n_new must be >= 0 (got %d, %d)", B, n_new);
+  if (B == 0 || n_new == 0) return ok();
+  REQUIRE(kv != nullptr, CSA_EINVAL, "kv is NULL");
+  REQUIRE(logits != nullptr || out->window == 1, CSA_EINVAL, "logits is NULL (allowed only when window == 1)");
+  const int C = out->C;
+  REQUIRE(C % 8 == 0 && C <= 2048 && (256 % (C / 8)) == 0, CSA_ENOTSUP,
+          "C must be 8 times a divisor of 256 (got %d)", C);
+  REQUIRE(first_row >= 0 && (int64_t)first_row + n_new <= out->cap, CSA_EINVAL,
+          "rows [%d, %d) exceed cap %d", first_row, first_row + n_new, out->cap);
+  REQUIRE((int64_t)T_raw >= (int64_t)(n_new - 1) * out->stride + out->window, CSA_EINVAL,
+          "T_raw %d is too short for %d rows of window %d, stride %d", T_raw, n_new, out->window, out->stride);
+  REQUIRE(ld_tok >= C && ld_tok % 8 == 0, CSA_EINVAL, "ld_tok must be >= C and a multiple of 8 (got %lld)",
+          (long long)ld_tok);
+  REQUIRE(B == 1 || (ld_seq >= (int64_t)T_raw * ld_tok && ld_seq % 8 == 0), CSA_EINVAL,
+          "ld_seq must be >= T_raw * ld_tok and a multiple of 8 (got %lld)", (long long)ld_seq);
+  REQUIRE(aligned(kv, 16) && (logits == nullptr || aligned(logits, 16)), CSA_EINVAL,
+          "kv and logits must be 16-byte aligned");
+  if (out->dtype == CSA_FP8_E4M3) {
+    const int sb = out->scale_block;
+    REQUIRE(sb % 8 == 0 && sb <= 512 && ((sb / 8) & (sb / 8 - 1)) == 0, CSA_ENOTSUP,
+            "fp8 scale_block must be 8 times a power of two, at most 512 (got %d)", sb);
+  }
+  rc = check_rope(inv_freq, rope_dim, C);
+  if (rc) return rc;
+  csa::CompressArgs a{};
+  a.kv = kv;
+  a.logits = out->window == 1 ? nullptr : logits;
+  a.ld_tok = ld_tok;
+  a.ld_seq = ld_seq;
+  a.B = B;
+  a.T_raw = T_raw;
+  a.first_row = first_row;
+  a.n_new = n_new;
+  a.out = out->data;
+  a.scales = out->scales;
+  a.pos0 = out->pos0;
+  a.dtype = out->dtype;
+  a.cap = out->cap;
+  a.C = C;
+  a.scale_block = out->scale_block;
+  a.window = out->window;
+  a.stride = out->stride;
+  a.inv_freq = inv_freq;
+  a.rope_dim = rope_dim;
+  hipError_t e = csa::launch_compress(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "compress launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t csa_index_topk_workspace_bytes(int B, int Tq, int Hi, int cap, int topk) {
+  (void)Hi;
+  (void)topk;
+  if (B <= 0 || Tq <= 0 || cap <= 0) return 0;
+  return (size_t)B * Tq * cap * sizeof(float) + 256;
+}
+
+int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int B, int Tq, int Hi,
+                   const csa_cache_t* keys, int topk, int32_t* idx_out, float* scores_out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_cache(keys, "keys", true);
+  if (rc) return rc;
+  REQUIRE(B >= 0 && Tq >= 0, CSA_EINVAL, "B and Tq must be >= 0");
+  REQUIRE(topk >= 1 && topk <= keys->cap, CSA_EINVAL, "topk must be in [1, cap=%d] (got %d)", keys->cap, topk);
+  if (B == 0 || Tq == 0) return ok();
+  REQUIRE(q_idx && w && q_pos && idx_out, CSA_EINVAL, "q_idx, w, q_pos and idx_out must be non-NULL");
+  REQUIRE(Hi >= 1 && Hi <= 64, CSA_ENOTSUP, "Hi must be in [1, 64] (got %d)", Hi);
+  REQUIRE(keys->C == 128, CSA_ENOTSUP, "indexer key dim must be 128 (got %d)", keys->C);
+  REQUIRE(keys->dtype == CSA_BF16 || keys->scale_block == keys->C, CSA_ENOTSUP,
+          "fp8 indexer keys need one scale per key (scale_block == C)");
+  REQUIRE(aligned(q_idx, 16), CSA_EINVAL, "q_idx must be 16-byte aligned");
+  const int64_t rows = (int64_t)B * Tq;
+  REQUIRE(rows <= 0x7fffffff && (keys->cap + 1023) / 1024 <= 65535, CSA_ENOTSUP, "problem too large");
+  float* scores = scores_out;
+  if (scores == nullptr) {
+    const size_t need = csa_index_topk_workspace_bytes(B, Tq, Hi, keys->cap, topk);
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, CSA_EWORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    REQUIRE(aligned(workspace, 256), CSA_EINVAL, "workspace must be 256-byte aligned");
+    scores = static_cast<float*>(workspace);
+  } else {
+    REQUIRE(aligned(scores_out, 16), CSA_EINVAL, "scores_out must be 16-byte aligned");
+  }
+  csa::IndexArgs a{};
+  a.q_idx = q_idx;
+  a.w = w;
+  a.q_pos = q_pos;
+  a.B = B;
+  a.Tq = Tq;
+  a.Hi = Hi;
+  a.Di = keys->C;
+  a.keys = keys->data;
+  a.key_scales = keys->dtype == CSA_FP8_E4M3 ? keys->scales : nullptr;
+  a.n_valid = keys->n_valid;
+  a.pos0 = keys->pos0;
+  a.key_dtype = keys->dtype;
+  a.cap = keys->cap;
+  a.window = keys->window;
+  a.stride = keys->stride;
+  a.topk = topk;
+  a.scores = scores;
+  a.idx_out = idx_out;
+  hipError_t e = csa::launch_index_scores(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "index score launch failed: %s", hipGetErrorString(e));
+  e = csa::launch_topk(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "top-k launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t csa_attend_workspace_bytes(int B, int Tq, int H, int topk, int W) {
+  if (B <= 0 || Tq <= 0 || H <= 0) return 0;
+  return csa::attend_workspace(B * Tq, H, topk + (W > 0 ? W : 0));
+}
+
+size_t hca_attend_workspace_bytes(int B, int Tq, int H, int cap, int W) {
+  if (B <= 0 || Tq <= 0 || H <= 0) return 0;
+  return csa::attend_workspace(B * Tq, H, cap + (W > 0 ? W : 0));
+}
+
+static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int H, const csa_cache_t* kv,
+                         const int32_t* idx, int topk, bool csa_mode, const csa_cache_t* win, int W,
+                         const float* sink, const double* inv_freq, int rope_dim, float softmax_scale, void* out,
+                         int out_dtype, float* lse_out, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  int rc = check_cache(kv, "kv", true);
+  if (rc) return rc;
+  rc = check_cache(win, "win", true);
+  if (rc) return rc;
+  REQUIRE(B >= 0 && Tq >= 0, CSA_EINVAL, "B and Tq must be >= 0");
+  if (B == 0 || Tq == 0) return ok();
+  REQUIRE(q && q_pos && sink && out, CSA_EINVAL, "q, q_pos, sink and out must be non-NULL");
+  REQUIRE(H >= 1 && H <= 1024, CSA_EINVAL, "H must be in [1, 1024] (got %d)", H);
+  REQUIRE(kv->C == 512 && win->C == 512, CSA_ENOTSUP, "head dim must be 512 (kv %d, win %d)", kv->C, win->C);
+  REQUIRE(win->dtype == CSA_BF16, CSA_ENOTSUP, "window cache must be bf16");
+  REQUIRE(win->window == 1 && win->stride == 1, CSA_EINVAL, "window cache must have window = stride = 1");
+  REQUIRE(kv->dtype == CSA_BF16 || kv->scale_block % 8 == 0, CSA_ENOTSUP,
+          "fp8 KV scale_block must be a multiple of 8 (got %d)", kv->scale_block);
+  REQUIRE(W >= 0, CSA_EINVAL, "W must be >= 0 (got %d)", W);
+  REQUIRE(out_dtype == CSA_FP32 || out_dtype == CSA_BF16, CSA_ENOTSUP, "out_dtype must be FP32 or BF16");
+  REQUIRE(aligned(q, 16) && aligned(out, 16), CSA_EINVAL, "q and out must be 16-byte aligned");
+  if (csa_mode) {
+    REQUIRE(topk >= 0 && topk <= kv->cap, CSA_EINVAL, "topk must be in [0, cap=%d] (got %d)", kv->cap, topk);
+    REQUIRE(topk == 0 || idx != nullptr, CSA_EINVAL, "idx is NULL");
+  }
+  rc = check_rope(inv_freq, rope_dim, 512);
+  if (rc) return rc;
+  const int rows = B * Tq;
+  const int slot_cap = (csa_mode ? topk : kv->cap) + W;
+  const size_t need = csa::attend_workspace(rows, H, slot_cap);
+  if (need > 0) {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, CSA_EWORKSPACE,
+            "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+    REQUIRE(aligned(workspace, 256), CSA_EINVAL, "workspace must be 256-byte aligned");
+  }
+  csa::AttendArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.B = B;
+  a.Tq = Tq;
+  a.H = H;
+  a.kv = kv->data;
+  a.kv_scales = kv->dtype == CSA_FP8_E4M3 ? kv->scales : nullptr;
+  a.kv_n_valid = kv->n_valid;
+  a.kv_pos0 = kv->pos0;
+  a.kv_dtype = kv->dtype;
+  a.kv_cap = kv->cap;
+  a.kv_scale_block = kv->scale_block;
+  a.kv_window = kv->window;
+  a.kv_stride = kv->stride;
+  a.idx = csa_mode ? (topk > 0 ? idx : nullptr) : nullptr;
+  a.topk = csa_mode ? topk : 0;
+  a.win = win->data;
+  a.win_n_valid = win->n_valid;
+  a.win_pos0 = win->pos0;
+  a.win_cap = win->cap;
+  a.W = W;
+  a.sink = sink;
+  a.inv_freq = inv_freq;
+  a.rope_dim = rope_dim;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.lse = lse_out;
+  a.slot_cap = slot_cap;
+  if (need > 0) {
+    const int ns = csa::attend_nsplit(rows, H, slot_cap);
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = a.part_o + (size_t)rows * ns * H * 512;
+  }
+  a.csa_mode = csa_mode ? 1 : 0;
+  hipError_t e;
+  e = csa::launch_attend(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "attend launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int csa_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H, const csa_cache_t* kv,
+               const int32_t* idx, int topk, const csa_cache_t* win, int W, const float* sink,
+               const double* inv_freq, int rope_dim, float softmax_scale, void* out, int out_dtype,
+               float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attend_common(q, q_pos, B, Tq, H, kv, idx, topk, true, win, W, sink, inv_freq, rope_dim, softmax_scale,
+                       out, out_dtype, lse_out, workspace, workspace_bytes, stream);
+}
+
+int hca_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H, const csa_cache_t* kv,
+               const csa_cache_t* win, int W, const float* sink, const double* inv_freq, int rope_dim,
+               float softmax_scale, void* out, int out_dtype, float* lse_out, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  return attend_common(q, q_pos, B, Tq, H, kv, nullptr, 0, false, win, W, sink, inv_freq, rope_dim,
+                       softmax_scale, out, out_dtype, lse_out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,409 @@
+// Shared-KV multi-query attention with sink and inverse output rotation (CSA and HCA).
+//
+// Every query head attends to the same rows, each row being key and value at once:
+// the selected compressed entries (CSA) or every visible entry (HCA), plus the raw
+// tokens of the sliding window.  Each head's sink logit adds its exponential to the
+// softmax denominator only.  Queries are rotated at their position on the last
+// rope_dim channels, and the same channels of each head's output are rotated back by
+// that position (DeepSeek-V4-Pro vs Inkling, Component-by-component table: CSA, HCA,
+// sink and partial-RoPE rows; atlas Raw config fields head_dim 512, one KV head).
+//
+// Kernel design (gfx950, wave64, bf16 MFMA 16x16x32, fp32 accumulation):
+//  * a block = 4 waves = 64 heads of one query row and one split of its row set;
+//    tiles of 32 rows are staged in LDS once and used by all 4 waves for both
+//    contractions (K = V);
+//  * scores are computed transposed, S^T = K Q^T (M = rows, N = heads, K = channels),
+//    and the output as O^T = V^T P^T (M = channels, N = heads, K = rows): every
+//    accumulator lane then belongs to one head, so the online-softmax statistics,
+//    the rescaling and the final normalisation stay in the lane, and the P tile
+//    leaves the score accumulators already in the B-operand layout of the second
+//    contraction;
+//  * the V^T operand is read from the same row-major LDS tile with the gfx950
+//    transposing LDS load (ds_read_b64_tr_b16), so no transposed copy is stored;
+//  * the sink enters as the initial running maximum and a weight of one in split 0;
+//  * several splits of the row set run in parallel when the query rows alone cannot
+//    fill the GPU; their (max, sum, unnormalised output) partials are merged by
+//    k_attend_combine.  With one split the kernel normalises, rotates and stores.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+
+constexpr int kAttWaves = 4;
+constexpr int kHeadsPerBlock = 64;
+constexpr int kTile = 32;           // rows per LDS tile
+constexpr int kD = 512;             // channels (head dim)
+constexpr int kPitch = 520;         // bf16 per LDS row: 1040 B, rows land 4 banks apart
+constexpr int kTargetBlocks = 256;  // split until the grid has about this many blocks
+
+__device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int window, int stride,
+                                                int n_valid, int cap) {
+  int nv = min(max(n_valid, 0), cap);
+  int64_t num = qp - pos0 - (window - 1);
+  if (num < 0) return 0;
+  return (int)min((int64_t)nv, num / stride + 1);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <bool CSA, bool FP8>
+__global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kPitch];
+  __shared__ int tvalid[kTile];
+
+  const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const uint32_t total = gridDim.x;
+  const uint32_t logical = xcd_remap(blockIdx.x, total);
+  const int hg = logical % HG;
+  const int split = (logical / HG) % a.nsplit;
+  const int row = logical / (HG * a.nsplit);
+  const int b = row / a.Tq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int head = hg * kHeadsPerBlock + wave * 16 + n;
+  const bool head_ok = head < a.H;
+
+  const int64_t p = a.q_pos[row];
+
+  // ---- the row set of this query: entries, then window rows
+  const int kv_nv = min(max(a.kv_n_valid[b], 0), a.kv_cap);
+  int n_ent;
+  if (CSA) n_ent = a.topk;
+  else n_ent = visible_rows_att(p, a.kv_pos0[b], a.kv_window, a.kv_stride, a.kv_n_valid[b], a.kv_cap);
+  const int64_t wp0 = a.win_pos0[b];
+  const int w_nv = min(max(a.win_n_valid[b], 0), a.win_cap);
+  int64_t r_lo = p - a.W + 1 - wp0;
+  int64_t r_hi = p - wp0;
+  if (r_lo < 0) r_lo = 0;
+  if (r_hi > w_nv - 1) r_hi = w_nv - 1;
+  const int n_win = (a.W > 0 && r_hi >= r_lo) ? (int)(r_hi - r_lo + 1) : 0;
+  const int n_slots = n_ent + n_win;
+  const int s0 = split * a.slots_per_split;
+  const int s1 = min(n_slots, s0 + a.slots_per_split);
+
+  // ---- query fragments (B operand of S^T = K Q^T): head = n, channels 32c + 8g + [0, 8).
+  // The rotated query is not a bf16 value: its last two chunks (channels 448..511, which
+  // hold the rotated pairs for rope_dim <= 64) are carried as bf16 hi + lo so the logits
+  // keep fp32 accuracy; rotated channels below 448 (rope_dim > 64) are rounded to bf16.
+  bf16x8 qf[16];
+  bf16x8 qlo[2];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + head) * kD;
+    const int rot0 = kD - a.rope_dim;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      u32x4 lo = {0u, 0u, 0u, 0u};
+      if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+      if (32 * c + 32 > rot0 && a.rope_dim > 0) {
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int d = 32 * c + 8 * g + 2 * k2;
+          if (d >= rot0) {
+            float cs, sn;
+            rope_cs(p, a.inv_freq[(d - rot0) >> 1], cs, sn);
+            const float x0 = bf16lo_to_f32(v[k2]), x1 = bf16hi_to_f32(v[k2]);
+            const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+            v[k2] = pack_bf16x2(y0, y1);
+            lo[k2] = pack_bf16x2(y0 - bf16lo_to_f32(v[k2]), y1 - bf16hi_to_f32(v[k2]));
+          }
+        }
+      }
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+      if (c >= 14) qlo[c - 14] = __builtin_bit_cast(bf16x8, lo);
+    }
+  }
+  const bool q_split = a.rope_dim > 0;
+
+  // ---- online softmax state (per lane: head n; the 4 lanes of a head hold equal m)
+  float m_run, l_run;
+  if (split == 0 && head_ok) {
+    m_run = a.sink[head] * kLog2e;
+    l_run = (g == 0) ? 1.f : 0.f;
+  } else {
+    m_run = kNegBig;
+    l_run = 0.f;
+  }
+  f32x4 acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- row loader: wave w stages tile rows w, w+4, ..., w+28; lane = 8 channels
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
+  const uint16_t* winb = reinterpret_cast<const uint16_t*>(a.win);
+  const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
+  auto fetch = [&](int t0, u32x4 (&r)[8], int (&ok)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = t0 + wave + 4 * i;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      int valid = 0;
+      if (slot < s1) {
+        if (slot < n_ent) {
+          int j = CSA ? idxrow[slot] : slot;
+          if (j >= 0 && j < kv_nv) {
+            valid = 1;
+            const int64_t rr = (int64_t)b * a.kv_cap + j;
+            if (FP8) {
+              const u32x2 c2 = *reinterpret_cast<const u32x2*>(kvb + rr * kD + 8 * lane);
+              const float sc = a.kv_scales[rr * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
+              const f32x2 f0 = fp8x2_lo(c2[0]), f1 = fp8x2_hi(c2[0]);
+              const f32x2 f2 = fp8x2_lo(c2[1]), f3 = fp8x2_hi(c2[1]);
+              v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
+              v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
+              v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
+              v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
+            } else {
+              v = *reinterpret_cast<const u32x4*>(kvb + rr * (2 * kD) + 16 * lane);
+            }
+          }
+        } else {
+          const int64_t rr = (int64_t)b * a.win_cap + r_lo + (slot - n_ent);
+          v = *reinterpret_cast<const u32x4*>(winb + rr * kD + 8 * lane);
+          valid = 1;
+        }
+      }
+      r[i] = v;
+      ok[i] = valid;
+    }
+  };
+
+  u32x4 pre[8];
+  int pok[8];
+  const int ntile = s1 > s0 ? (s1 - s0 + kTile - 1) / kTile : 0;
+  if (ntile > 0) fetch(s0, pre, pok);
+
+  for (int t = 0; t < ntile; ++t) {
+    // stage the prefetched rows
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = wave + 4 * i;
+      *reinterpret_cast<u32x4*>(&tile[rr * kPitch + 8 * lane]) = pre[i];
+      if (lane == 0) tvalid[rr] = pok[i];
+    }
+    __syncthreads();
+    if (t + 1 < ntile) fetch(s0 + (t + 1) * kTile, pre, pok);
+
+    // S^T = K Q^T for rows 16kb + [0,16) of the tile
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* rp = &tile[(16 * kb + n) * kPitch + 8 * g];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + 32 * c);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
+        if (c >= 14 && q_split)
+          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[c - 14], sacc[kb], 0, 0, 0);
+      }
+    }
+    // online softmax over this tile's rows 16kb + 4g + i (lane's head n)
+    float sv[8];
+    int vmask = 0;
+    float tmax = kNegBig;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * kb + i;
+        const int ok = tvalid[16 * kb + 4 * g + i];
+        sv[e] = sacc[kb][i] * a.scale_log2;
+        if (ok) { vmask |= 1 << e; tmax = fmaxf(tmax, sv[e]); }
+      }
+    tmax = wave_max_xor(tmax, 16);
+    tmax = wave_max_xor(tmax, 32);
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = exp2f(m_run - m_new);
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = (vmask >> e & 1) ? exp2f(sv[e] - m_new) : 0.f;
+      psum += pv[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+    }
+    u32x4 pw;
+    pw[0] = pack_bf16x2(pv[0], pv[1]);
+    pw[1] = pack_bf16x2(pv[2], pv[3]);
+    pw[2] = pack_bf16x2(pv[4], pv[5]);
+    pw[3] = pack_bf16x2(pv[6], pv[7]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+
+    // O^T += V^T P^T: A operand (channel 16db + n, rows 16r + 4g + j) via transposing loads
+    const int L = lane & 15;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)&tile[(4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)&tile[(16 + 4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+      const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  if (!head_ok) return;
+  if (a.nsplit == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int rot0 = kD - a.rope_dim;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = acc[db][i] * inv;
+      const int d0 = 16 * db + 4 * g;
+      if (16 * db + 16 > rot0 && a.rope_dim > 0) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int d = d0 + 2 * k2;
+          if (d >= rot0) {
+            float cs, sn;
+            rope_cs(-p, a.inv_freq[(d - rot0) >> 1], cs, sn);
+            const float x0 = o[2 * k2], x1 = o[2 * k2 + 1];
+            o[2 * k2] = x0 * cs - x1 * sn;
+            o[2 * k2 + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
+      const int64_t off = ((int64_t)row * a.H + head) * kD + d0;
+      if (a.out_dtype == CSA_FP32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = f32x4{o[0], o[1], o[2], o[3]};
+      } else {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(o[0], o[1]);
+        w2[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w2;
+      }
+    }
+    if (a.lse && g == 0) a.lse[(int64_t)row * a.H + head] = (m_run + log2f(l_tot)) * kLn2;
+  } else {
+    const int64_t pr = ((int64_t)row * a.nsplit + split) * a.H + head;
+#pragma unroll
+    for (int db = 0; db < 32; ++db)
+      *reinterpret_cast<f32x4*>(a.part_o + pr * kD + 16 * db + 4 * g) = acc[db];
+    if (g == 0) {
+      a.part_ml[2 * pr] = m_run;
+      a.part_ml[2 * pr + 1] = l_tot;
+    }
+  }
+}
+
+// Merge split partials: M = max m_s, Z = sum l_s 2^(m_s - M), o = sum 2^(m_s - M) o_s / Z,
+// then rotate back and store.  grid: rows * H blocks of 128 lanes (4 channels each).
+__global__ void __launch_bounds__(128) k_attend_combine(AttendArgs a) {
+  const int rh = blockIdx.x;               // row * H + head
+  const int row = rh / a.H;
+  const int d0 = threadIdx.x * 4;
+  const int64_t p = a.q_pos[row];
+  float M = kNegBig;
+  for (int s = 0; s < a.nsplit; ++s)
+    M = fmaxf(M, a.part_ml[2 * (((int64_t)row * a.nsplit + s) * a.H + rh % a.H)]);
+  float Z = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.nsplit; ++s) {
+    const int64_t pr = ((int64_t)row * a.nsplit + s) * a.H + rh % a.H;
+    const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
+    const float wgt = exp2f(ms - M);
+    Z += ls * wgt;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] += wgt * v[i];
+  }
+  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] *= inv;
+  const int rot0 = kD - a.rope_dim;
+  if (a.rope_dim > 0 && d0 + 4 > rot0) {
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int d = d0 + 2 * k2;
+      if (d >= rot0) {
+        float cs, sn;
+        rope_cs(-p, a.inv_freq[(d - rot0) >> 1], cs, sn);
+        const float x0 = o[2 * k2], x1 = o[2 * k2 + 1];
+        o[2 * k2] = x0 * cs - x1 * sn;
+        o[2 * k2 + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+  const int64_t off = (int64_t)rh * kD + d0;
+  if (a.out_dtype == CSA_FP32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = f32x4{o[0], o[1], o[2], o[3]};
+  } else {
+    u32x2 w2;
+    w2[0] = pack_bf16x2(o[0], o[1]);
+    w2[1] = pack_bf16x2(o[2], o[3]);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w2;
+  }
+  if (a.lse && threadIdx.x == 0) a.lse[rh] = (M + log2f(Z)) * kLn2;
+}
+
+int attend_nsplit(int rows, int H, int slot_cap) {
+  const int HG = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const long long base = (long long)rows * HG;
+  int ns = (int)((kTargetBlocks + base - 1) / base);
+  const int max_ns = (slot_cap + 2 * kTile - 1) / (2 * kTile);   // at least two tiles per split
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  // round the per-split count up to whole tiles, then recount
+  int sps = (slot_cap + ns - 1) / ns;
+  sps = (sps + kTile - 1) / kTile * kTile;
+  if (sps < kTile) sps = kTile;
+  return (slot_cap + sps - 1) / sps;
+}
+
+static int attend_sps(int nsplit, int slot_cap) {
+  int sps = (slot_cap + nsplit - 1) / nsplit;
+  sps = (sps + kTile - 1) / kTile * kTile;
+  return sps < kTile ? kTile : sps;
+}
+
+size_t attend_workspace(int rows, int H, int slot_cap) {
+  const int ns = attend_nsplit(rows, H, slot_cap);
+  if (ns <= 1) return 0;
+  return (size_t)rows * ns * H * (kD + 2) * sizeof(float) + 256;
+}
+
+hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
+  AttendArgs a = a0;
+  const int rows = a.B * a.Tq;
+  a.nsplit = attend_nsplit(rows, a.H, a.slot_cap);
+  a.slots_per_split = attend_sps(a.nsplit, a.slot_cap);
+  const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const long long blocks = (long long)rows * HG * a.nsplit;
+  const bool csa = a.csa_mode != 0;
+  const bool f8 = a.kv_dtype == CSA_FP8_E4M3;
+  dim3 grid((unsigned)blocks);
+  if (csa) {
+    if (f8) hipLaunchKernelGGL((k_attend<true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attend<true, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (f8) hipLaunchKernelGGL((k_attend<false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_attend<false, false>), grid, dim3(256), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.nsplit > 1) {
+    hipLaunchKernelGGL(k_attend_combine, dim3(rows * a.H), dim3(128), 0, s, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace csa

@@ -1,0 +1,90 @@
+// Device helpers shared by the CSA/HCA kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -3.0e38f;   // "no logit yet"; finite so that differences stay finite
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- fp8 e4m3fn (OCP)
+
+// Two codes (bytes 0,1 or 2,3 of `w`) -> two fp32 values; gfx950's converter reads OCP E4M3FN.
+__device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false); }
+__device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true); }
+
+// fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (finite input).
+// Written from the format definition: 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+// subnormal spacing 2^-9, largest finite value 1.75 * 2^8.
+__device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fminf(fabsf(x), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                    // below 2^-6: subnormal range, spacing 2^-9
+    float m = rintf(a * 512.0f);          // exact scaling; rintf rounds half to even
+    code = (uint32_t)m;                   // 0..8 (8 == smallest normal, encoded correctly as 1<<3)
+  } else {
+    uint32_t ua = __float_as_uint(a);
+    // keep 3 mantissa bits of the fp32 value with round-to-nearest-even
+    uint32_t lsb = (ua >> 20) & 1u;
+    ua += 0x7ffffu + lsb;
+    uint32_t e = (ua >> 23) - 127 + 7;    // biased e4m3 exponent (1..15)
+    uint32_t m = (ua >> 20) & 7u;
+    code = (e << 3) | m;
+    if (code > 0x7eu) code = 0x7eu;       // saturate (448 = 0x7e)
+  }
+  return code == 0 ? 0u : (code | sign);
+}
+
+// ---------------------------------------------------------------- rotary
+
+// (cos, sin) of pos * inv_freq evaluated in fp64, returned in fp32.
+__device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float& c, float& s) {
+  double ang = (double)pos * inv_freq;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// ---------------------------------------------------------------- XCD-aware block order
+
+// Blocks are dispatched round-robin over the 8 XCDs (block L lands on XCD L % 8).
+// Remap so that each XCD works on one contiguous range of logical blocks: neighbours in
+// logical order (which share input rows) then share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t L, uint32_t total) {
+  if ((total & 7u) != 0u) return L;
+  return (L & 7u) * (total >> 3) + (L >> 3);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, kWave));
+}
+
+}  // namespace csa

@@ -1,0 +1,187 @@
+// Softmax-pooled KV compression with fused partial RoPE and bf16 / fp8 storage.
+//
+// Each cache row pools `window` raw tokens at step `stride` with a softmax taken
+// separately per channel over the window's pooling logits, then rotates the last
+// rope_dim channels at the row's position (its last token's) and stores the row
+// (DeepSeek-V4-Pro vs Inkling, Component-by-component table: CSA row, HCA row,
+// partial-RoPE row; DeepSeek-V4.1-Flash vs Inkling: cache quantized after RoPE).
+//
+// Layout of the work: a group of C/8 lanes owns one sequence's run of consecutive
+// rows, each lane 8 channels (16-byte loads of kv and logits).  When window ==
+// 2*stride (CSA: 8 tokens at stride 4) consecutive rows share half their tokens, so
+// the group walks the raw stream once, block of `stride` tokens by block, keeps the
+// previous block's partial softmax state (running max, sum of weights, weighted sum)
+// in registers and combines it with the current block: every raw token is read from
+// HBM once.  Other geometries (HCA 128/128, the raw-window write 1/1) read each
+// row's own tokens.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+
+struct PoolState {
+  float m[8], s[8], sv[8];
+};
+
+__device__ __forceinline__ void pool_reset(PoolState& p) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { p.m[i] = kNegBig; p.s[i] = 0.f; p.sv[i] = 0.f; }
+}
+
+// Fold one raw token (8 channels: values v, logits already multiplied by log2 e) into p.
+__device__ __forceinline__ void pool_add(PoolState& p, const float* v, const float* z2) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float mn = fmaxf(p.m[i], z2[i]);
+    float a = exp2f(p.m[i] - mn);
+    float b = exp2f(z2[i] - mn);
+    p.s[i] = p.s[i] * a + b;
+    p.sv[i] = p.sv[i] * a + b * v[i];
+    p.m[i] = mn;
+  }
+}
+
+__device__ __forceinline__ void pool_merge(PoolState& out, const PoolState& x, const PoolState& y) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float mn = fmaxf(x.m[i], y.m[i]);
+    float a = exp2f(x.m[i] - mn), b = exp2f(y.m[i] - mn);
+    out.m[i] = mn;
+    out.s[i] = x.s[i] * a + y.s[i] * b;
+    out.sv[i] = x.sv[i] * a + y.sv[i] * b;
+  }
+}
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[2 * i] = bf16lo_to_f32(w[i]); f[2 * i + 1] = bf16hi_to_f32(w[i]); }
+}
+
+// Add one block of `n` raw tokens starting at token row `t0` into p.
+__device__ __forceinline__ void pool_block(PoolState& p, const uint16_t* kv, const uint16_t* lg,
+                                           int64_t ld_tok, int t0, int n, int c0) {
+  for (int t = 0; t < n; ++t) {
+    float v[8], z[8];
+    load8(kv + (int64_t)(t0 + t) * ld_tok + c0, v);
+    if (lg) {
+      load8(lg + (int64_t)(t0 + t) * ld_tok + c0, z);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] *= kLog2e;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) z[i] = 0.f;
+    }
+    pool_add(p, v, z);
+  }
+}
+
+// Finish one row: normalise, rotate, store.
+__device__ __forceinline__ void finish_row(const PoolState& p, const CompressArgs& a, int b, int row,
+                                           int c0, int lane_in_group) {
+  float e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = p.sv[i] / p.s[i];
+  const int rot0 = a.C - a.rope_dim;
+  if (c0 + 8 > rot0 && a.rope_dim > 0) {
+    int64_t pos = a.pos0[b] + (int64_t)row * a.stride + (a.window - 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      int c = c0 + 2 * k;
+      if (c >= rot0) {
+        float cs, sn;
+        rope_cs(pos, a.inv_freq[(c - rot0) >> 1], cs, sn);
+        float x0 = e[2 * k], x1 = e[2 * k + 1];
+        e[2 * k] = x0 * cs - x1 * sn;
+        e[2 * k + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+  const int64_t rowoff = ((int64_t)b * a.cap + row) * a.C;
+  if (a.dtype == CSA_BF16) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + rowoff + c0) = w;
+  } else {
+    // fp8: one scale per scale_block channels = scale_block/8 consecutive lanes.
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
+    for (int m = 1; m < a.scale_block / 8; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, kWave));
+    float scale = amax / 448.0f;
+    uint32_t lo = 0, hi = 0;
+    if (scale > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= f32_to_fp8_e4m3(e[i] / scale) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= f32_to_fp8_e4m3(e[4 + i] / scale) << (8 * i);
+    }
+    u32x2 w;
+    w[0] = lo;
+    w[1] = hi;
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.out) + rowoff + c0) = w;
+    if ((c0 % a.scale_block) == 0) {
+      int nsb = a.C / a.scale_block;
+      a.scales[((int64_t)b * a.cap + row) * nsb + c0 / a.scale_block] = scale;
+    }
+  }
+  (void)lane_in_group;
+}
+
+// grid: (ceil(n_new / run), B); block: groups of C/8 lanes, one run of rows per group.
+__global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
+  const int lanes = a.C / 8;
+  const int groups = blockDim.x / lanes;
+  const int g = threadIdx.x / lanes;
+  const int li = threadIdx.x % lanes;
+  if (g >= groups) return;
+  const int b = blockIdx.y;
+  const int first = (blockIdx.x * groups + g) * a.run;   // first new row (relative) of this run
+  if (first >= a.n_new) return;
+  const int last = min(first + a.run, a.n_new);           // exclusive
+  const int c0 = li * 8;
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
+  const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
+                                : nullptr;
+  if (a.window == 2 * a.stride) {
+    // Overlapping rows: entry i = block i + block i+1 (blocks of `stride` tokens).
+    PoolState prev, cur, both;
+    pool_reset(prev);
+    pool_block(prev, kv, lg, a.ld_tok, first * a.stride, a.stride, c0);
+    for (int i = first; i < last; ++i) {
+      pool_reset(cur);
+      pool_block(cur, kv, lg, a.ld_tok, (i + 1) * a.stride, a.stride, c0);
+      pool_merge(both, prev, cur);
+      finish_row(both, a, b, a.first_row + i, c0, li);
+      prev = cur;
+    }
+  } else {
+    for (int i = first; i < last; ++i) {
+      PoolState p;
+      pool_reset(p);
+      pool_block(p, kv, lg, a.ld_tok, i * a.stride, a.window, c0);
+      finish_row(p, a, b, a.first_row + i, c0, li);
+    }
+  }
+}
+
+hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
+  CompressArgs a = a0;
+  const int lanes = a.C / 8;
+  const int groups = 256 / lanes;
+  // Long runs amortise the extra leading block of overlapping windows; short runs keep
+  // enough blocks in flight for small calls.
+  int run = 1;
+  if (a.window == 2 * a.stride) {
+    long long rows = (long long)a.n_new * a.B;
+    run = rows >= 4096 ? 16 : (rows >= 1024 ? 4 : 1);
+  }
+  a.run = run;
+  const int runs = (a.n_new + run - 1) / run;
+  dim3 grid((runs + groups - 1) / groups, a.B);
+  hipLaunchKernelGGL(k_compress, grid, dim3(groups * lanes), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,349 @@
+// Lightning indexer scores and top-k selection.
+//
+// Score of compressed entry j for one query token: a weighted sum over the indexer
+// heads of the ReLU of the head's query dotted with the entry's key; the k best
+// visible entries are kept (DeepSeek-V4-Pro vs Inkling, Component-by-component
+// table, CSA row; atlas Raw config fields index_n_heads / index_head_dim /
+// index_topk).
+//
+// Scores: the contraction is q_idx [heads x Di] times keys [Di x entries], run on
+// bf16 MFMA 16x16x32 with heads as M, entries as N and Di as K.  Each lane then owns
+// one entry and 4 heads per 16-head block, so the ReLU and the per-head weights are
+// applied in registers and only two cross-lane adds finish the head sum.  Keys
+// stream from HBM straight into registers (no LDS): lane (entry n, group g) reads the
+// contiguous channels [32g, 32g+32) of key n, so a wave reads 16 whole key rows per
+// tile; the query fragments follow the same channel permutation.  fp8 keys are
+// widened to bf16 in registers (exact: E4M3 values fit bf16) and the per-key scale
+// multiplies the finished score (scales are >= 0, so they commute with the ReLU).
+//
+// Top-k: one 1024-lane block per query row.  Scores map to order-preserving uint32
+// keys.  A 2048-bin histogram over a linear scale of the current key range finds the
+// bin holding the k-th largest key; that bin's own key range becomes the next range
+// (at most three passes reach a single key) until the candidates fit in LDS, where
+// they are ranked exactly by (score descending, index ascending).  The k-th candidate
+// (T, I) is a threshold in that total order; a final pass writes every j with key > T,
+// or key == T and j <= I, in ascending index order.  Bins that are linear in the key
+// (uniform in value within a binade) keep LDS atomics spread out even when all scores
+// crowd into one binade.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace csa {
+
+// Number of entries of a cache visible to a query at position qp (see csa.h).
+__device__ __forceinline__ int visible_rows(int64_t qp, int64_t pos0, int window, int stride,
+                                            int n_valid, int cap) {
+  int nv = min(max(n_valid, 0), cap);
+  int64_t num = qp - pos0 - (window - 1);
+  if (num < 0) return 0;
+  int64_t jmax = num / stride;             // last visible row
+  return (int)min((int64_t)nv, jmax + 1);
+}
+
+// ---------------------------------------------------------------- scores
+
+constexpr int kIdxTilesPerWave = 16;     // 16 entries per tile
+constexpr int kIdxWaves = 4;
+constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
+
+template <int HB, bool FP8>
+__global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
+  const int row = blockIdx.x;                 // query row (b * Tq + t)
+  const int b = row / a.Tq;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t qp = a.q_pos[row];
+  const int nvis = visible_rows(qp, a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
+  float* srow = a.scores + (int64_t)row * a.cap;
+  const int base = blockIdx.y * kIdxEntPerBlock + wave * (kIdxTilesPerWave * 16);
+
+  // query fragments: A operand, row = head (hb*16 + n), k = 8g + i <-> channel 32g + 8s + i
+  bf16x8 qf[HB][4];
+  float wv[HB][4];
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q_idx) + (int64_t)row * a.Hi * a.Di;
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int h = hb * 16 + n;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (h < a.Hi) v = *reinterpret_cast<const u32x4*>(q + (int64_t)h * a.Di + 32 * g + 8 * s);
+      qf[hb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = hb * 16 + 4 * g + i;
+      wv[hb][i] = hh < a.Hi ? a.w[(int64_t)row * a.Hi + hh] : 0.f;
+    }
+  }
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys) +
+                         (int64_t)b * a.cap * (FP8 ? a.Di : 2 * a.Di);
+  constexpr int KW = FP8 ? 8 : 16;            // dwords of key data per lane per tile
+  auto load_tile = [&](int t0, uint32_t (&r)[KW]) {
+    const int j = t0 + n;
+    if (j < nvis) {
+      const uint8_t* p = kbase + (int64_t)j * (FP8 ? 128 : 256) + (FP8 ? 32 : 64) * g;
+#pragma unroll
+      for (int c = 0; c < KW / 4; ++c) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * c);
+        r[4 * c] = v[0]; r[4 * c + 1] = v[1]; r[4 * c + 2] = v[2]; r[4 * c + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KW; ++c) r[c] = 0u;
+    }
+  };
+
+  uint32_t cur[KW], nxt[KW];
+  int ntile = 0;
+  if (base < nvis) ntile = min(kIdxTilesPerWave, (nvis - base + 15) / 16);
+  if (ntile > 0) load_tile(base, cur);
+  for (int t = 0; t < ntile; ++t) {
+    const int t0 = base + 16 * t;
+    if (t + 1 < ntile) load_tile(t0 + 16, nxt);
+    f32x4 acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 kb;
+      if (FP8) {
+        // 8 codes (channels 32g + 8s .. +8) -> 8 bf16, exactly
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          uint32_t w = cur[2 * s + h2];
+          f32x2 lo = fp8x2_lo(w), hi = fp8x2_hi(w);
+          kb[2 * h2] = (__float_as_uint(lo[1]) & 0xffff0000u) | (__float_as_uint(lo[0]) >> 16);
+          kb[2 * h2 + 1] = (__float_as_uint(hi[1]) & 0xffff0000u) | (__float_as_uint(hi[0]) >> 16);
+        }
+      } else {
+        kb[0] = cur[4 * s]; kb[1] = cur[4 * s + 1]; kb[2] = cur[4 * s + 2]; kb[3] = cur[4 * s + 3];
+      }
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, kb);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[hb][s], kf, acc[hb], 0, 0, 0);
+    }
+    float sc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc += wv[hb][i] * fmaxf(acc[hb][i], 0.f);
+    sc += __shfl_xor(sc, 16, kWave);
+    sc += __shfl_xor(sc, 32, kWave);
+    const int j = t0 + n;
+    if (FP8 && j < nvis) sc *= a.key_scales[(int64_t)b * a.cap + j];
+    if (g == 0 && j < a.cap) srow[j] = j < nvis ? sc : -INFINITY;
+    if (t + 1 < ntile) {
+#pragma unroll
+      for (int c = 0; c < KW; ++c) cur[c] = nxt[c];
+    }
+  }
+  // rows of this wave's range beyond the visible count
+  for (int j = max(base + 16 * ntile, base) + lane; j < min(base + kIdxTilesPerWave * 16, a.cap); j += 64)
+    srow[j] = -INFINITY;
+}
+
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
+  const int rows = a.B * a.Tq;
+  dim3 grid(rows, (a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
+  const int HB = (a.Hi + 15) / 16;
+  const bool f8 = a.key_dtype == CSA_FP8_E4M3;
+#define CSA_IDX_LAUNCH(hb)                                                                     \
+  if (HB == hb) {                                                                              \
+    if (f8) hipLaunchKernelGGL((k_index_scores<hb, true>), grid, dim3(256), 0, s, a);          \
+    else hipLaunchKernelGGL((k_index_scores<hb, false>), grid, dim3(256), 0, s, a);            \
+  }
+  CSA_IDX_LAUNCH(1) CSA_IDX_LAUNCH(2) CSA_IDX_LAUNCH(3) CSA_IDX_LAUNCH(4)
+#undef CSA_IDX_LAUNCH
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- top-k
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkBins = 2048;
+constexpr int kCandMax = 512;
+
+struct TopkShared {
+  int hist[kTopkBins];
+  uint32_t ckey[kCandMax];
+  int cidx[kCandMax];
+  int wsum[kTopkThreads / 64];
+  uint32_t wmin[kTopkThreads / 64], wmax[kTopkThreads / 64];
+  int ccount;
+  int bstar, above;
+  uint32_t TK;
+  int I;
+};
+
+// Order-preserving map of fp32 bit patterns onto uint32.
+__device__ __forceinline__ uint32_t okey(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the block (1024 lanes); also returns the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kTopkThreads / 64; ++w2) {
+    int s = wsum[w2];
+    if (w2 < wave) before += s;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return before + x - v;
+}
+
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TopkShared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+  }
+  if (lane == 0) { sh.wmin[wave] = mn; sh.wmax[wave] = mx; }
+  __syncthreads();
+  mn = sh.wmin[0];
+  mx = sh.wmax[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kTopkThreads / 64; ++w2) { mn = min(mn, sh.wmin[w2]); mx = max(mx, sh.wmax[w2]); }
+  __syncthreads();
+}
+
+// One block (1024 lanes) per query row.  Keys are bins of a linear scale over the
+// current key range [klo, khi]: bin = (key - klo) >> shift with 2048 bins.  Each
+// refinement keeps only the bin holding the k-th largest key, whose key range is
+// at most 2^shift - 1 wide, so after at most three passes the candidates are one
+// key value (the range shrinks from < 2^32 to < 2^21, < 2^10, then 0).
+__global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x;
+  const int b = row / a.Tq;
+  const int tid = threadIdx.x;
+  const int k = a.topk;
+  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
+  const float* s = a.scores + (int64_t)row * a.cap;
+  int32_t* out = a.idx_out + (int64_t)row * k;
+
+  uint32_t TK = 0xffffffffu;   // threshold (key, index) in the order (score desc, index asc)
+  int I = -1;
+  const bool take_all = nvis <= k;
+  if (!take_all) {
+    if (tid == 0) { sh.bstar = 0; sh.above = 0; sh.TK = 0xffffffffu; sh.I = -1; }
+    uint32_t klo = 0xffffffffu, khi = 0u;
+    for (int j = tid; j < nvis; j += kTopkThreads) { uint32_t v = okey(s[j]); klo = min(klo, v); khi = max(khi, v); }
+    block_minmax(klo, khi, sh);
+    int above = 0;                          // entries known to rank above the current range
+    for (int iter = 0; iter < 4 && klo < khi; ++iter) {
+      for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0;
+      __syncthreads();
+      const uint32_t range = khi - klo;
+      const int shift = max(0, 32 - __clz((int)range) - 11);
+      for (int j = tid; j < nvis; j += kTopkThreads) {
+        uint32_t v = okey(s[j]);
+        if (v >= klo && v <= khi) atomicAdd(&sh.hist[(v - klo) >> shift], 1);
+      }
+      __syncthreads();
+      // thread t owns bins 2u+1 and 2u with u = 1023 - t, so the scan runs from the top bin down
+      const int u = kTopkThreads - 1 - tid;
+      const int hA = sh.hist[2 * u + 1], hB = sh.hist[2 * u];
+      int tot;
+      const int pre = block_excl_scan(hA + hB, sh.wsum, tot);   // entries in higher bins
+      const int need = k - above;
+      if (pre < need && pre + hA >= need) { sh.bstar = 2 * u + 1; sh.above = pre; }
+      else if (pre + hA < need && pre + hA + hB >= need) { sh.bstar = 2 * u; sh.above = pre + hA; }
+      __syncthreads();
+      const int bstar = min(max(sh.bstar, 0), kTopkBins - 1);
+      const int cnt = sh.hist[bstar];
+      above += sh.above;
+      uint32_t nlo = 0xffffffffu, nhi = 0u;
+      for (int j = tid; j < nvis; j += kTopkThreads) {
+        uint32_t v = okey(s[j]);
+        if (v >= klo && v <= khi && (int)((v - klo) >> shift) == bstar) { nlo = min(nlo, v); nhi = max(nhi, v); }
+      }
+      block_minmax(nlo, nhi, sh);
+      klo = nlo;
+      khi = nhi;
+      if (cnt <= kCandMax) break;
+    }
+    // candidates: keys in [klo, khi]; `need` of them are taken, best first
+    const int need = k - above;
+    if (klo == khi) {
+      // all candidates share one key: the need-th smallest index among them
+      TK = klo;
+      int base = 0;
+      for (int j0 = 0; j0 < nvis; j0 += kTopkThreads) {
+        const int j = j0 + tid;
+        const int f = (j < nvis && okey(s[j]) == klo) ? 1 : 0;
+        int tot;
+        const int pre = block_excl_scan(f, sh.wsum, tot);
+        if (f && base + pre == need - 1) sh.I = j;
+        base += tot;
+        if (base >= need) break;
+      }
+      __syncthreads();
+      I = sh.I;
+    } else {
+      if (tid == 0) sh.ccount = 0;
+      __syncthreads();
+      for (int j = tid; j < nvis; j += kTopkThreads) {
+        uint32_t v = okey(s[j]);
+        if (v >= klo && v <= khi) {
+          int slot = atomicAdd(&sh.ccount, 1);
+          if (slot < kCandMax) { sh.ckey[slot] = v; sh.cidx[slot] = j; }
+        }
+      }
+      __syncthreads();
+      const int c = min(sh.ccount, kCandMax);
+      for (int ci = tid; ci < c; ci += kTopkThreads) {
+        const uint32_t v = sh.ckey[ci];
+        const int ji = sh.cidx[ci];
+        int rank = 0;
+        for (int o = 0; o < c; ++o) {
+          const uint32_t vo = sh.ckey[o];
+          rank += (vo > v || (vo == v && sh.cidx[o] < ji)) ? 1 : 0;
+        }
+        if (rank == need - 1) { sh.TK = v; sh.I = ji; }
+      }
+      __syncthreads();
+      TK = sh.TK;
+      I = sh.I;
+    }
+  }
+  // ascending compaction of the selected entries
+  int base = 0;
+  for (int j0 = 0; j0 < nvis; j0 += kTopkThreads) {
+    const int j = j0 + tid;
+    int f = 0;
+    if (j < nvis) {
+      if (take_all) f = 1;
+      else { const uint32_t v = okey(s[j]); f = (v > TK || (v == TK && j <= I)) ? 1 : 0; }
+    }
+    int tot;
+    const int pre = block_excl_scan(f, sh.wsum, tot);
+    if (f && base + pre < k) out[base + pre] = j;
+    base += tot;
+  }
+  for (int p = base + tid; p < k; p += kTopkThreads) out[p] = -1;
+}
+
+hipError_t launch_topk(const IndexArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk, dim3(a.B * a.Tq), dim3(kTopkThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

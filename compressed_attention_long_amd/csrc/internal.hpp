@@ -1,0 +1,76 @@
+// Internal launch interfaces between the C ABI (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "../../include/csa.h"
+
+namespace csa {
+
+struct CompressArgs {
+  const void* kv;
+  const void* logits;
+  int64_t ld_tok, ld_seq;
+  int B, T_raw, first_row, n_new;
+  void* out;
+  float* scales;
+  const int64_t* pos0;
+  int dtype, cap, C, scale_block, window, stride;
+  const double* inv_freq;
+  int rope_dim;
+  int run;   // rows per lane group (set by the launcher)
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+struct IndexArgs {
+  const void* q_idx;      // bf16 [rows, Hi, Di]
+  const float* w;         // [rows, Hi]
+  const int64_t* q_pos;   // [rows]
+  int B, Tq, Hi, Di;
+  const void* keys;       // [B, cap, Di]
+  const float* key_scales;  // [B, cap] (fp8) or null
+  const int32_t* n_valid;
+  const int64_t* pos0;
+  int key_dtype, cap, window, stride;
+  int topk;
+  float* scores;          // [rows, cap]
+  int32_t* idx_out;       // [rows, topk]
+};
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
+hipError_t launch_topk(const IndexArgs& a, hipStream_t s);
+
+struct AttendArgs {
+  const void* q;          // bf16 [rows, H, 512]
+  const int64_t* q_pos;   // [rows]
+  int B, Tq, H;
+  // compressed KV cache
+  const void* kv;
+  const float* kv_scales;
+  const int32_t* kv_n_valid;
+  const int64_t* kv_pos0;
+  int kv_dtype, kv_cap, kv_scale_block, kv_window, kv_stride;
+  // selection (CSA) or dense (HCA)
+  const int32_t* idx;     // [rows, topk] (CSA)
+  int topk;
+  int csa_mode;           // 1: rows from idx (CSA); 0: every visible entry (HCA)
+  // window cache
+  const void* win;
+  const int32_t* win_n_valid;
+  const int64_t* win_pos0;
+  int win_cap, W;
+  const float* sink;
+  const double* inv_freq;
+  int rope_dim;
+  float scale_log2;       // softmax_scale * log2(e)
+  void* out;
+  int out_dtype;
+  float* lse;
+  // split-KV partials
+  int nsplit, slot_cap, slots_per_split;
+  float* part_o;          // [rows, nsplit, H, 512]
+  float* part_ml;         // [rows, nsplit, H, 2]
+};
+int attend_nsplit(int rows, int H, int slot_cap);
+size_t attend_workspace(int rows, int H, int slot_cap);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+}  // namespace csa

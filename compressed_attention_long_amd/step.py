@@ -1,0 +1,92 @@
+"""One attention-layer step of the CSA/HCA path on the GPU, through the C ABI.
+
+A step is what a layer does for one batch of new tokens:
+  1. compress the entries the new tokens complete (csa_compress, pooled rows);
+  2. write the new raw tokens, rotated, into the sliding-window cache
+     (csa_compress with window = stride = 1);
+  3. CSA only: score every visible entry with the lightning indexer and keep
+     the top-k (csa_index_topk);
+  4. attend (csa_attend over top-k + window, or hca_attend over every visible
+     entry + window).
+All buffers are allocated once, in __init__; run() only enqueues kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as ops
+
+
+def rope_inv_freq(theta: float, rope_dim: int, device) -> torch.Tensor:
+    """theta ** (-2i / rope_dim) for i < rope_dim / 2, fp64 (base 160,000 on the pages)."""
+    i = np.arange(rope_dim // 2, dtype=np.float64)
+    return torch.from_numpy(np.power(theta, -2.0 * i / rope_dim)).to(device)
+
+
+class LayerStep:
+    """Holds the caches and buffers of one layer for a workload and runs its step."""
+
+    def __init__(self, wl, tensors: dict, meta: dict, out_dtype=torch.bfloat16, theta: float = 160000.0,
+                 softmax_scale: Optional[float] = None):
+        self.wl = wl
+        self.t = tensors
+        self.meta = meta
+        dev = tensors["q"].device
+        self.device = dev
+        B = wl.B
+        self.inv_freq = rope_inv_freq(theta, wl.R, dev)
+        self.scale = 1.0 / math.sqrt(wl.D) if softmax_scale is None else softmax_scale
+        kv = tensors["kv_cache"]
+        self.kv = ops.Cache(kv, tensors["kv_n_valid"], tensors["kv_pos0"], wl.window, wl.stride,
+                            scales=tensors.get("kv_cache_scale"),
+                            scale_block=wl.kv_scale_block if wl.kv_dtype == "fp8" else 0)
+        self.win = ops.Cache(tensors["win_cache"], tensors["win_n_valid"], tensors["win_pos0"], 1, 1)
+        if wl.mode == "csa":
+            ks = tensors.get("k_idx_scale")
+            self.keys = ops.Cache(tensors["k_idx"], tensors["kv_n_valid"], tensors["kv_pos0"], wl.window,
+                                  wl.stride, scales=ks, scale_block=wl.Di if ks is not None else 0)
+            self.idx = torch.empty((B, wl.Tq, wl.topk), dtype=torch.int32, device=dev)
+            self.scores = torch.empty((B, wl.Tq, wl.E), dtype=torch.float32, device=dev)
+            ws = ops.csa_attend_workspace_bytes(B, wl.Tq, wl.H, wl.topk, wl.W)
+        else:
+            self.keys = None
+            ws = ops.hca_attend_workspace_bytes(B, wl.Tq, wl.H, wl.E, wl.W)
+        self.att_ws = ops.workspace(ws, dev)
+        self.out = torch.empty((B, wl.Tq, wl.H, wl.D), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((B, wl.Tq, wl.H), dtype=torch.float32, device=dev)
+        # raw tokens of this step: all rows for the compressor, the new tokens for the window
+        self.kv_raw = tensors["kv_raw"]
+        self.z_raw = tensors["z_raw"]
+        self.new_raw = self.kv_raw[:, self.kv_raw.shape[1] - meta["new_tok"]:]
+
+    def compress(self, stream=None):
+        m = self.meta
+        if m["n_new_entries"] > 0:
+            ops.compress(self.kv_raw, self.z_raw, self.kv, m["E_pre"], m["n_new_entries"], self.inv_freq,
+                         self.wl.R, stream)
+        ops.compress(self.new_raw, None, self.win, m["win_first_new"], m["new_tok"], self.inv_freq, self.wl.R,
+                     stream)
+
+    def index(self, stream=None):
+        wl = self.wl
+        ops.index_topk(self.t["q_idx"], self.t["w"], self.t["q_pos"], self.keys, wl.topk, self.idx,
+                       scores_out=self.scores, stream=stream)
+
+    def attend(self, stream=None):
+        wl = self.wl
+        if wl.mode == "csa":
+            ops.csa_attend(self.t["q"], self.t["q_pos"], self.kv, self.idx, self.win, wl.W, self.t["sink"],
+                           self.inv_freq, wl.R, self.scale, self.out, self.lse, self.att_ws, stream)
+        else:
+            ops.hca_attend(self.t["q"], self.t["q_pos"], self.kv, self.win, wl.W, self.t["sink"], self.inv_freq,
+                           wl.R, self.scale, self.out, self.lse, self.att_ws, stream)
+
+    def run(self, stream=None):
+        self.compress(stream)
+        if self.wl.mode == "csa":
+            self.index(stream)
+        self.attend(stream)

@@ -195,3 +195,57 @@ def decode_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, n_raw_
             out["kv_cache"] = d.normal((wl.B, E, wl.D))
         out["win_cache"] = d.normal((wl.B, wl.W, wl.D))
     return out
+
+
+def step_tensors(wl: Workload, device="cpu", seed: Optional[int] = None):
+    """Tensors of one timed step of `wl` (decode or prefill chunk), plain torch.
+
+    The stored caches of everything before the step are drawn; the step's own
+    raw tokens (the newest `window` tokens for decode, or the chunk plus the
+    overlap for prefill) are drawn as raw kv / pooling logits, so the step runs
+    the compressor, the raw-window write, the indexer, top-k and attention.
+    Geometry (positions are pos0 + raw index; one cache row per entry):
+      entries of the prefix:        E_pre = n_entries(N - Tq_new)
+      entries after the step:       E     = n_entries(N)
+      window cache rows:            the last W raw tokens before the step, then the step's tokens
+    """
+    seed = seed_for(wl.name) if seed is None else seed
+    d = Draw(seed, device)
+    B, D, Tq = wl.B, wl.D, wl.Tq
+    new_tok = Tq                                   # raw tokens that arrive in this step
+    E = wl.E
+    E_pre = wl.n_entries(wl.N - new_tok)
+    n_new_entries = E - E_pre
+    # raw rows needed to compress the new entries (the first one overlaps the prefix)
+    raw_first = E_pre * wl.stride                  # raw index of the first token of entry E_pre
+    T_raw = wl.N - raw_first
+    t = {}
+    t["kv_raw"] = d.normal((B, T_raw, D))
+    t["z_raw"] = d.normal((B, T_raw, D))
+    t["q"] = d.normal((B, Tq, wl.H, D), std=1.0 / math.sqrt(D))
+    if wl.mode == "csa":
+        t["q_idx"] = d.normal((B, Tq, wl.Hi, wl.Di), std=1.0 / math.sqrt(wl.Di))
+        if wl.idx_dtype == "fp8":
+            t["k_idx"], t["k_idx_scale"] = d.fp8_codes((B, E, wl.Di), wl.Di, std=1.0 / math.sqrt(wl.Di))
+        else:
+            t["k_idx"] = d.normal((B, E, wl.Di), std=1.0 / math.sqrt(wl.Di))
+        t["w"] = d.uniform((B, Tq, wl.Hi))
+    t["sink"] = d.normal((wl.H,), dtype=torch.float32)
+    if wl.kv_dtype == "fp8":
+        t["kv_cache"], t["kv_cache_scale"] = d.fp8_codes((B, E, D), wl.kv_scale_block)
+    else:
+        t["kv_cache"] = d.normal((B, E, D))
+    win_cap = wl.W + new_tok
+    t["win_cache"] = d.normal((B, win_cap, D))
+    dev = t["q"].device
+    t["kv_n_valid"] = torch.full((B,), E, dtype=torch.int32, device=dev)
+    t["kv_pos0"] = torch.full((B,), wl.pos0, dtype=torch.int64, device=dev)
+    # window cache row r holds raw position win_pos0 + r; the step writes rows W .. W+new_tok-1
+    win_pos0 = wl.pos0 + wl.N - new_tok - wl.W
+    t["win_n_valid"] = torch.full((B,), win_cap, dtype=torch.int32, device=dev)
+    t["win_pos0"] = torch.full((B,), win_pos0, dtype=torch.int64, device=dev)
+    q_pos = wl.pos0 + wl.N - new_tok + torch.arange(Tq, dtype=torch.int64, device=dev)
+    t["q_pos"] = q_pos.unsqueeze(0).repeat(B, 1).contiguous()
+    meta = dict(E=E, E_pre=E_pre, n_new_entries=n_new_entries, raw_first=raw_first, T_raw=T_raw,
+                win_cap=win_cap, win_first_new=wl.W, new_tok=new_tok)
+    return t, meta

@@ -1,0 +1,119 @@
+"""Host-only tests of the C ABI: the library loads, exports every declared entry
+point, and rejects bad arguments before touching the GPU.  No compute calls."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_attention_long_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+FAKE = 0x10000          # an aligned, never-dereferenced stand-in for a device pointer
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(csa_[a-z_0-9]+|hca_[a-z_0-9]+)\s*\(", src, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.csa_abi_version() == 1
+
+
+def cache(dtype=L.CSA_BF16, cap=64, C=512, window=8, stride=4, scales=True, sb=64):
+    return L.CCache(FAKE, FAKE if (dtype == L.CSA_FP8_E4M3 and scales) else None, FAKE, FAKE, dtype, cap, C,
+                    sb, window, stride)
+
+
+def rc_msg(rc):
+    return rc, L.last_error()
+
+
+def compress(out, kv=FAKE, logits=FAKE, ld_tok=512, ld_seq=512 * 64, B=1, T=64, first=0, n_new=4,
+             inv=FAKE, rope=64):
+    lib = L.load()
+    return rc_msg(lib.csa_compress(kv, logits, ld_tok, ld_seq, B, T, first, n_new, ctypes.byref(out), inv, rope, None))
+
+
+def test_compress_validation():
+    c = cache()
+    assert compress(c, kv=None)[0] == L.CSA_EINVAL
+    rc, msg = compress(c, logits=None)
+    assert rc == L.CSA_EINVAL and "logits" in msg
+    assert compress(c, T=15, n_new=4)[0] == L.CSA_EINVAL          # needs (4-1)*4 + 8 = 20 rows
+    assert compress(c, first=62, n_new=4)[0] == L.CSA_EINVAL      # past cap
+    assert compress(c, rope=63)[0] == L.CSA_EINVAL
+    assert compress(c, inv=None)[0] == L.CSA_EINVAL
+    assert compress(c, kv=FAKE + 4)[0] == L.CSA_EINVAL            # misaligned
+    assert compress(cache(C=520))[0] == L.CSA_ENOTSUP
+    assert compress(cache(dtype=7))[0] == L.CSA_ENOTSUP
+    assert compress(cache(dtype=L.CSA_FP8_E4M3, scales=False))[0] == L.CSA_EINVAL
+    assert compress(cache(dtype=L.CSA_FP8_E4M3, sb=24))[0] == L.CSA_EINVAL   # does not divide C
+    assert compress(cache(dtype=L.CSA_FP8_E4M3, sb=1024, C=1024), ld_tok=1024, ld_seq=1024 * 64)[0] == L.CSA_ENOTSUP
+    # nothing to do is a success with no launch
+    rc, msg = compress(c, n_new=0)
+    assert rc == L.CSA_OK and msg == ""
+
+
+def index(keys, topk=16, B=1, Tq=1, Hi=64, ws=None, wsb=0, scores=None, q=FAKE):
+    lib = L.load()
+    return rc_msg(lib.csa_index_topk(q, FAKE, FAKE, B, Tq, Hi, ctypes.byref(keys), topk, FAKE, scores, ws, wsb, None))
+
+
+def test_index_topk_validation():
+    k = cache(C=128)
+    assert index(k, topk=65)[0] == L.CSA_EINVAL                    # topk > cap
+    assert index(k, topk=0)[0] == L.CSA_EINVAL
+    assert index(k, Hi=65)[0] == L.CSA_ENOTSUP
+    assert index(cache(C=256))[0] == L.CSA_ENOTSUP
+    assert index(cache(C=128, dtype=L.CSA_FP8_E4M3, sb=64))[0] == L.CSA_ENOTSUP
+    need = L.index_topk_workspace_bytes(1, 1, 64, 64, 16)
+    assert need >= 64 * 4
+    rc, msg = index(k, ws=FAKE, wsb=need - 1)
+    assert rc == L.CSA_EWORKSPACE and str(need) in msg
+    assert index(k, ws=FAKE + 16, wsb=need)[0] == L.CSA_EINVAL     # misaligned workspace
+    assert index(k, q=None)[0] == L.CSA_EINVAL
+    assert index(k, B=0)[0] == L.CSA_OK
+
+
+def attend(kv, win, topk=16, H=128, W=128, ws=None, wsb=0, out_dtype=L.CSA_FP32, rope=64, hca=False, B=32):
+    lib = L.load()
+    if hca:
+        return rc_msg(lib.hca_attend(FAKE, FAKE, B, 1, H, ctypes.byref(kv), ctypes.byref(win), W, FAKE, FAKE, rope,
+                                     0.04, FAKE, out_dtype, None, ws, wsb, None))
+    return rc_msg(lib.csa_attend(FAKE, FAKE, B, 1, H, ctypes.byref(kv), FAKE, topk, ctypes.byref(win), W, FAKE,
+                                 FAKE, rope, 0.04, FAKE, out_dtype, None, ws, wsb, None))
+
+
+def test_attend_validation():
+    kv = cache(cap=2048)
+    win = cache(cap=160, window=1, stride=1)
+    assert attend(kv, win, topk=4096)[0] == L.CSA_EINVAL
+    assert attend(kv, cache(cap=160, window=2, stride=1))[0] == L.CSA_EINVAL
+    assert attend(cache(cap=2048, C=256), win)[0] == L.CSA_ENOTSUP
+    assert attend(kv, win, out_dtype=9)[0] == L.CSA_ENOTSUP
+    assert attend(kv, win, W=-1)[0] == L.CSA_EINVAL
+    need = L.csa_attend_workspace_bytes(32, 1, 128, 16, 128)
+    assert need > 0                                               # 32 rows cannot fill the GPU: split
+    assert attend(kv, win, ws=FAKE, wsb=need - 1)[0] == L.CSA_EWORKSPACE
+    assert attend(kv, win, ws=None, wsb=0)[0] == L.CSA_EWORKSPACE
+    hneed = L.hca_attend_workspace_bytes(32, 1, 128, 2048, 128)
+    assert attend(kv, win, hca=True, ws=FAKE, wsb=hneed - 256)[0] == L.CSA_EWORKSPACE
+    assert attend(kv, win, B=0)[0] == L.CSA_OK
+
+
+def test_workspace_sizes_scale_with_work():
+    assert L.csa_attend_workspace_bytes(4096, 1, 128, 1024, 128) == 0   # enough rows: no split partials
+    a = L.hca_attend_workspace_bytes(16, 1, 128, 8192, 128)
+    b = L.hca_attend_workspace_bytes(16, 1, 128, 4096, 128)
+    assert a > 0 and b > 0
+    assert L.index_topk_workspace_bytes(32, 1, 64, 16383, 1024) >= 32 * 16383 * 4

@@ -1,0 +1,102 @@
+"""GPU parity at the page-shaped workload sizes, in the launch configuration the
+benchmark times (one LayerStep: compress, window write, indexer + top-k, attend).
+
+The oracle recomputes sampled query rows one by one from the same device tensors
+(the step's inputs and the cache bytes the step wrote); bars: tests/gpu_common.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import csa_inputs as ci
+from compressed_attention_long_amd.step import LayerStep
+from oracle import csa_oracle as O
+
+from gpu_common import (check_attention, check_bf16_rows, check_scores, check_topk, np64, oracle_rows_csa,
+                        oracle_rows_hca, pool_error_bound, stored_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_step(name):
+    wl = ci.WORKLOADS[name]
+    print(f"\n[gpu case] full-size step {name}", flush=True)
+    t, meta = ci.step_tensors(wl, DEV)
+    step = LayerStep(wl, t, meta, out_dtype=torch.float32)
+    step.run()
+    torch.cuda.synchronize()
+    return wl, t, meta, step
+
+
+def check_rows(wl, t, meta, step, samples):
+    fo = O.rope_inv_freq(160000.0, wl.R)
+    kv_block = wl.kv_scale_block
+    ent_pos_all = O.entry_positions(wl.pos0, wl.E, wl.window, wl.stride)
+    win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
+    sink = np64(t["sink"])
+    for b, tq in samples:
+        qp = int(t["q_pos"][b, tq])
+        win_rows = np64(step.win.data[b])
+        sc_b = step.kv.scales[b] if step.kv.scales is not None else None
+        if wl.mode == "csa":
+            ks = t.get("k_idx_scale")
+            keys = stored_rows(t["k_idx"][b], ks[b] if ks is not None else None, wl.Di)
+            so = O.index_scores(np64(t["q_idx"][b, tq]), np64(t["w"][b, tq]), keys)
+            vis = O.visible_mask(ent_pos_all, qp)
+            sg = step.scores[b, tq].cpu().numpy()
+            check_scores(sg, so, vis, f"{wl.name} b={b} t={tq}")
+            ig = step.idx[b, tq].cpu().numpy()
+            check_topk(ig, sg, so, vis, wl.topk, f"{wl.name} b={b} t={tq}")
+            sel = torch.from_numpy(ig[ig >= 0].astype(np.int64)).to(DEV)
+            kv_sel = stored_rows(step.kv.data[b][sel], sc_b[sel] if sc_b is not None else None, kv_block)
+            X = oracle_rows_csa(kv_sel, np.arange(len(sel)), win_rows, win_pos, qp, wl.W, len(sel))
+        else:
+            kv_rows = stored_rows(step.kv.data[b], sc_b, kv_block)
+            X = oracle_rows_hca(kv_rows, ent_pos_all, win_rows, win_pos, qp, wl.W)
+        o, l = O.attend(np64(t["q"][b, tq]), qp, X, sink, step.scale, fo)
+        check_attention(np64(step.out[b, tq]), o, f"{wl.name} b={b} t={tq}")
+        np.testing.assert_allclose(step.lse[b, tq].cpu().numpy(), l, atol=1e-4)
+
+
+def check_new_entry(wl, t, meta, step, b):
+    """The entries this step compressed, against the oracle on the same raw rows."""
+    fo = O.rope_inv_freq(160000.0, wl.R)
+    first = meta["E_pre"]
+    n = meta["n_new_entries"]
+    ent, _ = O.compress(np64(t["kv_raw"][b]), np64(t["z_raw"][b]), wl.window, wl.stride,
+                        wl.pos0 + first * wl.stride, fo)
+    got = stored_rows(step.kv.data[b, first:first + n],
+                      step.kv.scales[b, first:first + n] if step.kv.scales is not None else None, wl.kv_scale_block)
+    if wl.kv_dtype == "fp8":
+        codes, sc = O.fp8_block_quantize(ent[:n], wl.kv_scale_block)
+        ref = O.fp8_block_dequantize(codes, sc, wl.kv_scale_block)
+        assert np.abs(got - ref).max() <= 2 * np.abs(ref).max() / 448 * 8 / 16 + 1e-6
+    else:
+        bound = pool_error_bound(np64(t["kv_raw"][b]), np64(t["z_raw"][b]), wl.window, wl.stride, wl.R)[:n]
+        check_bf16_rows(got, ent[:n], bound, f"{wl.name} new entries b={b}")
+
+
+def test_v4pro_csa_decode_65k():
+    wl, t, meta, step = run_step("v4pro_csa_decode_65k")
+    check_new_entry(wl, t, meta, step, 0)
+    check_new_entry(wl, t, meta, step, 31)
+    check_rows(wl, t, meta, step, [(0, 0), (17, 0), (31, 0)])
+
+
+def test_v4pro_hca_decode_1m():
+    wl, t, meta, step = run_step("v4pro_hca_decode_1m")
+    check_new_entry(wl, t, meta, step, 3)
+    check_rows(wl, t, meta, step, [(0, 0), (15, 0)])
+
+
+def test_v4flash_csa_decode_1m_fp8():
+    wl, t, meta, step = run_step("v4flash_csa_decode_1m_fp8")
+    check_new_entry(wl, t, meta, step, 1)
+    check_rows(wl, t, meta, step, [(0, 0), (3, 0)])
+
+
+def test_v4pro_csa_prefill_4k_on_131k():
+    wl, t, meta, step = run_step("v4pro_csa_prefill_4k_on_131k")
+    check_new_entry(wl, t, meta, step, 0)
+    check_rows(wl, t, meta, step, [(0, 0), (0, 1), (0, 2047), (0, 4095)])

@@ -1,0 +1,349 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Sizes span several tiles and ragged tails; edge cases: fewer visible entries
+than k, a window cut by the start of the stream, heads fewer than one MFMA
+block, split and unsplit attention, prefill rows with causal visibility, fp8
+caches, tied scores, bf16 output and bitwise determinism.  Bars: tests/gpu_common.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import csa_inputs as ci
+from compressed_attention_long_amd import _lib as ops
+from compressed_attention_long_amd.step import rope_inv_freq
+from oracle import csa_oracle as O
+
+from gpu_common import (LSE_TOL, check_attention, check_bf16_rows, check_scores, check_topk, np64,
+                        oracle_rows_csa, oracle_rows_hca, pool_error_bound, stored_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu case] {request.node.name}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def inv_freq_pair(R=64):
+    return rope_inv_freq(160000.0, R, DEV), O.rope_inv_freq(160000.0, R)
+
+
+# ---------------------------------------------------------------- compressor
+
+@pytest.mark.parametrize("window,stride,dtype,B,n_new,first,R", [
+    (8, 4, "bf16", 2, 1023, 0, 64),      # CSA, many rows (run mode), tiny-config length
+    (8, 4, "bf16", 3, 37, 5, 64),        # ragged row count, offset first row
+    (8, 4, "bf16", 1, 1, 9, 64),         # one decode-step entry
+    (128, 128, "bf16", 2, 9, 1, 64),     # HCA geometry
+    (1, 1, "bf16", 2, 200, 3, 64),       # raw-window write
+    (8, 4, "fp8", 2, 333, 0, 64),        # fp8 cache, per-64 scales
+    (128, 128, "fp8", 1, 5, 2, 64),
+    (8, 4, "bf16", 1, 50, 0, 0),         # no rotation
+])
+def test_compress_parity(window, stride, dtype, B, n_new, first, R):
+    d = ci.Draw(100 + n_new + window, "cpu")
+    T = (n_new - 1) * stride + window + 3
+    kv = d.normal((B, T, 512))
+    z = d.normal((B, T, 512))
+    cap = first + n_new + 2
+    pos0_list = [1 + 977 * b for b in range(B)]
+    pos0_list[-1] = 1048576 - (first + n_new) * stride - window      # large angles
+    pos0 = torch.tensor(pos0_list, dtype=torch.int64)
+    sb = 64
+    if dtype == "bf16":
+        data = torch.full((B, cap, 512), 12345, dtype=torch.int16).view(torch.bfloat16)
+        scales = None
+    else:
+        data = torch.full((B, cap, 512), 0xAA, dtype=torch.uint8)
+        scales = torch.full((B, cap, 512 // sb), -1.0, dtype=torch.float32)
+    dg = data.to(DEV)
+    sg = scales.to(DEV) if scales is not None else None
+    cache = ops.Cache(dg, torch.full((B,), cap, dtype=torch.int32, device=DEV), pos0.to(DEV), window, stride,
+                      scales=sg, scale_block=sb if dtype == "fp8" else 0)
+    fg, fo = inv_freq_pair(R) if R else (None, np.zeros(0))
+    ops.compress(kv.to(DEV), z.to(DEV) if window > 1 else None, cache, first, n_new, fg, R)
+    torch.cuda.synchronize()
+    out = dg.cpu()
+    for b in range(B):
+        ent, _ = O.compress(np64(kv[b]), np64(z[b]), window, stride, pos0_list[b] + first * stride, fo)
+        ref = ent[:n_new]
+        if dtype == "bf16":
+            got = np64(out[b, first:first + n_new])
+            bound = pool_error_bound(np64(kv[b]), np64(z[b]), window, stride, R)[:n_new]
+            check_bf16_rows(got, ref, bound, f"b={b}")
+            untouched = torch.cat([out[b, :first], out[b, first + n_new:]]).view(torch.int16)
+            assert torch.all(untouched == 12345)
+        else:
+            codes_o, sc_o = O.fp8_block_quantize(ref, sb)
+            sc_g = sg.cpu()[b, first:first + n_new].numpy()
+            np.testing.assert_allclose(sc_g, sc_o, rtol=1e-6, atol=0)
+            cg = out[b, first:first + n_new].numpy()
+            vg, vo = O.fp8_e4m3_decode(cg), O.fp8_e4m3_decode(codes_o)
+            step = np.ldexp(1.0, np.maximum(np.frexp(np.maximum(np.abs(vg), np.abs(vo)))[1] - 4, -9))
+            assert np.all(np.abs(vg - vo) <= step), f"b={b}: fp8 codes more than one step apart"
+            assert np.mean(cg == codes_o) > 0.99
+            assert torch.all(out[b, :first] == 0xAA) and torch.all(out[b, first + n_new:] == 0xAA)
+
+
+# ---------------------------------------------------------------- indexer + top-k
+
+def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
+    d = ci.Draw(seed, "cpu")
+    if fp8:
+        codes, sc = d.fp8_codes((B, cap, 128), 128, std=1 / math.sqrt(128))
+        c = ops.Cache(codes.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV),
+                      torch.tensor(pos0, dtype=torch.int64, device=DEV), window, stride,
+                      scales=sc.to(DEV), scale_block=128)
+        ref = O.fp8_block_dequantize(codes.numpy(), sc.numpy(), 128)
+    else:
+        k = d.normal((B, cap, 128), std=1 / math.sqrt(128))
+        c = ops.Cache(k.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV),
+                      torch.tensor(pos0, dtype=torch.int64, device=DEV), window, stride)
+        ref = np64(k)
+    return c, ref
+
+
+@pytest.mark.parametrize("B,Tq,Hi,cap,n_valid,fp8,topk,qpos_of", [
+    (1, 1, 8, 1023, [1023], False, 256, "end"),               # tiny decode shape
+    (3, 1, 64, 3010, [3000, 2500, 10], True, 1024, "end"),     # ragged caches, one row with < k visible
+    (2, 5, 16, 700, [700, 650], False, 100, "causal"),         # prefill rows: causal visibility
+    (1, 2, 48, 1500, [1500], True, 1, "end"),                  # k = 1, Hi not a multiple of 64
+    (2, 1, 64, 20000, [20000, 19999], True, 1024, "end"),      # spans many blocks
+])
+def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
+    d = ci.Draw(200 + cap, "cpu")
+    q_idx = d.normal((B, Tq, Hi, 128), std=1 / math.sqrt(128))
+    w = d.uniform((B, Tq, Hi))
+    pos0 = [1, 40][:B] + [1] * max(0, B - 2)
+    keys, kref = _keys_cache(B, cap, fp8, 300 + cap, n_valid, pos0)
+    ent_pos = [O.entry_positions(pos0[b], cap, 8, 4) for b in range(B)]
+    if qpos_of == "end":
+        qp = np.array([[ent_pos[b][n_valid[b] - 1] + t for t in range(Tq)] for b in range(B)])
+    else:
+        qp = np.array([[ent_pos[b][0] + (t * (cap * 4)) // Tq for t in range(Tq)] for b in range(B)])
+    q_pos = torch.tensor(qp, dtype=torch.int64, device=DEV)
+    idx = torch.empty((B, Tq, topk), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, Tq, cap), dtype=torch.float32, device=DEV)
+    ops.index_topk(q_idx.to(DEV), w.to(DEV), q_pos, keys, topk, idx, scores_out=scores)
+    torch.cuda.synchronize()
+    sg, ig = scores.cpu().numpy(), idx.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            vis = O.visible_mask(ent_pos[b], qp[b, t]) & (np.arange(cap) < n_valid[b])
+            so = O.index_scores(np64(q_idx[b, t]), np64(w[b, t]), kref[b])
+            check_scores(sg[b, t], so, vis, f"b={b} t={t}")
+            check_topk(ig[b, t], sg[b, t], so, vis, topk, f"b={b} t={t}")
+    # workspace instead of scores_out gives the same selection
+    ws = ops.workspace(ops.index_topk_workspace_bytes(B, Tq, Hi, cap, topk), DEV)
+    idx2 = torch.empty_like(idx)
+    ops.index_topk(q_idx.to(DEV), w.to(DEV), q_pos, keys, topk, idx2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+
+
+def test_topk_all_scores_tied():
+    # zero indexer queries: every visible score is 0, so the k smallest indices win
+    B, cap, topk = 2, 5000, 777
+    keys, _ = _keys_cache(B, cap, False, 11, [5000, 4000], [1, 1])
+    q_idx = torch.zeros((B, 1, 64, 128), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones((B, 1, 64), dtype=torch.float32, device=DEV)
+    q_pos = torch.tensor([[1 + 4 * 4999 + 7], [1 + 4 * 3999 + 7]], dtype=torch.int64, device=DEV)
+    idx = torch.empty((B, 1, topk), dtype=torch.int32, device=DEV)
+    ops.index_topk(q_idx, w, q_pos, keys, topk, idx, workspace=ops.workspace(
+        ops.index_topk_workspace_bytes(B, 1, 64, cap, topk), DEV))
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert idx[b, 0].cpu().tolist() == list(range(topk))
+
+
+def test_topk_clustered_scores():
+    # scores crowded into ~3000 ulps of one binade, with many exact duplicates:
+    # score = 1 + lo with lo = bf16(m * 2^-23), m < 3000 (exact in fp32)
+    cap, topk = 30000, 1024
+    m = np.random.default_rng(5).integers(0, 3000, size=cap)
+    kt = torch.zeros((1, cap, 128), dtype=torch.bfloat16)
+    kt[0, :, 0] = 1.0
+    kt[0, :, 1] = torch.from_numpy(m * 2.0 ** -23).to(torch.bfloat16)
+    keys = ops.Cache(kt.to(DEV), torch.tensor([cap], dtype=torch.int32, device=DEV),
+                     torch.tensor([1], dtype=torch.int64, device=DEV), 8, 4)
+    q_idx = torch.zeros((1, 1, 1, 128), dtype=torch.bfloat16)
+    q_idx[..., 0] = 1.0
+    q_idx[..., 1] = 1.0
+    w = torch.ones((1, 1, 1), dtype=torch.float32, device=DEV)
+    q_pos = torch.tensor([[1 + 4 * (cap - 1) + 7]], dtype=torch.int64, device=DEV)
+    idx = torch.empty((1, 1, topk), dtype=torch.int32, device=DEV)
+    scores = torch.empty((1, 1, cap), dtype=torch.float32, device=DEV)
+    ops.index_topk(q_idx.to(DEV), w, q_pos, keys, topk, idx, scores_out=scores)
+    torch.cuda.synchronize()
+    sg = scores[0, 0].cpu().numpy()
+    ref = 1.0 + np64(kt[0, :, 1])
+    np.testing.assert_array_equal(sg.astype(np.float64), ref)
+    assert 100 < len(np.unique(sg)) < cap // 5
+    exact = O.topk_select(ref, np.ones(cap, bool), topk)
+    assert np.array_equal(idx[0, 0].cpu().numpy(), exact)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, qmul, seed, out_dtype="fp32",
+                 win_start=None):
+    d = ci.Draw(seed, "cpu")
+    q = d.normal((B, Tq, H, 512), std=qmul / math.sqrt(512))
+    sink = d.normal((H,), dtype=torch.float32)
+    if kv_fp8:
+        codes, sc = d.fp8_codes((B, cap, 512), 64)
+        kv = ops.Cache(codes.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV), None, 8, 4,
+                       scales=sc.to(DEV), scale_block=64)
+        kv_ref = O.fp8_block_dequantize(codes.numpy(), sc.numpy(), 64)
+    else:
+        kvt = d.normal((B, cap, 512))
+        kv = ops.Cache(kvt.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV), None, 8, 4)
+        kv_ref = np64(kvt)
+    if mode == "hca":
+        kv.window, kv.stride = 128, 128
+    kv_pos0 = [1 + 1000 * b for b in range(B)]
+    kv.pos0 = torch.tensor(kv_pos0, dtype=torch.int64, device=DEV)
+    ent_pos = [O.entry_positions(kv_pos0[b], cap, kv.window, kv.stride) for b in range(B)]
+    # query positions: the newest token sits right after the last valid entry (prefill rows step back)
+    qp = np.array([[ent_pos[b][max(n_valid[b], 1) - 1] + 1 - (Tq - 1 - t) * 3 for t in range(Tq)]
+                   for b in range(B)])
+    wt = d.normal((B, win_cap, 512))
+    wpos0 = [int(qp[b, -1]) - win_cap + 1 if win_start is None else win_start for b in range(B)]
+    win = ops.Cache(wt.to(DEV), torch.tensor([win_cap] * B, dtype=torch.int32, device=DEV),
+                    torch.tensor(wpos0, dtype=torch.int64, device=DEV), 1, 1)
+    q_pos = torch.tensor(qp, dtype=torch.int64, device=DEV)
+    fg, fo = inv_freq_pair(64)
+    odt = torch.float32 if out_dtype == "fp32" else torch.bfloat16
+    out = torch.empty((B, Tq, H, 512), dtype=odt, device=DEV)
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
+    idx = None
+    if mode == "csa":
+        rng = np.random.default_rng(seed)
+        idx_np = np.full((B, Tq, topk), -1, dtype=np.int32)
+        for b in range(B):
+            for t in range(Tq):
+                nvis = int((ent_pos[b][:n_valid[b]] <= qp[b, t]).sum())
+                take = min(topk, nvis)
+                idx_np[b, t, :take] = np.sort(rng.choice(nvis, size=take, replace=False))
+        idx = torch.from_numpy(idx_np).to(DEV)
+        ws = ops.workspace(ops.csa_attend_workspace_bytes(B, Tq, H, topk, W), DEV)
+        ops.csa_attend(q.to(DEV), q_pos, kv, idx, win, W, sink.to(DEV), fg, 64, scale, out, lse, ws)
+    else:
+        ws = ops.workspace(ops.hca_attend_workspace_bytes(B, Tq, H, cap, W), DEV)
+        ops.hca_attend(q.to(DEV), q_pos, kv, win, W, sink.to(DEV), fg, 64, scale, out, lse, ws)
+    torch.cuda.synchronize()
+    og, lg = np64(out), lse.cpu().numpy()
+    worst = 0.0
+    win_ref = np64(wt)
+    for b in range(B):
+        wpos = wpos0[b] + np.arange(win_cap)
+        for t in range(Tq):
+            if mode == "csa":
+                X = oracle_rows_csa(kv_ref[b], idx.cpu().numpy()[b, t], win_ref[b], wpos, qp[b, t], W, n_valid[b])
+            else:
+                X = oracle_rows_hca(kv_ref[b][:n_valid[b]], ent_pos[b][:n_valid[b]], win_ref[b], wpos,
+                                    qp[b, t], W)
+            o, l = O.attend(np64(q[b, t]), qp[b, t], X, np64(sink), scale, fo)
+            if out_dtype == "fp32":
+                worst = max(worst, check_attention(og[b, t], o, f"b={b} t={t}"))
+            np.testing.assert_allclose(lg[b, t], l, atol=LSE_TOL, rtol=0)
+    return out, lse, worst
+
+
+@pytest.mark.parametrize("mode,B,Tq,H,cap,n_valid,fp8,topk,W,win_cap,scale,qmul", [
+    ("csa", 1, 1, 8, 1023, [1023], False, 256, 128, 129, 1 / math.sqrt(512), 1.0),   # tiny decode shape
+    ("csa", 2, 1, 128, 3000, [3000, 2000], False, 1024, 128, 129, 1 / math.sqrt(512), 1.0),  # splits
+    ("csa", 2, 1, 128, 3000, [3000, 2000], False, 1024, 128, 129, 1.0, 8.0),           # peaked softmax
+    ("csa", 2, 3, 64, 900, [900, 40], True, 300, 128, 140, 1 / math.sqrt(512), 1.0),   # fp8 KV, < k visible
+    ("csa", 1, 1, 16, 500, [500], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),        # window only
+    ("csa", 4, 64, 64, 600, [600] * 4, False, 200, 128, 200, 0.1, 2.0),               # 256 rows: no split
+    ("hca", 2, 1, 128, 700, [700, 300], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),
+    # fp8 rows are staged in LDS as bf16 (code x scale rounded): sharper softmax than this
+    # exceeds the bar (CPU emulation of that rounding: 1.1% at scale 1, 5.8% at scale 1 with q x 4)
+    ("hca", 1, 2, 128, 64, [64], True, 0, 128, 129, 1 / math.sqrt(512), 4.0),        # fp8, sharper q
+    ("hca", 3, 1, 24, 300, [300, 299, 1], False, 0, 0, 1, 1 / math.sqrt(512), 1.0),   # no window, H < 32
+])
+def test_attend_parity(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul):
+    _attend_case(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul, seed=400 + cap + H)
+
+
+def test_attend_window_cut_by_stream_start():
+    # the window cache starts 40 tokens before the query: only 41 window rows exist
+    _attend_case("csa", 2, 1, 64, 200, [10, 10], False, 8, 128, 41, 1 / math.sqrt(512), 1.0, seed=9)
+
+
+def test_attend_bf16_output_and_determinism():
+    args = ("csa", 2, 1, 128, 2000, [2000, 1800], False, 1024, 128, 129, 1 / math.sqrt(512), 1.0)
+    o32, l32, _ = _attend_case(*args, seed=77)
+    o32b, l32b, _ = _attend_case(*args, seed=77)
+    assert torch.equal(o32, o32b) and torch.equal(l32, l32b)        # bitwise deterministic
+    o16, _, _ = _attend_case(*args, seed=77, out_dtype="bf16")
+    ref = o32.double()
+    spacing = torch.ldexp(torch.ones_like(ref), torch.frexp(ref.abs())[1] - 8)
+    assert torch.all((o16.double() - ref).abs() <= spacing)
+
+
+# ---------------------------------------------------------------- tiny decode from raw tokens
+
+def test_tiny_csa_decode_end_to_end():
+    """The tiny decode workload (4,096 raw tokens, 8 heads, top-256) through the whole path."""
+    wl = ci.WORKLOADS["tiny_csa_decode"]
+    inp = ci.decode_inputs(wl, "cpu")
+    N, B = wl.N, wl.B
+    E = wl.E
+    fg, fo = inv_freq_pair(wl.R)
+    kv, z = inp["kv"].to(DEV), inp["z"].to(DEV)
+    one = lambda v, dt: torch.tensor([v], dtype=dt, device=DEV)
+    cache = ops.Cache(torch.empty((B, E, 512), dtype=torch.bfloat16, device=DEV), one(E, torch.int32),
+                      one(wl.pos0, torch.int64), 8, 4)
+    ops.compress(kv, z, cache, 0, E, fg, wl.R)
+    win = ops.Cache(torch.empty((B, wl.W, 512), dtype=torch.bfloat16, device=DEV), one(wl.W, torch.int32),
+                    one(wl.pos0 + N - wl.W, torch.int64), 1, 1)
+    ops.compress(kv[:, N - wl.W:], None, win, 0, wl.W, fg, wl.R)
+    keys = ops.Cache(inp["k_idx"].to(DEV), one(E, torch.int32), one(wl.pos0, torch.int64), 8, 4)
+    q_pos = torch.tensor([[wl.q_pos]], dtype=torch.int64, device=DEV)
+    assert wl.q_pos == 4096
+    idx = torch.empty((B, 1, wl.topk), dtype=torch.int32, device=DEV)
+    scores = torch.empty((B, 1, E), dtype=torch.float32, device=DEV)
+    ops.index_topk(inp["q_idx"].to(DEV), inp["w"].to(DEV), q_pos, keys, wl.topk, idx, scores_out=scores)
+    out = torch.empty((B, 1, wl.H, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((B, 1, wl.H), dtype=torch.float32, device=DEV)
+    ws = ops.workspace(ops.csa_attend_workspace_bytes(B, 1, wl.H, wl.topk, wl.W), DEV)
+    scale = 1 / math.sqrt(512)
+    ops.csa_attend(inp["q"].to(DEV), q_pos, cache, idx, win, wl.W, inp["sink"].to(DEV), fg, wl.R, scale, out, lse, ws)
+    torch.cuda.synchronize()
+
+    # oracle, from the same raw tokens
+    kv64, z64 = np64(inp["kv"][0]), np64(inp["z"][0])
+    ent, ep = O.compress(kv64, z64, 8, 4, wl.pos0, fo)
+    assert ent.shape[0] == 1023
+    got = np64(cache.data[0])
+    check_bf16_rows(got, ent, pool_error_bound(kv64, z64, 8, 4, wl.R), "tiny entries")
+    raw, rp = O.compress(kv64, z64, 1, 1, wl.pos0, fo)
+    check_bf16_rows(np64(win.data[0]), raw[N - wl.W:],
+                    pool_error_bound(kv64, z64, 1, 1, wl.R)[N - wl.W:], "tiny window")
+    keys64 = np64(inp["k_idx"][0])
+    so = O.index_scores(np64(inp["q_idx"][0, 0]), np64(inp["w"][0, 0]), keys64)
+    vis = O.visible_mask(ep, wl.q_pos)
+    assert vis.all()
+    sg = scores[0, 0].cpu().numpy()
+    check_scores(sg, so, vis, "tiny")
+    ig = idx[0, 0].cpu().numpy()
+    ndiff = check_topk(ig, sg, so, vis, wl.topk, "tiny")
+    # attention on the GPU's selection and stored bytes
+    X = oracle_rows_csa(got, ig, np64(win.data[0]), rp[N - wl.W:], wl.q_pos, wl.W, E)
+    o, l = O.attend(np64(inp["q"][0, 0]), wl.q_pos, X, np64(inp["sink"]), scale, fo)
+    check_attention(np64(out[0, 0]), o, "tiny on GPU selection")
+    np.testing.assert_allclose(lse[0, 0].cpu().numpy(), l, atol=LSE_TOL)
+    # and the all-oracle path (fp64 entries, oracle selection) when the selections agree
+    if ndiff == 0:
+        o2, _, sel, _, _ = O.csa_query(np64(inp["q"][0, 0]), wl.q_pos, np64(inp["q_idx"][0, 0]),
+                                       np64(inp["w"][0, 0]), ent, ep, keys64, raw, rp, np64(inp["sink"]),
+                                       wl.topk, scale, fo, wl.W)
+        check_attention(np64(out[0, 0]), o2, "tiny end to end")
