@@ -169,7 +169,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v4pro_csa_decode_65k")
     ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8",
-                    help="comma-separated extra workloads measured into 'extra' ('' for none)")
+                    help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
@@ -221,7 +221,7 @@ def main():
              "layers_rotated": tm["layers"], "pages_config_context": {
                  "layers": 61, "csa_layers": 30, "hca_layers": 31, "heads": 128, "head_dim": 512,
                  "index_topk": 1024, "sliding_window": 128}}
-    for name in [x for x in args.extra.split(",") if x]:
+    for name in [x for x in args.extra.split(",") if x and x != "none"]:
         w2 = ci.WORKLOADS[name]
         print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
         t2 = time_workload(w2, max(10, args.steps // 2), args.warmup, torch)

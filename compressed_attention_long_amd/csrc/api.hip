@@ -185,12 +185,12 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int 
 
 size_t csa_attend_workspace_bytes(int B, int Tq, int H, int topk, int W) {
   if (B <= 0 || Tq <= 0 || H <= 0) return 0;
-  return csa::attend_workspace(B * Tq, H, topk + (W > 0 ? W : 0));
+  return csa::attend_workspace(B * Tq, H, topk + (W > 0 ? W : 0), true);
 }
 
 size_t hca_attend_workspace_bytes(int B, int Tq, int H, int cap, int W) {
   if (B <= 0 || Tq <= 0 || H <= 0) return 0;
-  return csa::attend_workspace(B * Tq, H, cap + (W > 0 ? W : 0));
+  return csa::attend_workspace(B * Tq, H, cap + (W > 0 ? W : 0), false);
 }
 
 static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int H, const csa_cache_t* kv,
@@ -222,7 +222,7 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   if (rc) return rc;
   const int rows = B * Tq;
   const int slot_cap = (csa_mode ? topk : kv->cap) + W;
-  const size_t need = csa::attend_workspace(rows, H, slot_cap);
+  const size_t need = csa::attend_workspace(rows, H, slot_cap, csa_mode);
   if (need > 0) {
     REQUIRE(workspace != nullptr && workspace_bytes >= need, CSA_EWORKSPACE,
             "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
@@ -259,7 +259,7 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   a.lse = lse_out;
   a.slot_cap = slot_cap;
   if (need > 0) {
-    const int ns = csa::attend_nsplit(rows, H, slot_cap);
+    const int ns = csa::attend_nsplit(rows, H, slot_cap, csa_mode);
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = a.part_o + (size_t)rows * ns * H * 512;
   }

@@ -20,7 +20,8 @@
 //    contraction;
 //  * the V^T operand is read from the same row-major LDS tile with the gfx950
 //    transposing LDS load (ds_read_b64_tr_b16), so no transposed copy is stored;
-//  * the sink enters as the initial running maximum and a weight of one in split 0;
+//  * the sink joins the denominator once, in the epilogue (one split) or the split merge;
+//  * lazy rescaling: the reference maximum moves only when a tile exceeds it by 2^8;
 //  * several splits of the row set run in parallel when the query rows alone cannot
 //    fill the GPU; their (max, sum, unnormalised output) partials are merged by
 //    k_attend_combine.  With one split the kernel normalises, rotates and stores.
@@ -35,6 +36,9 @@ constexpr int kTile = 32;           // rows per LDS tile
 constexpr int kD = 512;             // channels (head dim)
 constexpr int kPitch = 520;         // bf16 per LDS row: 1040 B, rows land 4 banks apart
 constexpr int kTargetBlocks = 256;  // split until the grid has about this many blocks
+constexpr int kSlotChunk = 2048;    // CSA: slots whose row index is staged in LDS at a time
+constexpr int kBufs = 4;            // LDS tile buffers: kBufs - 1 tiles in flight while one is consumed
+constexpr float kRescale = 8.f;     // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int window, int stride,
                                                 int n_valid, int cap) {
@@ -46,10 +50,23 @@ __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int wi
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// Hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which softmax weights tolerate.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory loads of this wave are outstanding (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima = no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool CSA, bool FP8>
 __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile * kPitch];
-  __shared__ int tvalid[kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kBufs][kTile * kPitch];
+  __shared__ int tvalid[kBufs][kTile];
+  __shared__ int srow[CSA ? kSlotChunk : 1];   // CSA: per slot of the current chunk: kv row, -2 - window row, or -1
+  __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
 
   const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const uint32_t total = gridDim.x;
@@ -60,7 +77,8 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   const int b = row / a.Tq;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int n = lane & 15, g = lane >> 4;
   const int head = hg * kHeadsPerBlock + wave * 16 + n;
   const bool head_ok = head < a.H;
@@ -82,11 +100,109 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   const int n_slots = n_ent + n_win;
   const int s0 = split * a.slots_per_split;
   const int s1 = min(n_slots, s0 + a.slots_per_split);
+  const int ntile = s1 > s0 ? (s1 - s0 + kTile - 1) / kTile : 0;
 
+  // ---- slot table and the first tiles go out before the query setup so their latency overlaps it
+  const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
+  auto stage_slots = [&](int c0) {
+    for (int i = tid; i < kSlotChunk; i += 256) {
+      const int slot = c0 + i;
+      int r = -1;
+      if (slot < s1) {
+        if (slot < n_ent) {
+          const int j = idxrow[slot];
+          r = (j >= 0 && j < kv_nv) ? j : -1;
+        } else {
+          r = -2 - (int)(r_lo + (slot - n_ent));
+        }
+      }
+      srow[i] = r;
+    }
+  };
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * (FP8 ? kD : 2 * kD);
+  const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
+  auto row_src = [&](int r) -> const uint8_t* {
+    if (r >= 0) return kvb + (int64_t)r * (FP8 ? kD : 2 * kD);
+    if (r <= -2) return winb + (int64_t)(-2 - r) * (2 * kD);
+    return kvb;   // unused slot: any valid row (masked by tvalid)
+  };
+  // row of a slot: CSA reads the staged table, HCA maps slots to rows directly
+  auto slot_row = [&](int slot, int cbase) -> int {
+    if (slot >= s1) return -1;
+    if (CSA) return srow[min(max(slot - cbase, 0), kSlotChunk - 1)];
+    return slot < n_ent ? slot : -2 - (int)(r_lo + (slot - n_ent));
+  };
+  // bf16 rows: wave w moves tile rows w, w+4, ..., w+28 straight into LDS (1 KB per
+  // instruction, 16 B per lane); always 8 loads per wave so vmcnt counts are uniform.
+  auto issue_tile = [&](int t, int buf, int cbase) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = wave + 4 * i;
+      const int r = slot_row(s0 + t * kTile + rr, cbase);
+      const uint8_t* src = row_src(r);
+      const bool fp8_row = FP8 && r >= 0;
+      if (!fp8_row) {
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + 16 * lane),
+                                         (lds_void*)&tile[buf][rr * kPitch], 16, 0, 0);
+      }
+      if (lane == 0) tvalid[buf][rr] = r != -1;
+    }
+  };
+  // fp8 entry rows: codes and the channel block's scale go through registers and are
+  // widened to bf16 (code * scale, rounded) on the way into LDS.
+  u32x2 pre8[8];
+  float pres[8];
+  auto fetch_fp8 = [&](int t, int cbase) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = wave + 4 * i;
+      const int r = slot_row(s0 + t * kTile + rr, cbase);
+      pre8[i] = u32x2{0u, 0u};
+      pres[i] = 0.f;
+      if (r >= 0) {
+        const int64_t rg = (int64_t)b * a.kv_cap + r;
+        pre8[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.kv) + rg * kD + 8 * lane);
+        pres[i] = a.kv_scales[rg * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
+      }
+    }
+  };
+  auto store_fp8 = [&](int t, int buf, int cbase) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = wave + 4 * i;
+      const int r = slot_row(s0 + t * kTile + rr, cbase);
+      if (r >= 0) {
+        const float sc = pres[i];
+        const f32x2 f0 = fp8x2_lo(pre8[i][0]), f1 = fp8x2_hi(pre8[i][0]);
+        const f32x2 f2 = fp8x2_lo(pre8[i][1]), f3 = fp8x2_hi(pre8[i][1]);
+        u32x4 v;
+        v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
+        v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
+        v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
+        v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
+        *reinterpret_cast<u32x4*>(&tile[buf][rr * kPitch + 8 * lane]) = v;
+      }
+    }
+  };
+
+  // a CSA split never spans more than kSlotChunk slots (the launcher splits further), so one
+  // staged table covers every tile of the split
+  const int cbase = s0;
+  if (ntile > 0) {
+    if (CSA) { stage_slots(cbase); __syncthreads(); }
+    for (int t = 0; t < min(kBufs - 1, ntile); ++t) issue_tile(t, t, cbase);
+    if (FP8) { fetch_fp8(0, cbase); store_fp8(0, 0, cbase); }
+  }
   // ---- query fragments (B operand of S^T = K Q^T): head = n, channels 32c + 8g + [0, 8).
   // The rotated query is not a bf16 value: its last two chunks (channels 448..511, which
   // hold the rotated pairs for rope_dim <= 64) are carried as bf16 hi + lo so the logits
   // keep fp32 accuracy; rotated channels below 448 (rope_dim > 64) are rounded to bf16.
+  for (int i = tid; i < a.rope_dim / 2; i += 256) {
+    float cs, sn;
+    rope_cs(p, a.inv_freq[i], cs, sn);
+    rtab[i] = f32x2{cs, sn};
+  }
+  __syncthreads();
   bf16x8 qf[16];
   bf16x8 qlo[2];
   {
@@ -102,8 +218,8 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
         for (int k2 = 0; k2 < 4; ++k2) {
           const int d = 32 * c + 8 * g + 2 * k2;
           if (d >= rot0) {
-            float cs, sn;
-            rope_cs(p, a.inv_freq[(d - rot0) >> 1], cs, sn);
+            const f32x2 t2 = rtab[(d - rot0) >> 1];
+            const float cs = t2[0], sn = t2[1];
             const float x0 = bf16lo_to_f32(v[k2]), x1 = bf16hi_to_f32(v[k2]);
             const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
             v[k2] = pack_bf16x2(y0, y1);
@@ -117,81 +233,36 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   }
   const bool q_split = a.rope_dim > 0;
 
-  // ---- online softmax state (per lane: head n; the 4 lanes of a head hold equal m)
-  float m_run, l_run;
-  if (split == 0 && head_ok) {
-    m_run = a.sink[head] * kLog2e;
-    l_run = (g == 0) ? 1.f : 0.f;
-  } else {
-    m_run = kNegBig;
-    l_run = 0.f;
-  }
+  // ---- online softmax state (per lane: head n; the 4 lanes of a head hold equal m).  The
+  // reference maximum starts at the first tile's maximum (so a dominant row there gets weight
+  // exactly 1); the sink joins once, in the epilogue or in the split merge.
+  float m_run = kNegBig, l_run = 0.f;
   f32x4 acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- row loader: wave w stages tile rows w, w+4, ..., w+28; lane = 8 channels
-  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv);
-  const uint16_t* winb = reinterpret_cast<const uint16_t*>(a.win);
-  const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
-  auto fetch = [&](int t0, u32x4 (&r)[8], int (&ok)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int slot = t0 + wave + 4 * i;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      int valid = 0;
-      if (slot < s1) {
-        if (slot < n_ent) {
-          int j = CSA ? idxrow[slot] : slot;
-          if (j >= 0 && j < kv_nv) {
-            valid = 1;
-            const int64_t rr = (int64_t)b * a.kv_cap + j;
-            if (FP8) {
-              const u32x2 c2 = *reinterpret_cast<const u32x2*>(kvb + rr * kD + 8 * lane);
-              const float sc = a.kv_scales[rr * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
-              const f32x2 f0 = fp8x2_lo(c2[0]), f1 = fp8x2_hi(c2[0]);
-              const f32x2 f2 = fp8x2_lo(c2[1]), f3 = fp8x2_hi(c2[1]);
-              v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
-              v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
-              v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
-              v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
-            } else {
-              v = *reinterpret_cast<const u32x4*>(kvb + rr * (2 * kD) + 16 * lane);
-            }
-          }
-        } else {
-          const int64_t rr = (int64_t)b * a.win_cap + r_lo + (slot - n_ent);
-          v = *reinterpret_cast<const u32x4*>(winb + rr * kD + 8 * lane);
-          valid = 1;
-        }
-      }
-      r[i] = v;
-      ok[i] = valid;
-    }
-  };
-
-  u32x4 pre[8];
-  int pok[8];
-  const int ntile = s1 > s0 ? (s1 - s0 + kTile - 1) / kTile : 0;
-  if (ntile > 0) fetch(s0, pre, pok);
-
   for (int t = 0; t < ntile; ++t) {
-    // stage the prefetched rows
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = wave + 4 * i;
-      *reinterpret_cast<u32x4*>(&tile[rr * kPitch + 8 * lane]) = pre[i];
-      if (lane == 0) tvalid[rr] = pok[i];
-    }
+    const int buf = t % kBufs;
+    // issue tile t + kBufs - 1 into the buffer tile t - 1 used (freed by the last barrier)
+    const int tn = t + kBufs - 1;
+    if (tn < ntile) issue_tile(tn, tn % kBufs, cbase);
+    if (FP8 && t + 1 < ntile) fetch_fp8(t + 1, cbase);
+    // tile t has landed once at most the loads of the later tiles are outstanding
+    const int later = min(kBufs - 1, ntile - 1 - t);
+    if (FP8) wait_vmcnt<0>();
+    else if (later >= 3) wait_vmcnt<24>();
+    else if (later == 2) wait_vmcnt<16>();
+    else if (later == 1) wait_vmcnt<8>();
+    else wait_vmcnt<0>();
     __syncthreads();
-    if (t + 1 < ntile) fetch(s0 + (t + 1) * kTile, pre, pok);
+    const uint16_t* tl = tile[buf];
 
     // S^T = K Q^T for rows 16kb + [0,16) of the tile
     f32x4 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* rp = &tile[(16 * kb + n) * kPitch + 8 * g];
+      const uint16_t* rp = &tl[(16 * kb + n) * kPitch + 8 * g];
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + 32 * c);
@@ -209,28 +280,34 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * kb + i;
-        const int ok = tvalid[16 * kb + 4 * g + i];
+        const int ok = tvalid[buf][16 * kb + 4 * g + i];
         sv[e] = sacc[kb][i] * a.scale_log2;
         if (ok) { vmask |= 1 << e; tmax = fmaxf(tmax, sv[e]); }
       }
     tmax = wave_max_xor(tmax, 16);
     tmax = wave_max_xor(tmax, 32);
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
+    // Lazy rescaling: the reference maximum m_run only moves when a tile's maximum exceeds it
+    // by more than kRescale (log2 units), so the 128 output accumulators are rescaled rarely;
+    // in between, weights exp2(s - m_run) stay below 2^kRescale, well inside bf16 and fp32.
+    const bool grow = tmax > m_run + kRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      // nothing accumulated yet (first tile with rows): the accumulators are zero already
+      if (__any(grow && m_run > kNegBig)) {
+#pragma unroll
+        for (int db = 0; db < 32; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+      }
+      m_run = m_new;
+    }
     float pv[8];
-    float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pv[e] = (vmask >> e & 1) ? exp2f(sv[e] - m_new) : 0.f;
-      psum += pv[e];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+      pv[e] = (vmask >> e & 1) ? fast_exp2(sv[e] - m_run) : 0.f;
+      l_run += pv[e];
     }
     u32x4 pw;
     pw[0] = pack_bf16x2(pv[0], pv[1]);
@@ -244,13 +321,14 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
       const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&tile[(4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+          (lds_i16x4*)&tl[(4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
       const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&tile[(16 + 4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+          (lds_i16x4*)&tl[(16 + 4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
       typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
       const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
     }
+    if (FP8 && t + 1 < ntile) store_fp8(t + 1, (t + 1) % kBufs, cbase);
     __syncthreads();
   }
 
@@ -260,7 +338,13 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   l_tot += __shfl_xor(l_tot, 32, kWave);
   if (!head_ok) return;
   if (a.nsplit == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // fold in the sink: Z = l 2^(m - M) + 2^(sink - M), M = max(m, sink)
+    const float sink2 = a.sink[head] * kLog2e;
+    const float M = fmaxf(m_run, sink2);
+    const float sc = exp2f(m_run - M);
+    l_tot = l_tot * sc + exp2f(sink2 - M);
+    m_run = M;
+    const float inv = sc / l_tot;
     const int rot0 = kD - a.rope_dim;
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
@@ -273,8 +357,9 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
         for (int k2 = 0; k2 < 2; ++k2) {
           const int d = d0 + 2 * k2;
           if (d >= rot0) {
-            float cs, sn;
-            rope_cs(-p, a.inv_freq[(d - rot0) >> 1], cs, sn);
+            // rotation by -q_pos: same cosine, negated sine
+            const f32x2 t2 = rtab[(d - rot0) >> 1];
+            const float cs = t2[0], sn = -t2[1];
             const float x0 = o[2 * k2], x1 = o[2 * k2 + 1];
             o[2 * k2] = x0 * cs - x1 * sn;
             o[2 * k2 + 1] = x0 * sn + x1 * cs;
@@ -311,10 +396,11 @@ __global__ void __launch_bounds__(128) k_attend_combine(AttendArgs a) {
   const int row = rh / a.H;
   const int d0 = threadIdx.x * 4;
   const int64_t p = a.q_pos[row];
-  float M = kNegBig;
+  const float sink2 = a.sink[rh % a.H] * kLog2e;
+  float M = sink2;
   for (int s = 0; s < a.nsplit; ++s)
     M = fmaxf(M, a.part_ml[2 * (((int64_t)row * a.nsplit + s) * a.H + rh % a.H)]);
-  float Z = 0.f;
+  float Z = exp2f(sink2 - M);
   float o[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.nsplit; ++s) {
     const int64_t pr = ((int64_t)row * a.nsplit + s) * a.H + rh % a.H;
@@ -354,13 +440,14 @@ __global__ void __launch_bounds__(128) k_attend_combine(AttendArgs a) {
   if (a.lse && threadIdx.x == 0) a.lse[rh] = (M + log2f(Z)) * kLn2;
 }
 
-int attend_nsplit(int rows, int H, int slot_cap) {
+int attend_nsplit(int rows, int H, int slot_cap, bool csa) {
   const int HG = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const long long base = (long long)rows * HG;
   int ns = (int)((kTargetBlocks + base - 1) / base);
   const int max_ns = (slot_cap + 2 * kTile - 1) / (2 * kTile);   // at least two tiles per split
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
+  if (csa && ns < (slot_cap + kSlotChunk - 1) / kSlotChunk) ns = (slot_cap + kSlotChunk - 1) / kSlotChunk;
   // round the per-split count up to whole tiles, then recount
   int sps = (slot_cap + ns - 1) / ns;
   sps = (sps + kTile - 1) / kTile * kTile;
@@ -374,8 +461,8 @@ static int attend_sps(int nsplit, int slot_cap) {
   return sps < kTile ? kTile : sps;
 }
 
-size_t attend_workspace(int rows, int H, int slot_cap) {
-  const int ns = attend_nsplit(rows, H, slot_cap);
+size_t attend_workspace(int rows, int H, int slot_cap, bool csa) {
+  const int ns = attend_nsplit(rows, H, slot_cap, csa);
   if (ns <= 1) return 0;
   return (size_t)rows * ns * H * (kD + 2) * sizeof(float) + 256;
 }
@@ -383,7 +470,7 @@ size_t attend_workspace(int rows, int H, int slot_cap) {
 hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   AttendArgs a = a0;
   const int rows = a.B * a.Tq;
-  a.nsplit = attend_nsplit(rows, a.H, a.slot_cap);
+  a.nsplit = attend_nsplit(rows, a.H, a.slot_cap, a.csa_mode != 0);
   a.slots_per_split = attend_sps(a.nsplit, a.slot_cap);
   const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const long long blocks = (long long)rows * HG * a.nsplit;

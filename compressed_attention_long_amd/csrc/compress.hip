@@ -52,27 +52,35 @@ __device__ __forceinline__ void pool_merge(PoolState& out, const PoolState& x, c
   }
 }
 
-__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
-  u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { f[2 * i] = bf16lo_to_f32(w[i]); f[2 * i + 1] = bf16hi_to_f32(w[i]); }
-}
-
-// Add one block of `n` raw tokens starting at token row `t0` into p.
+// Add one block of `n` raw tokens starting at token row `t0` into p.  Loads are issued
+// kU tokens at a time before the (serially dependent) softmax updates consume them.
+constexpr int kU = 8;
 __device__ __forceinline__ void pool_block(PoolState& p, const uint16_t* kv, const uint16_t* lg,
                                            int64_t ld_tok, int t0, int n, int c0) {
-  for (int t = 0; t < n; ++t) {
-    float v[8], z[8];
-    load8(kv + (int64_t)(t0 + t) * ld_tok + c0, v);
-    if (lg) {
-      load8(lg + (int64_t)(t0 + t) * ld_tok + c0, z);
+  for (int t = 0; t < n; t += kU) {
+    u32x4 wv[kU], wz[kU];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] *= kLog2e;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) z[i] = 0.f;
+    for (int u = 0; u < kU; ++u) {
+      if (t + u < n) {
+        wv[u] = *reinterpret_cast<const u32x4*>(kv + (int64_t)(t0 + t + u) * ld_tok + c0);
+        wz[u] = lg ? *reinterpret_cast<const u32x4*>(lg + (int64_t)(t0 + t + u) * ld_tok + c0)
+                   : u32x4{0u, 0u, 0u, 0u};
+      }
     }
-    pool_add(p, v, z);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (t + u < n) {
+        float v[8], z[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16lo_to_f32(wv[u][i]);
+          v[2 * i + 1] = bf16hi_to_f32(wv[u][i]);
+          z[2 * i] = bf16lo_to_f32(wz[u][i]) * kLog2e;
+          z[2 * i + 1] = bf16hi_to_f32(wz[u][i]) * kLog2e;
+        }
+        pool_add(p, v, z);
+      }
+    }
   }
 }
 
@@ -144,7 +152,7 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
   const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
                                 : nullptr;
-  if (a.window == 2 * a.stride) {
+  if (a.window == 2 * a.stride && a.run > 1) {
     // Overlapping rows: entry i = block i + block i+1 (blocks of `stride` tokens).
     PoolState prev, cur, both;
     pool_reset(prev);

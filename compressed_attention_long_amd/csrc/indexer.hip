@@ -44,14 +44,16 @@ __device__ __forceinline__ int visible_rows(int64_t qp, int64_t pos0, int window
 
 constexpr int kIdxTilesPerWave = 16;     // 16 entries per tile
 constexpr int kIdxWaves = 4;
+constexpr int kDepth = 4;                // score-tile loads in flight per wave
 constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
 
 template <int HB, bool FP8>
 __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
+  __shared__ float sbuf[kIdxWaves][kIdxTilesPerWave * 16];
   const int row = blockIdx.x;                 // query row (b * Tq + t)
   const int b = row / a.Tq;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
   const int n = lane & 15, g = lane >> 4;
   const int64_t qp = a.q_pos[row];
   const int nvis = visible_rows(qp, a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
@@ -67,83 +69,96 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
     const int h = hb * 16 + n;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < a.Hi) v = *reinterpret_cast<const u32x4*>(q + (int64_t)h * a.Di + 32 * g + 8 * s);
+      u32x4 v = *reinterpret_cast<const u32x4*>(q + (int64_t)min(h, a.Hi - 1) * a.Di + 32 * g + 8 * s);
+      if (h >= a.Hi) v = u32x4{0u, 0u, 0u, 0u};
       qf[hb][s] = __builtin_bit_cast(bf16x8, v);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = hb * 16 + 4 * g + i;
-      wv[hb][i] = hh < a.Hi ? a.w[(int64_t)row * a.Hi + hh] : 0.f;
+      const float wl = a.w[(int64_t)row * a.Hi + min(hh, a.Hi - 1)];
+      wv[hb][i] = hh < a.Hi ? wl : 0.f;
     }
   }
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys) +
                          (int64_t)b * a.cap * (FP8 ? a.Di : 2 * a.Di);
-  constexpr int KW = FP8 ? 8 : 16;            // dwords of key data per lane per tile
-  auto load_tile = [&](int t0, uint32_t (&r)[KW]) {
-    const int j = t0 + n;
-    if (j < nvis) {
-      const uint8_t* p = kbase + (int64_t)j * (FP8 ? 128 : 256) + (FP8 ? 32 : 64) * g;
+  // per tile and lane: KW dwords of key channels, plus (fp8) one dword holding the key's scale
+  constexpr int KW = FP8 ? 8 : 16;
+  constexpr int KR = FP8 ? KW + 1 : KW;
+  const float* sbase = FP8 ? a.key_scales + (int64_t)b * a.cap : nullptr;
+  // Branch-free loads (row index clamped into the visible range; results past nvis are
+  // masked when the score is written) so the compiler can keep kDepth tiles in flight.
+  const int jlast = max(nvis - 1, 0);
+  auto load_tile = [&](int t0, uint32_t (&r)[KR]) {
+    const int j = min(t0 + n, jlast);
+    const uint8_t* p = kbase + (int64_t)j * (FP8 ? 128 : 256) + (FP8 ? 32 : 64) * g;
 #pragma unroll
-      for (int c = 0; c < KW / 4; ++c) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * c);
-        r[4 * c] = v[0]; r[4 * c + 1] = v[1]; r[4 * c + 2] = v[2]; r[4 * c + 3] = v[3];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < KW; ++c) r[c] = 0u;
+    for (int c = 0; c < KW / 4; ++c) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * c);
+      r[4 * c] = v[0]; r[4 * c + 1] = v[1]; r[4 * c + 2] = v[2]; r[4 * c + 3] = v[3];
     }
+    if (FP8) r[KW] = __float_as_uint(sbase[j]);
   };
 
-  uint32_t cur[KW], nxt[KW];
+  // kDepth tiles in flight per wave: the loads of tile t + kDepth are issued as tile t is
+  // consumed, from a ring of register buffers indexed at compile time.
+  uint32_t ring[kDepth][KR];
   int ntile = 0;
   if (base < nvis) ntile = min(kIdxTilesPerWave, (nvis - base + 15) / 16);
-  if (ntile > 0) load_tile(base, cur);
-  for (int t = 0; t < ntile; ++t) {
-    const int t0 = base + 16 * t;
-    if (t + 1 < ntile) load_tile(t0 + 16, nxt);
-    f32x4 acc[HB];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < kDepth; ++d)
+    load_tile(base + 16 * min(d, max(ntile - 1, 0)), ring[d]);
+  for (int t0 = 0; t0 < ntile; t0 += kDepth) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 kb;
-      if (FP8) {
-        // 8 codes (channels 32g + 8s .. +8) -> 8 bf16, exactly
+    for (int d = 0; d < kDepth; ++d) {
+      const int t = t0 + d;
+      if (t >= ntile) break;
+      uint32_t (&cur)[KR] = ring[d];
+      f32x4 acc[HB];
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint32_t w = cur[2 * s + h2];
-          f32x2 lo = fp8x2_lo(w), hi = fp8x2_hi(w);
-          kb[2 * h2] = (__float_as_uint(lo[1]) & 0xffff0000u) | (__float_as_uint(lo[0]) >> 16);
-          kb[2 * h2 + 1] = (__float_as_uint(hi[1]) & 0xffff0000u) | (__float_as_uint(hi[0]) >> 16);
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 kb;
+        if (FP8) {
+          // 8 codes (channels 32g + 8s .. +8) -> 8 bf16, exactly
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            uint32_t w = cur[2 * s + h2];
+            f32x2 lo = fp8x2_lo(w), hi = fp8x2_hi(w);
+            kb[2 * h2] = (__float_as_uint(lo[1]) & 0xffff0000u) | (__float_as_uint(lo[0]) >> 16);
+            kb[2 * h2 + 1] = (__float_as_uint(hi[1]) & 0xffff0000u) | (__float_as_uint(hi[0]) >> 16);
+          }
+        } else {
+          kb[0] = cur[4 * s]; kb[1] = cur[4 * s + 1]; kb[2] = cur[4 * s + 2]; kb[3] = cur[4 * s + 3];
         }
-      } else {
-        kb[0] = cur[4 * s]; kb[1] = cur[4 * s + 1]; kb[2] = cur[4 * s + 2]; kb[3] = cur[4 * s + 3];
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, kb);
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[hb][s], kf, acc[hb], 0, 0, 0);
       }
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, kb);
+      const float kscale = FP8 ? __uint_as_float(cur[KW]) : 1.f;
+      // next load for this ring slot (past the last tile it re-reads that tile: an L2 hit)
+      load_tile(base + 16 * min(t + kDepth, ntile - 1), ring[d]);
+      float sc = 0.f;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
-        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[hb][s], kf, acc[hb], 0, 0, 0);
-    }
-    float sc = 0.f;
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc += wv[hb][i] * fmaxf(acc[hb][i], 0.f);
-    sc += __shfl_xor(sc, 16, kWave);
-    sc += __shfl_xor(sc, 32, kWave);
-    const int j = t0 + n;
-    if (FP8 && j < nvis) sc *= a.key_scales[(int64_t)b * a.cap + j];
-    if (g == 0 && j < a.cap) srow[j] = j < nvis ? sc : -INFINITY;
-    if (t + 1 < ntile) {
-#pragma unroll
-      for (int c = 0; c < KW; ++c) cur[c] = nxt[c];
+        for (int i = 0; i < 4; ++i) sc += wv[hb][i] * fmaxf(acc[hb][i], 0.f);
+      sc += __shfl_xor(sc, 16, kWave);
+      sc += __shfl_xor(sc, 32, kWave);
+      if (FP8) sc *= kscale;
+      // staged in LDS: global stores inside the loop would count against vmcnt and stall the ring
+      if (g == 0) sbuf[wave][16 * t + n] = sc;
     }
   }
-  // rows of this wave's range beyond the visible count
-  for (int j = max(base + 16 * ntile, base) + lane; j < min(base + kIdxTilesPerWave * 16, a.cap); j += 64)
-    srow[j] = -INFINITY;
+  // write this wave's scores, coalesced; entries past the visible count score -inf
+#pragma unroll
+  for (int i = lane; i < kIdxTilesPerWave * 16; i += 64) {
+    const int j = base + i;
+    if (j < a.cap) srow[j] = j < nvis ? sbuf[wave][i] : -INFINITY;
+  }
 }
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
@@ -229,6 +244,24 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TopkSha
 // refinement keeps only the bin holding the k-th largest key, whose key range is
 // at most 2^shift - 1 wide, so after at most three passes the candidates are one
 // key value (the range shrinks from < 2^32 to < 2^21, < 2^10, then 0).
+// Visit every visible entry j < nvis of a row in global memory, 8 loads per lane in
+// flight (indices clamped into the row; out-of-range lanes are masked).
+template <typename F>
+__device__ __forceinline__ void for_each_key(const float* s, int nvis, F&& fn) {
+  constexpr int U = 8;
+  const int last = max(nvis - 1, 0);
+  for (int j0 = threadIdx.x; j0 < nvis; j0 += U * kTopkThreads) {
+    uint32_t kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kk[u] = okey(s[min(j0 + u * kTopkThreads, last)]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kTopkThreads;
+      if (j < nvis) fn(kk[u], j);
+    }
+  }
+}
+
 __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
   __shared__ TopkShared sh;
   const int row = blockIdx.x;
@@ -245,7 +278,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
   if (!take_all) {
     if (tid == 0) { sh.bstar = 0; sh.above = 0; sh.TK = 0xffffffffu; sh.I = -1; }
     uint32_t klo = 0xffffffffu, khi = 0u;
-    for (int j = tid; j < nvis; j += kTopkThreads) { uint32_t v = okey(s[j]); klo = min(klo, v); khi = max(khi, v); }
+    for_each_key(s, nvis, [&](uint32_t v, int) { klo = min(klo, v); khi = max(khi, v); });
     block_minmax(klo, khi, sh);
     int above = 0;                          // entries known to rank above the current range
     for (int iter = 0; iter < 4 && klo < khi; ++iter) {
@@ -253,10 +286,9 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
       __syncthreads();
       const uint32_t range = khi - klo;
       const int shift = max(0, 32 - __clz((int)range) - 11);
-      for (int j = tid; j < nvis; j += kTopkThreads) {
-        uint32_t v = okey(s[j]);
+      for_each_key(s, nvis, [&](uint32_t v, int) {
         if (v >= klo && v <= khi) atomicAdd(&sh.hist[(v - klo) >> shift], 1);
-      }
+      });
       __syncthreads();
       // thread t owns bins 2u+1 and 2u with u = 1023 - t, so the scan runs from the top bin down
       const int u = kTopkThreads - 1 - tid;
@@ -271,10 +303,9 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
       const int cnt = sh.hist[bstar];
       above += sh.above;
       uint32_t nlo = 0xffffffffu, nhi = 0u;
-      for (int j = tid; j < nvis; j += kTopkThreads) {
-        uint32_t v = okey(s[j]);
+      for_each_key(s, nvis, [&](uint32_t v, int) {
         if (v >= klo && v <= khi && (int)((v - klo) >> shift) == bstar) { nlo = min(nlo, v); nhi = max(nhi, v); }
-      }
+      });
       block_minmax(nlo, nhi, sh);
       klo = nlo;
       khi = nhi;
@@ -300,13 +331,12 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
     } else {
       if (tid == 0) sh.ccount = 0;
       __syncthreads();
-      for (int j = tid; j < nvis; j += kTopkThreads) {
-        uint32_t v = okey(s[j]);
+      for_each_key(s, nvis, [&](uint32_t v, int j) {
         if (v >= klo && v <= khi) {
           int slot = atomicAdd(&sh.ccount, 1);
           if (slot < kCandMax) { sh.ckey[slot] = v; sh.cidx[slot] = j; }
         }
-      }
+      });
       __syncthreads();
       const int c = min(sh.ccount, kCandMax);
       for (int ci = tid; ci < c; ci += kTopkThreads) {
@@ -341,8 +371,150 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
   for (int p = base + tid; p < k; p += kTopkThreads) out[p] = -1;
 }
 
+// Same selection with the row held in registers: thread t owns the NPT consecutive
+// entries [t*NPT, t*NPT + NPT), so the row is read from memory once and the compaction
+// needs a single block-wide scan.  Used when the row has at most NPT * 1024 entries.
+template <int NPT>
+__global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
+  __shared__ TopkShared sh;
+  const int row = blockIdx.x;
+  const int b = row / a.Tq;
+  const int tid = threadIdx.x;
+  const int k = a.topk;
+  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
+  const float* s = a.scores + (int64_t)row * a.cap;
+  int32_t* out = a.idx_out + (int64_t)row * k;
+  const int j0 = tid * NPT;
+
+  // Every lane issues all NPT loads unconditionally (index clamped into the row) so they
+  // are in flight together; entries at or past nvis are masked by `j0 + i < nvis` below.
+  uint32_t key[NPT];
+  {
+    const int last = max(nvis - 1, 0);
+    float v[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) v[i] = s[min(j0 + i, last)];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) key[i] = okey(v[i]);
+  }
+  // entries past nvis are never selected: they fail every `j0 + i < nvis` test below
+
+  uint32_t TK = 0xffffffffu;
+  int I = -1;
+  const bool take_all = nvis <= k;
+  if (!take_all) {
+    if (tid == 0) { sh.bstar = 0; sh.above = 0; sh.TK = 0xffffffffu; sh.I = -1; }
+    uint32_t klo = 0xffffffffu, khi = 0u;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (j0 + i < nvis) { klo = min(klo, key[i]); khi = max(khi, key[i]); }
+    block_minmax(klo, khi, sh);
+    int above = 0;
+    for (int iter = 0; iter < 4 && klo < khi; ++iter) {
+      for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0;
+      __syncthreads();
+      const uint32_t range = khi - klo;
+      const int shift = max(0, 32 - __clz((int)range) - 11);
+#pragma unroll
+      for (int i = 0; i < NPT; ++i)
+        if (j0 + i < nvis && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[(key[i] - klo) >> shift], 1);
+      __syncthreads();
+      const int u = kTopkThreads - 1 - tid;
+      const int hA = sh.hist[2 * u + 1], hB = sh.hist[2 * u];
+      int tot;
+      const int pre = block_excl_scan(hA + hB, sh.wsum, tot);
+      const int need = k - above;
+      if (pre < need && pre + hA >= need) { sh.bstar = 2 * u + 1; sh.above = pre; }
+      else if (pre + hA < need && pre + hA + hB >= need) { sh.bstar = 2 * u; sh.above = pre + hA; }
+      __syncthreads();
+      const int bstar = min(max(sh.bstar, 0), kTopkBins - 1);
+      const int cnt = sh.hist[bstar];
+      above += sh.above;
+      uint32_t nlo = 0xffffffffu, nhi = 0u;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i)
+        if (j0 + i < nvis && key[i] >= klo && key[i] <= khi && (int)((key[i] - klo) >> shift) == bstar) {
+          nlo = min(nlo, key[i]);
+          nhi = max(nhi, key[i]);
+        }
+      block_minmax(nlo, nhi, sh);
+      klo = nlo;
+      khi = nhi;
+      if (cnt <= kCandMax) break;
+    }
+    const int need = k - above;
+    if (klo == khi) {
+      TK = klo;
+      int f = 0;
+#pragma unroll
+      for (int i = 0; i < NPT; ++i) f += (j0 + i < nvis && key[i] == klo) ? 1 : 0;
+      int tot;
+      const int pre = block_excl_scan(f, sh.wsum, tot);
+      if (pre < need && pre + f >= need) {
+        int c = pre;
+#pragma unroll
+        for (int i = 0; i < NPT; ++i)
+          if (j0 + i < nvis && key[i] == klo) {
+            if (c == need - 1) sh.I = j0 + i;
+            ++c;
+          }
+      }
+      __syncthreads();
+      I = sh.I;
+    } else {
+      if (tid == 0) sh.ccount = 0;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < NPT; ++i)
+        if (j0 + i < nvis && key[i] >= klo && key[i] <= khi) {
+          const int slot = atomicAdd(&sh.ccount, 1);
+          if (slot < kCandMax) { sh.ckey[slot] = key[i]; sh.cidx[slot] = j0 + i; }
+        }
+      __syncthreads();
+      const int c = min(sh.ccount, kCandMax);
+      for (int ci = tid; ci < c; ci += kTopkThreads) {
+        const uint32_t v = sh.ckey[ci];
+        const int ji = sh.cidx[ci];
+        int rank = 0;
+        for (int o = 0; o < c; ++o) {
+          const uint32_t vo = sh.ckey[o];
+          rank += (vo > v || (vo == v && sh.cidx[o] < ji)) ? 1 : 0;
+        }
+        if (rank == need - 1) { sh.TK = v; sh.I = ji; }
+      }
+      __syncthreads();
+      TK = sh.TK;
+      I = sh.I;
+    }
+  }
+  // ascending compaction: one scan over the per-thread counts
+  int f = 0;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = j0 + i;
+    const bool sel = j < nvis && (take_all || key[i] > TK || (key[i] == TK && j <= I));
+    f += sel ? 1 : 0;
+  }
+  int tot;
+  int pos = block_excl_scan(f, sh.wsum, tot);
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const int j = j0 + i;
+    const bool sel = j < nvis && (take_all || key[i] > TK || (key[i] == TK && j <= I));
+    if (sel) {
+      if (pos < k) out[pos] = j;
+      ++pos;
+    }
+  }
+  for (int p2 = min(tot, k) + tid; p2 < k; p2 += kTopkThreads) out[p2] = -1;
+}
+
 hipError_t launch_topk(const IndexArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_topk, dim3(a.B * a.Tq), dim3(kTopkThreads), 0, s, a);
+  const dim3 grid(a.B * a.Tq), block(kTopkThreads);
+  if (a.cap <= 16 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<16>, grid, block, 0, s, a);
+  else if (a.cap <= 32 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<32>, grid, block, 0, s, a);
+  else if (a.cap <= 48 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<48>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(k_topk, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

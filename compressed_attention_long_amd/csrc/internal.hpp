@@ -2,7 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include "../../include/csa.h"
+#include "csa.h"
 
 namespace csa {
 
@@ -69,8 +69,8 @@ struct AttendArgs {
   float* part_o;          // [rows, nsplit, H, 512]
   float* part_ml;         // [rows, nsplit, H, 2]
 };
-int attend_nsplit(int rows, int H, int slot_cap);
-size_t attend_workspace(int rows, int H, int slot_cap);
+int attend_nsplit(int rows, int H, int slot_cap, bool csa);
+size_t attend_workspace(int rows, int H, int slot_cap, bool csa);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 }  // namespace csa
