@@ -104,21 +104,6 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
 
   // ---- slot table and the first tiles go out before the query setup so their latency overlaps it
   const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
-  auto stage_slots = [&](int c0) {
-    for (int i = tid; i < kSlotChunk; i += 256) {
-      const int slot = c0 + i;
-      int r = -1;
-      if (slot < s1) {
-        if (slot < n_ent) {
-          const int j = idxrow[slot];
-          r = (j >= 0 && j < kv_nv) ? j : -1;
-        } else {
-          r = -2 - (int)(r_lo + (slot - n_ent));
-        }
-      }
-      srow[i] = r;
-    }
-  };
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * (FP8 ? kD : 2 * kD);
   const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
   auto row_src = [&](int r) -> const uint8_t* {
@@ -185,11 +170,44 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
     }
   };
 
+  // ---- prologue: every independent global load (query fragments, rotary frequencies, the
+  // split's row indices) is issued first so that their latencies overlap; then one barrier
+  // publishes the slot table and the rotation table, and the first tiles go out.
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + min(head, a.H - 1)) * kD;
+  u32x4 qraw[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+  const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
+  constexpr int kSlotsPerThread = kSlotChunk / 256;
+  int jraw[CSA ? kSlotsPerThread : 1];
+  if (CSA) {
+    const int last = max(n_ent - 1, 0);
+#pragma unroll
+    for (int k = 0; k < kSlotsPerThread; ++k)
+      jraw[k] = n_ent > 0 ? idxrow[min(s0 + tid + 256 * k, last)] : -1;
+  }
   // a CSA split never spans more than kSlotChunk slots (the launcher splits further), so one
   // staged table covers every tile of the split
   const int cbase = s0;
+  if (CSA) {
+#pragma unroll
+    for (int k = 0; k < kSlotsPerThread; ++k) {
+      const int slot = cbase + tid + 256 * k;
+      int r = -1;
+      if (slot < s1) {
+        if (slot < n_ent) r = (jraw[k] >= 0 && jraw[k] < kv_nv) ? jraw[k] : -1;
+        else r = -2 - (int)(r_lo + (slot - n_ent));
+      }
+      srow[tid + 256 * k] = r;
+    }
+  }
+  if (tid < a.rope_dim / 2) {
+    float cs, sn;
+    rope_cs(p, fr, cs, sn);
+    rtab[tid] = f32x2{cs, sn};
+  }
+  __syncthreads();
   if (ntile > 0) {
-    if (CSA) { stage_slots(cbase); __syncthreads(); }
     for (int t = 0; t < min(kBufs - 1, ntile); ++t) issue_tile(t, t, cbase);
     if (FP8) { fetch_fp8(0, cbase); store_fp8(0, 0, cbase); }
   }
@@ -197,22 +215,14 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   // The rotated query is not a bf16 value: its last two chunks (channels 448..511, which
   // hold the rotated pairs for rope_dim <= 64) are carried as bf16 hi + lo so the logits
   // keep fp32 accuracy; rotated channels below 448 (rope_dim > 64) are rounded to bf16.
-  for (int i = tid; i < a.rope_dim / 2; i += 256) {
-    float cs, sn;
-    rope_cs(p, a.inv_freq[i], cs, sn);
-    rtab[i] = f32x2{cs, sn};
-  }
-  __syncthreads();
   bf16x8 qf[16];
   bf16x8 qlo[2];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + head) * kD;
     const int rot0 = kD - a.rope_dim;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      u32x4 v = {0u, 0u, 0u, 0u};
+      u32x4 v = head_ok ? qraw[c] : u32x4{0u, 0u, 0u, 0u};
       u32x4 lo = {0u, 0u, 0u, 0u};
-      if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
       if (32 * c + 32 > rot0 && a.rope_dim > 0) {
 #pragma unroll
         for (int k2 = 0; k2 < 4; ++k2) {

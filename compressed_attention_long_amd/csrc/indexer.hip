@@ -40,6 +40,20 @@ __device__ __forceinline__ int visible_rows(int64_t qp, int64_t pos0, int window
   return (int)min((int64_t)nv, jmax + 1);
 }
 
+// ReLU as an integer max on the bit pattern: negative floats are negative integers.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] for every lane, with the gfx950 lane-swap
+// permutes (row pairs, then wave halves) instead of LDS-routed shuffles.
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------- scores
 
 constexpr int kIdxTilesPerWave = 16;     // 16 entries per tile
@@ -127,8 +141,9 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
           for (int h2 = 0; h2 < 2; ++h2) {
             uint32_t w = cur[2 * s + h2];
             f32x2 lo = fp8x2_lo(w), hi = fp8x2_hi(w);
-            kb[2 * h2] = (__float_as_uint(lo[1]) & 0xffff0000u) | (__float_as_uint(lo[0]) >> 16);
-            kb[2 * h2 + 1] = (__float_as_uint(hi[1]) & 0xffff0000u) | (__float_as_uint(hi[0]) >> 16);
+            // upper halves of two fp32 values (exact bf16 images of E4M3 values) in one v_perm
+            kb[2 * h2] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
+            kb[2 * h2 + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
           }
         } else {
           kb[0] = cur[4 * s]; kb[1] = cur[4 * s + 1]; kb[2] = cur[4 * s + 2]; kb[3] = cur[4 * s + 3];
@@ -145,9 +160,8 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc += wv[hb][i] * fmaxf(acc[hb][i], 0.f);
-      sc += __shfl_xor(sc, 16, kWave);
-      sc += __shfl_xor(sc, 32, kWave);
+        for (int i = 0; i < 4; ++i) sc += wv[hb][i] * relu(acc[hb][i]);
+      sc = sum_lane_groups(sc);
       if (FP8) sc *= kscale;
       // staged in LDS: global stores inside the loop would count against vmcnt and stall the ring
       if (g == 0) sbuf[wave][16 * t + n] = sc;
@@ -371,12 +385,48 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
   for (int p = base + tid; p < k; p += kTopkThreads) out[p] = -1;
 }
 
-// Same selection with the row held in registers: thread t owns the NPT consecutive
-// entries [t*NPT, t*NPT + NPT), so the row is read from memory once and the compaction
-// needs a single block-wide scan.  Used when the row has at most NPT * 1024 entries.
+// Same selection with the row held in registers, read once with coalesced loads: thread t
+// owns entries j = i * 1024 + t (i < NPT).  Order-dependent steps (ascending output, the
+// smallest index among tied keys) number the selected entries in index order with wave
+// ballots plus one scan over the per-(i, wave) counts.  Used when the row has at most
+// NPT * 1024 entries.
+template <int NPT>
+struct OrderShared {
+  int cnt[NPT * (kTopkThreads / 64)];
+};
+
+// For per-thread flags f[i] (entry j = i * 1024 + tid), the rank of each flagged entry among
+// all flagged entries in index order; returns the total.  Two barriers.
+template <int NPT>
+__device__ __forceinline__ int ordered_ranks(const bool (&f)[NPT], int (&rank)[NPT], int* cnt, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = kTopkThreads / 64;
+  uint64_t m[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    m[i] = __ballot(f[i]);
+    if (lane == 0) cnt[i * NW + wave] = __popcll(m[i]);
+  }
+  __syncthreads();
+  // exclusive scan of cnt[] (index order = (i, wave) lexicographic) by the first NPT*NW threads
+  const int t = threadIdx.x;
+  const int v = t < NPT * NW ? cnt[t] : 0;
+  int tot;
+  const int pre = block_excl_scan(v, wsum, tot);
+  if (t < NPT * NW) cnt[t] = pre;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const uint32_t lo = (uint32_t)m[i], hi = (uint32_t)(m[i] >> 32);
+    rank[i] = cnt[i * NW + wave] + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+  }
+  return tot;
+}
+
 template <int NPT>
 __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
   __shared__ TopkShared sh;
+  __shared__ OrderShared<NPT> osh;
   const int row = blockIdx.x;
   const int b = row / a.Tq;
   const int tid = threadIdx.x;
@@ -384,20 +434,20 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
   const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   const float* s = a.scores + (int64_t)row * a.cap;
   int32_t* out = a.idx_out + (int64_t)row * k;
-  const int j0 = tid * NPT;
 
-  // Every lane issues all NPT loads unconditionally (index clamped into the row) so they
-  // are in flight together; entries at or past nvis are masked by `j0 + i < nvis` below.
+  // Coalesced, unconditional loads (index clamped into the row; entries at or past nvis
+  // are masked by `ok(i)` below).
   uint32_t key[NPT];
   {
     const int last = max(nvis - 1, 0);
     float v[NPT];
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) v[i] = s[min(j0 + i, last)];
+    for (int i = 0; i < NPT; ++i) v[i] = s[min(i * kTopkThreads + tid, last)];
 #pragma unroll
     for (int i = 0; i < NPT; ++i) key[i] = okey(v[i]);
   }
-  // entries past nvis are never selected: they fail every `j0 + i < nvis` test below
+  auto jof = [&](int i) { return i * kTopkThreads + tid; };
+  auto ok = [&](int i) { return jof(i) < nvis; };
 
   uint32_t TK = 0xffffffffu;
   int I = -1;
@@ -407,7 +457,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
     uint32_t klo = 0xffffffffu, khi = 0u;
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
-      if (j0 + i < nvis) { klo = min(klo, key[i]); khi = max(khi, key[i]); }
+      if (ok(i)) { klo = min(klo, key[i]); khi = max(khi, key[i]); }
     block_minmax(klo, khi, sh);
     int above = 0;
     for (int iter = 0; iter < 4 && klo < khi; ++iter) {
@@ -417,7 +467,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
       const int shift = max(0, 32 - __clz((int)range) - 11);
 #pragma unroll
       for (int i = 0; i < NPT; ++i)
-        if (j0 + i < nvis && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[(key[i] - klo) >> shift], 1);
+        if (ok(i) && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[(key[i] - klo) >> shift], 1);
       __syncthreads();
       const int u = kTopkThreads - 1 - tid;
       const int hA = sh.hist[2 * u + 1], hB = sh.hist[2 * u];
@@ -433,7 +483,7 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
       uint32_t nlo = 0xffffffffu, nhi = 0u;
 #pragma unroll
       for (int i = 0; i < NPT; ++i)
-        if (j0 + i < nvis && key[i] >= klo && key[i] <= khi && (int)((key[i] - klo) >> shift) == bstar) {
+        if (ok(i) && key[i] >= klo && key[i] <= khi && (int)((key[i] - klo) >> shift) == bstar) {
           nlo = min(nlo, key[i]);
           nhi = max(nhi, key[i]);
         }
@@ -444,21 +494,16 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
     }
     const int need = k - above;
     if (klo == khi) {
+      // all candidates share one key: the need-th smallest index among them
       TK = klo;
-      int f = 0;
+      bool f[NPT];
+      int rk[NPT];
 #pragma unroll
-      for (int i = 0; i < NPT; ++i) f += (j0 + i < nvis && key[i] == klo) ? 1 : 0;
-      int tot;
-      const int pre = block_excl_scan(f, sh.wsum, tot);
-      if (pre < need && pre + f >= need) {
-        int c = pre;
+      for (int i = 0; i < NPT; ++i) f[i] = ok(i) && key[i] == klo;
+      ordered_ranks<NPT>(f, rk, osh.cnt, sh.wsum);
 #pragma unroll
-        for (int i = 0; i < NPT; ++i)
-          if (j0 + i < nvis && key[i] == klo) {
-            if (c == need - 1) sh.I = j0 + i;
-            ++c;
-          }
-      }
+      for (int i = 0; i < NPT; ++i)
+        if (f[i] && rk[i] == need - 1) sh.I = jof(i);
       __syncthreads();
       I = sh.I;
     } else {
@@ -466,9 +511,9 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < NPT; ++i)
-        if (j0 + i < nvis && key[i] >= klo && key[i] <= khi) {
+        if (ok(i) && key[i] >= klo && key[i] <= khi) {
           const int slot = atomicAdd(&sh.ccount, 1);
-          if (slot < kCandMax) { sh.ckey[slot] = key[i]; sh.cidx[slot] = j0 + i; }
+          if (slot < kCandMax) { sh.ckey[slot] = key[i]; sh.cidx[slot] = jof(i); }
         }
       __syncthreads();
       const int c = min(sh.ccount, kCandMax);
@@ -487,25 +532,16 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
       I = sh.I;
     }
   }
-  // ascending compaction: one scan over the per-thread counts
-  int f = 0;
+  // ascending compaction: selected entries numbered in index order
+  bool f[NPT];
+  int pos[NPT];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    const int j = j0 + i;
-    const bool sel = j < nvis && (take_all || key[i] > TK || (key[i] == TK && j <= I));
-    f += sel ? 1 : 0;
-  }
-  int tot;
-  int pos = block_excl_scan(f, sh.wsum, tot);
+  for (int i = 0; i < NPT; ++i)
+    f[i] = ok(i) && (take_all || key[i] > TK || (key[i] == TK && jof(i) <= I));
+  const int tot = ordered_ranks<NPT>(f, pos, osh.cnt, sh.wsum);
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    const int j = j0 + i;
-    const bool sel = j < nvis && (take_all || key[i] > TK || (key[i] == TK && j <= I));
-    if (sel) {
-      if (pos < k) out[pos] = j;
-      ++pos;
-    }
-  }
+  for (int i = 0; i < NPT; ++i)
+    if (f[i] && pos[i] < k) out[pos[i]] = jof(i);
   for (int p2 = min(tot, k) + tid; p2 < k; p2 += kTopkThreads) out[p2] = -1;
 }
 
