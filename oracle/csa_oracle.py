@@ -33,7 +33,11 @@ the definition states.  Sources (page title, then section):
 
 Readings where the pages are silent are listed beside the function that takes
 them (pairing of rotated dims, position of an entry, window edge, tie order,
-fp8 format).  All floating point is fp64 except where a reading says that a
+fp8 format).  Parity unpinned against the pages: the entry position (last raw
+token), the adjacent pairing of rotated dims, the default softmax scale
+1/sqrt(512), one indexer key per entry shared by all indexer heads, and the
+window edge (p - 128, p].  The tests pin each of these conventions as written,
+but no value on the pages fixes them.  All floating point is fp64 except where a reading says that a
 quantisation decision is taken in fp32 (the kernel's precision).
 """
 from __future__ import annotations
