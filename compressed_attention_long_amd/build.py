@@ -2,7 +2,8 @@
 
     python -m compressed_attention_long_amd.build
 
-compiles every csrc/*.hip into compressed_attention_long_amd/libcsa.so with hipcc.
+compiles every csrc/*.hip (objects under _build/) and links
+compressed_attention_long_amd/libcsa.so with hipcc.
 """
 from __future__ import annotations
 
@@ -23,13 +24,17 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the softmax / ReLU epilogues
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
+# MFMA accumulators in VGPRs: avoids AGPR<->VGPR copies around the softmax / ReLU epilogues.
+PER_FILE_FLAGS = {
+    "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "compress.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+BUILD_DIR = os.path.join(ROOT, "_build")
 
 
 def hipcc() -> str:
@@ -39,20 +44,36 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the CSA library needs ROCm's hipcc to build")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile csrc/*.hip into libcsa.so (always recompiles).  Returns the path."""
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                     if "packed-fp32-ops" not in l and l.strip())
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def _check(proc, what, verbose):
+    out, _ = proc.communicate()
+    msgs = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {what} ({proc.returncode}):\n{msgs}")
     if verbose and msgs:
         print(msgs, flush=True)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile csrc/*.hip (in parallel, one object each) and link libcsa.so (always recompiles)."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    objs, procs = [], []
+    for src in srcs:
+        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        flags = [*HIPCC_FLAGS, *PER_FILE_FLAGS.get(os.path.basename(src), []), *extra_flags]
+        procs.append((_run([hipcc(), *flags, *inc, "-c", src, "-o", obj], verbose), src))
+        objs.append(obj)
+    for proc, src in procs:
+        _check(proc, os.path.basename(src), verbose)
+    tmp = LIB + ".tmp"
+    _check(_run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose), "link", verbose)
     os.replace(tmp, LIB)
     return LIB
 

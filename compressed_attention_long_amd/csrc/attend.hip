@@ -9,9 +9,11 @@
 // sink and partial-RoPE rows; atlas Raw config fields head_dim 512, one KV head).
 //
 // Kernel design (gfx950, wave64, bf16 MFMA 16x16x32, fp32 accumulation):
-//  * a block = 4 waves = 64 heads of one query row and one split of its row set;
-//    tiles of 32 rows are staged in LDS once and used by all 4 waves for both
-//    contractions (K = V);
+//  * a block = 8 waves = two groups of 4 waves; each group holds 64 heads (16 per wave)
+//    of one query row and one split of its row set.  Tiles of 32 rows are staged in LDS
+//    and used by all 4 waves of a group for both contractions (K = V); the groups take
+//    alternate tiles and merge their softmax states through LDS at the end, so each SIMD
+//    runs two waves whose load, softmax and MFMA phases overlap;
 //  * scores are computed transposed, S^T = K Q^T (M = rows, N = heads, K = channels),
 //    and the output as O^T = V^T P^T (M = channels, N = heads, K = rows): every
 //    accumulator lane then belongs to one head, so the online-softmax statistics,
@@ -30,14 +32,16 @@
 
 namespace csa {
 
-constexpr int kAttWaves = 4;
+constexpr int kAttWaves = 8;        // two groups of kGroupWaves
+constexpr int kGroupWaves = 4;
+constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kHeadsPerBlock = 64;
 constexpr int kTile = 32;           // rows per LDS tile
 constexpr int kD = 512;             // channels (head dim)
 constexpr int kPitch = 520;         // bf16 per LDS row: 1040 B, rows land 4 banks apart
 constexpr int kTargetBlocks = 256;  // split until the grid has about this many blocks
 constexpr int kSlotChunk = 2048;    // CSA: slots whose row index is staged in LDS at a time
-constexpr int kBufs = 4;            // LDS tile buffers: kBufs - 1 tiles in flight while one is consumed
+constexpr int kBufs = 4;            // LDS tile buffers: one tile pair consumed while the next is in flight
 constexpr float kRescale = 8.f;     // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int window, int stride,
@@ -62,11 +66,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <bool CSA, bool FP8>
-__global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
+__global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[kBufs][kTile * kPitch];
   __shared__ int tvalid[kBufs][kTile];
   __shared__ int srow[CSA ? kSlotChunk : 1];   // CSA: per slot of the current chunk: kv row, -2 - window row, or -1
   __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
+  __shared__ f32x2 mrg_ml[kGroupWaves][kWave];  // group 1's (max, sum) per lane, for the merge
 
   const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const uint32_t total = gridDim.x;
@@ -79,8 +84,9 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  const int grp = wave >> 2, hw = wave & 3;                     // tile group, head block
   const int n = lane & 15, g = lane >> 4;
-  const int head = hg * kHeadsPerBlock + wave * 16 + n;
+  const int head = hg * kHeadsPerBlock + hw * 16 + n;
   const bool head_ok = head < a.H;
 
   const int64_t p = a.q_pos[row];
@@ -117,12 +123,12 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
     if (CSA) return srow[min(max(slot - cbase, 0), kSlotChunk - 1)];
     return slot < n_ent ? slot : -2 - (int)(r_lo + (slot - n_ent));
   };
-  // bf16 rows: wave w moves tile rows w, w+4, ..., w+28 straight into LDS (1 KB per
-  // instruction, 16 B per lane); always 8 loads per wave so vmcnt counts are uniform.
+  // bf16 rows: wave w moves tile rows w, w+8, w+16, w+24 straight into LDS (1 KB per
+  // instruction, 16 B per lane).
   auto issue_tile = [&](int t, int buf, int cbase) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = wave + 4 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int rr = wave + 8 * i;
       const int r = slot_row(s0 + t * kTile + rr, cbase);
       const uint8_t* src = row_src(r);
       const bool fp8_row = FP8 && r >= 0;
@@ -135,13 +141,16 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   };
   // fp8 entry rows: codes and the channel block's scale go through registers and are
   // widened to bf16 (code * scale, rounded) on the way into LDS.
+  // Rows of tile pair `pr` (tiles 2pr and 2pr + 1), 4 per wave per tile: k = 4 * (tile & 1) + i.
   u32x2 pre8[8];
   float pres[8];
-  auto fetch_fp8 = [&](int t, int cbase) {
+  auto fetch_fp8 = [&](int pr, int cbase) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = wave + 4 * i;
-      const int r = slot_row(s0 + t * kTile + rr, cbase);
+    for (int k = 0; k < 8; ++k) {
+      const int t = 2 * pr + (k >> 2);
+      const int rr = wave + 8 * (k & 3);
+      const int i = k;
+      const int r = t < ntile ? slot_row(s0 + t * kTile + rr, cbase) : -1;
       pre8[i] = u32x2{0u, 0u};
       pres[i] = 0.f;
       if (r >= 0) {
@@ -151,11 +160,14 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
       }
     }
   };
-  auto store_fp8 = [&](int t, int buf, int cbase) {
+  auto store_fp8 = [&](int pr, int cbase) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int rr = wave + 4 * i;
-      const int r = slot_row(s0 + t * kTile + rr, cbase);
+    for (int k = 0; k < 8; ++k) {
+      const int t = 2 * pr + (k >> 2);
+      const int buf = t % kBufs;
+      const int rr = wave + 8 * (k & 3);
+      const int i = k;
+      const int r = t < ntile ? slot_row(s0 + t * kTile + rr, cbase) : -1;
       if (r >= 0) {
         const float sc = pres[i];
         const f32x2 f0 = fp8x2_lo(pre8[i][0]), f1 = fp8x2_hi(pre8[i][0]);
@@ -178,13 +190,13 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
 #pragma unroll
   for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
   const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
-  constexpr int kSlotsPerThread = kSlotChunk / 256;
+  constexpr int kSlotsPerThread = kSlotChunk / kAttThreads;
   int jraw[CSA ? kSlotsPerThread : 1];
   if (CSA) {
     const int last = max(n_ent - 1, 0);
 #pragma unroll
     for (int k = 0; k < kSlotsPerThread; ++k)
-      jraw[k] = n_ent > 0 ? idxrow[min(s0 + tid + 256 * k, last)] : -1;
+      jraw[k] = n_ent > 0 ? idxrow[min(s0 + tid + kAttThreads * k, last)] : -1;
   }
   // a CSA split never spans more than kSlotChunk slots (the launcher splits further), so one
   // staged table covers every tile of the split
@@ -192,13 +204,13 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
   if (CSA) {
 #pragma unroll
     for (int k = 0; k < kSlotsPerThread; ++k) {
-      const int slot = cbase + tid + 256 * k;
+      const int slot = cbase + tid + kAttThreads * k;
       int r = -1;
       if (slot < s1) {
         if (slot < n_ent) r = (jraw[k] >= 0 && jraw[k] < kv_nv) ? jraw[k] : -1;
         else r = -2 - (int)(r_lo + (slot - n_ent));
       }
-      srow[tid + 256 * k] = r;
+      srow[tid + kAttThreads * k] = r;
     }
   }
   if (tid < a.rope_dim / 2) {
@@ -207,9 +219,16 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
     rtab[tid] = f32x2{cs, sn};
   }
   __syncthreads();
+  // tile pair pr = tiles 2pr (group 0) and 2pr + 1 (group 1), in buffers 2(pr % 2) + [0, 2)
+  auto issue_pair = [&](int pr) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (2 * pr + k < ntile) issue_tile(2 * pr + k, (2 * pr + k) % kBufs, cbase);
+  };
+  const int npair = (ntile + 1) / 2;
   if (ntile > 0) {
-    for (int t = 0; t < min(kBufs - 1, ntile); ++t) issue_tile(t, t, cbase);
-    if (FP8) { fetch_fp8(0, cbase); store_fp8(0, 0, cbase); }
+    issue_pair(0);
+    if (FP8) { fetch_fp8(0, cbase); store_fp8(0, cbase); }
   }
   // ---- query fragments (B operand of S^T = K Q^T): head = n, channels 32c + 8g + [0, 8).
   // The rotated query is not a bf16 value: its last two chunks (channels 448..511, which
@@ -251,20 +270,18 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t % kBufs;
-    // issue tile t + kBufs - 1 into the buffer tile t - 1 used (freed by the last barrier)
-    const int tn = t + kBufs - 1;
-    if (tn < ntile) issue_tile(tn, tn % kBufs, cbase);
-    if (FP8 && t + 1 < ntile) fetch_fp8(t + 1, cbase);
-    // tile t has landed once at most the loads of the later tiles are outstanding
-    const int later = min(kBufs - 1, ntile - 1 - t);
-    if (FP8) wait_vmcnt<0>();
-    else if (later >= 3) wait_vmcnt<24>();
-    else if (later == 2) wait_vmcnt<16>();
-    else if (later == 1) wait_vmcnt<8>();
-    else wait_vmcnt<0>();
+  for (int pr = 0; pr < npair; ++pr) {
+    // this wave's loads of pair pr are the only ones outstanding; after the barrier the pair
+    // is visible to all and every wave is done with pair pr - 1, whose buffers take pair pr + 1
+    wait_vmcnt<0>();
     __syncthreads();
+    if (pr + 1 < npair) {
+      issue_pair(pr + 1);
+      if (FP8) fetch_fp8(pr + 1, cbase);
+    }
+    const int t = 2 * pr + grp;
+    if (t < ntile) {
+    const int buf = t % kBufs;
     const uint16_t* tl = tile[buf];
 
     // S^T = K Q^T for rows 16kb + [0,16) of the tile
@@ -338,8 +355,33 @@ __global__ void __launch_bounds__(256, 1) k_attend(AttendArgs a) {
       const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
     }
-    if (FP8 && t + 1 < ntile) store_fp8(t + 1, (t + 1) % kBufs, cbase);
+    }
+    if (FP8 && pr + 1 < npair) store_fp8(pr + 1, cbase);
+  }
+
+  // ---- merge group 1's state into group 0 through LDS (the tile buffers are free now)
+  wait_vmcnt<0>();
+  __syncthreads();
+  {
+    f32x4* mbuf = reinterpret_cast<f32x4*>(&tile[0][0]);   // [head block][db][lane]: 128 KB
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) mbuf[(hw * 32 + db) * kWave + lane] = acc[db];
+      mrg_ml[hw][lane] = f32x2{m_run, l_run};
+    }
     __syncthreads();
+    if (grp == 1) return;
+    const f32x2 ml = mrg_ml[hw][lane];
+    const float M = fmaxf(m_run, ml[0]);
+    const float sa = fast_exp2(m_run - M), sb = fast_exp2(ml[0] - M);
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const f32x4 o = mbuf[(hw * 32 + db) * kWave + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * sa + o[i] * sb;
+    }
+    l_run = l_run * sa + ml[1] * sb;
+    m_run = M;
   }
 
   // ---- epilogue
@@ -488,11 +530,11 @@ hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   const bool f8 = a.kv_dtype == CSA_FP8_E4M3;
   dim3 grid((unsigned)blocks);
   if (csa) {
-    if (f8) hipLaunchKernelGGL((k_attend<true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attend<true, false>), grid, dim3(256), 0, s, a);
+    if (f8) hipLaunchKernelGGL((k_attend<true, true>), grid, dim3(kAttThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attend<true, false>), grid, dim3(kAttThreads), 0, s, a);
   } else {
-    if (f8) hipLaunchKernelGGL((k_attend<false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_attend<false, false>), grid, dim3(256), 0, s, a);
+    if (f8) hipLaunchKernelGGL((k_attend<false, true>), grid, dim3(kAttThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_attend<false, false>), grid, dim3(kAttThreads), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -174,8 +174,88 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
   }
 }
 
+// Long windows (HCA: 128 tokens per row): one block per (row, 128-channel slice).  The
+// window's tokens are dealt round-robin to 16 groups of 16 lanes (8 channels per lane), so
+// all of a row's loads are in flight at once instead of walking the window serially; the
+// 16 partial softmax states are merged through LDS.  Requires C % 128 == 0 and fp8 scale
+// blocks of at most 128 channels (one block never spans two slices).
+constexpr int kSplitGroups = 16;
+constexpr int kSliceC = 128;
+
+__global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
+  __shared__ float sm_m[kSplitGroups][kSliceC], sm_s[kSplitGroups][kSliceC], sm_v[kSplitGroups][kSliceC];
+  const int li = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int cs = li * 8;                                    // channel within the slice
+  const int c0 = blockIdx.z * kSliceC + cs;
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
+  const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
+                                : nullptr;
+  PoolState p;
+  pool_reset(p);
+  const int t0 = i * a.stride;
+  // group g takes tokens g, g + 16, g + 32, ... of the window, kU of them per load round
+  const int mine = g < a.window ? (a.window - 1 - g) / kSplitGroups + 1 : 0;
+  for (int u0 = 0; u0 < mine; u0 += kU) {
+    u32x4 wv[kU], wz[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (u0 + u < mine) {
+        const int64_t t = t0 + g + (int64_t)(u0 + u) * kSplitGroups;
+        wv[u] = *reinterpret_cast<const u32x4*>(kv + t * a.ld_tok + c0);
+        wz[u] = lg ? *reinterpret_cast<const u32x4*>(lg + t * a.ld_tok + c0) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (u0 + u < mine) {
+        float v[8], z[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = bf16lo_to_f32(wv[u][k]);
+          v[2 * k + 1] = bf16hi_to_f32(wv[u][k]);
+          z[2 * k] = bf16lo_to_f32(wz[u][k]) * kLog2e;
+          z[2 * k + 1] = bf16hi_to_f32(wz[u][k]) * kLog2e;
+        }
+        pool_add(p, v, z);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    sm_m[g][cs + k] = p.m[k];
+    sm_s[g][cs + k] = p.s[k];
+    sm_v[g][cs + k] = p.sv[k];
+  }
+  __syncthreads();
+  if (g != 0) return;
+  // group 0 merges the 16 states of its 8 channels (groups without tokens hold s = 0)
+  PoolState q;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float m = kNegBig;
+    for (int h = 0; h < kSplitGroups; ++h) m = fmaxf(m, sm_m[h][cs + k]);
+    float ss = 0.f, sv = 0.f;
+    for (int h = 0; h < kSplitGroups; ++h) {
+      const float f = exp2f(sm_m[h][cs + k] - m);
+      ss += sm_s[h][cs + k] * f;
+      sv += sm_v[h][cs + k] * f;
+    }
+    q.m[k] = m;
+    q.s[k] = ss;
+    q.sv[k] = sv;
+  }
+  finish_row(q, a, b, a.first_row + i, c0, li);
+}
+
 hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   CompressArgs a = a0;
+  if (a.window >= 2 * kSplitGroups && a.C % kSliceC == 0 && (a.dtype == CSA_BF16 || a.scale_block <= kSliceC)) {
+    if (a.n_new == 0 || a.B == 0) return hipSuccess;
+    dim3 grid(a.n_new, a.B, a.C / kSliceC);
+    hipLaunchKernelGGL(k_compress_split, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int lanes = a.C / 8;
   const int groups = 256 / lanes;
   // Long runs amortise the extra leading block of overlapping windows; short runs keep

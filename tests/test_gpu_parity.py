@@ -192,7 +192,7 @@ def test_topk_clustered_scores():
 # ---------------------------------------------------------------- attention
 
 def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, qmul, seed, out_dtype="fp32",
-                 win_start=None):
+                 win_start=None, kv_gain=None):
     d = ci.Draw(seed, "cpu")
     q = d.normal((B, Tq, H, 512), std=qmul / math.sqrt(512))
     sink = d.normal((H,), dtype=torch.float32)
@@ -203,6 +203,8 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
         kv_ref = O.fp8_block_dequantize(codes.numpy(), sc.numpy(), 64)
     else:
         kvt = d.normal((B, cap, 512))
+        if kv_gain is not None:
+            kvt = (kvt.float() * torch.as_tensor(kv_gain, dtype=torch.float32)[None, :, None]).to(torch.bfloat16)
         kv = ops.Cache(kvt.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV), None, 8, 4)
         kv_ref = np64(kvt)
     if mode == "hca":
@@ -271,6 +273,17 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
 ])
 def test_attend_parity(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul):
     _attend_case(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul, seed=400 + cap + H)
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_attend_scores_far_above_first_tile(mode):
+    """Rows of the first tile score ~100 log2 units below later rows (small-norm rows first,
+    then large-norm rows), so the first tile's maximum is no usable softmax reference and
+    the kernel must fall back to the split's exact maximum."""
+    cap = 3000
+    gain = np.where(np.arange(cap) < 400, 0.01, 3.0)
+    topk = 1024 if mode == "csa" else 0
+    _attend_case(mode, 1, 1, 128, cap, [cap], False, topk, 128, 129, 1.0, 8.0, seed=31, kv_gain=gain)
 
 
 def test_attend_window_cut_by_stream_start():
