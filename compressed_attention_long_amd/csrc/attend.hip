@@ -40,7 +40,6 @@ constexpr int kTile = 32;           // rows per LDS tile
 constexpr int kD = 512;             // channels (head dim)
 constexpr int kPitch = 520;         // bf16 per LDS row: 1040 B, rows land 4 banks apart
 constexpr int kTargetBlocks = 256;  // split until the grid has about this many blocks
-constexpr int kSlotChunk = 2048;    // CSA: slots whose row index is staged in LDS at a time
 constexpr int kBufs = 4;            // LDS tile buffers: one tile pair consumed while the next is in flight
 constexpr float kRescale = 8.f;     // lazy-rescale threshold (log2 units)
 
@@ -67,9 +66,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <bool CSA, bool FP8>
 __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kBufs][kTile * kPitch];
+  // Four tile buffers as four objects: a pair of tiles is read from one half while the next
+  // pair streams into the other, and separate objects let the compiler see that the LDS
+  // reads never touch the half in flight (it then does not wait for those loads).
+  __shared__ __attribute__((aligned(16))) uint16_t tbA0[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tbA1[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tbB0[kTile * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tbB1[kTile * kPitch];
   __shared__ int tvalid[kBufs][kTile];
-  __shared__ int srow[CSA ? kSlotChunk : 1];   // CSA: per slot of the current chunk: kv row, -2 - window row, or -1
   __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
   __shared__ f32x2 mrg_ml[kGroupWaves][kWave];  // group 1's (max, sum) per lane, for the merge
 
@@ -108,128 +112,121 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   const int s1 = min(n_slots, s0 + a.slots_per_split);
   const int ntile = s1 > s0 ? (s1 - s0 + kTile - 1) / kTile : 0;
 
-  // ---- slot table and the first tiles go out before the query setup so their latency overlaps it
+  // ---- rows.  Wave w moves rows w, w+8, w+16, w+24 of both tiles of a tile pair (tiles 2pr
+  // and 2pr + 1).  Lane k < 8 of the wave prepares the row of tile 2pr + (k >> 2), tile row
+  // w + 8 (k & 3), a pair ahead: its number (a kv row >= 0, -2 - a window row, or -1 for no
+  // row) and its byte offset from the kv base; the loads then take both from that lane.
   const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * (FP8 ? kD : 2 * kD);
   const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
-  auto row_src = [&](int r) -> const uint8_t* {
-    if (r >= 0) return kvb + (int64_t)r * (FP8 ? kD : 2 * kD);
-    if (r <= -2) return winb + (int64_t)(-2 - r) * (2 * kD);
-    return kvb;   // unused slot: any valid row (masked by tvalid)
+  const int64_t win_off = winb - kvb;   // window rows are addressed from the kv base too
+  struct PairRows {
+    int r;          // row number (lanes 0..7)
+    int64_t off;    // byte offset of the row from kvb (any valid row when there is none)
   };
-  // row of a slot: CSA reads the staged table, HCA maps slots to rows directly
-  auto slot_row = [&](int slot, int cbase) -> int {
-    if (slot >= s1) return -1;
-    if (CSA) return srow[min(max(slot - cbase, 0), kSlotChunk - 1)];
-    return slot < n_ent ? slot : -2 - (int)(r_lo + (slot - n_ent));
+  // the raw top-k index behind lane k's row (CSA entries only), loaded a pair ahead; turning
+  // it into a row waits until the pair is issued, so the load's latency stays hidden
+  auto pair_idx = [&](int pr) -> int {
+    const int k = lane & 7;
+    const int t = 2 * pr + (k >> 2);
+    const int slot = s0 + t * kTile + wave + 8 * (k & 3);
+    int j = -1;
+    if (CSA && lane < 8 && t < ntile && slot < s1 && slot < n_ent) j = idxrow[slot];
+    return j;
   };
-  // bf16 rows: wave w moves tile rows w, w+8, w+16, w+24 straight into LDS (1 KB per
-  // instruction, 16 B per lane).
-  auto issue_tile = [&](int t, int buf, int cbase) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = wave + 8 * i;
-      const int r = slot_row(s0 + t * kTile + rr, cbase);
-      const uint8_t* src = row_src(r);
-      const bool fp8_row = FP8 && r >= 0;
-      if (!fp8_row) {
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + 16 * lane),
-                                         (lds_void*)&tile[buf][rr * kPitch], 16, 0, 0);
-      }
-      if (lane == 0) tvalid[buf][rr] = r != -1;
+  auto pair_rows = [&](int pr, int j) -> PairRows {
+    const int k = lane & 7;
+    const int t = 2 * pr + (k >> 2);
+    const int slot = s0 + t * kTile + wave + 8 * (k & 3);
+    int r = -1;
+    if (lane < 8 && t < ntile && slot < s1) {
+      if (slot >= n_ent) r = -2 - (int)(r_lo + (slot - n_ent));
+      else if (!CSA) r = slot;
+      else r = (j >= 0 && j < kv_nv) ? j : -1;
     }
+    const int64_t off = r >= 0 ? (int64_t)r * (FP8 ? kD : 2 * kD)
+                               : (r <= -2 ? win_off + (int64_t)(-2 - r) * (2 * kD) : 0);
+    return PairRows{r, off};
+  };
+  // bf16 rows go straight into LDS (1 KB per instruction, 16 B per lane).  The valid flags
+  // of a pair are written first; the 8 loads may then be spread over the compute.
+  auto mark_pair = [&](int pr, const PairRows& pr_rows, int bnxt) {
+    if (lane < 8) {
+      const int t = 2 * pr + (lane >> 2);
+      if (t < ntile) tvalid[bnxt + (lane >> 2)][wave + 8 * (lane & 3)] = pr_rows.r != -1;
+    }
+  };
+  auto issue_row = [&](int pr, const PairRows& pr_rows, int k, uint16_t* n0, uint16_t* n1) {
+    const int t = 2 * pr + (k >> 2);
+    if (t >= ntile) return;
+    if (FP8 && __builtin_amdgcn_readlane(pr_rows.r, k) >= 0) return;   // fp8 rows: register path
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(pr_rows.off >> 32), k);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)pr_rows.off, k);
+    const int64_t off = (int64_t)((hi << 32) | lo);
+    uint16_t* dst = (k >> 2) ? n1 : n0;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kvb + off + 16 * lane),
+                                     (lds_void*)&dst[(wave + 8 * (k & 3)) * kPitch], 16, 0, 0);
   };
   // fp8 entry rows: codes and the channel block's scale go through registers and are
   // widened to bf16 (code * scale, rounded) on the way into LDS.
-  // Rows of tile pair `pr` (tiles 2pr and 2pr + 1), 4 per wave per tile: k = 4 * (tile & 1) + i.
   u32x2 pre8[8];
   float pres[8];
-  auto fetch_fp8 = [&](int pr, int cbase) {
+  auto fetch_fp8 = [&](int pr, const PairRows& pr_rows) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int t = 2 * pr + (k >> 2);
-      const int rr = wave + 8 * (k & 3);
-      const int i = k;
-      const int r = t < ntile ? slot_row(s0 + t * kTile + rr, cbase) : -1;
-      pre8[i] = u32x2{0u, 0u};
-      pres[i] = 0.f;
-      if (r >= 0) {
+      const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
+      pre8[k] = u32x2{0u, 0u};
+      pres[k] = 0.f;
+      if (2 * pr + (k >> 2) < ntile && r >= 0) {
         const int64_t rg = (int64_t)b * a.kv_cap + r;
-        pre8[i] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.kv) + rg * kD + 8 * lane);
-        pres[i] = a.kv_scales[rg * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
+        pre8[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.kv) + rg * kD + 8 * lane);
+        pres[k] = a.kv_scales[rg * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
       }
     }
   };
-  auto store_fp8 = [&](int pr, int cbase) {
+  auto store_fp8 = [&](int pr, const PairRows& pr_rows, uint16_t* n0, uint16_t* n1) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int t = 2 * pr + (k >> 2);
-      const int buf = t % kBufs;
-      const int rr = wave + 8 * (k & 3);
-      const int i = k;
-      const int r = t < ntile ? slot_row(s0 + t * kTile + rr, cbase) : -1;
-      if (r >= 0) {
-        const float sc = pres[i];
-        const f32x2 f0 = fp8x2_lo(pre8[i][0]), f1 = fp8x2_hi(pre8[i][0]);
-        const f32x2 f2 = fp8x2_lo(pre8[i][1]), f3 = fp8x2_hi(pre8[i][1]);
+      const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
+      if (t < ntile && r >= 0) {
+        const float sc = pres[k];
+        const f32x2 f0 = fp8x2_lo(pre8[k][0]), f1 = fp8x2_hi(pre8[k][0]);
+        const f32x2 f2 = fp8x2_lo(pre8[k][1]), f3 = fp8x2_hi(pre8[k][1]);
         u32x4 v;
         v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
         v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
         v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
         v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
-        *reinterpret_cast<u32x4*>(&tile[buf][rr * kPitch + 8 * lane]) = v;
+        uint16_t* dst = (k >> 2) ? n1 : n0;
+        *reinterpret_cast<u32x4*>(&dst[(wave + 8 * (k & 3)) * kPitch + 8 * lane]) = v;
       }
     }
   };
 
-  // ---- prologue: every independent global load (query fragments, rotary frequencies, the
-  // split's row indices) is issued first so that their latencies overlap; then one barrier
-  // publishes the slot table and the rotation table, and the first tiles go out.
+  // ---- prologue: the first two pairs' row numbers are loaded first (they gate the first
+  // tile loads) and the first pair's rows go out as soon as they arrive; the query
+  // fragments follow, and the rotation table is built while they are in flight.
+  const int npair = (ntile + 1) / 2;
+  const PairRows rows0 = pair_rows(0, pair_idx(0));
+  int idx_next = pair_idx(1);
+  const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
+  if (ntile > 0) {
+    mark_pair(0, rows0, 0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) issue_row(0, rows0, k, tbA0, tbA1);
+    if (FP8) { fetch_fp8(0, rows0); store_fp8(0, rows0, tbA0, tbA1); }
+  }
   const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + min(head, a.H - 1)) * kD;
   u32x4 qraw[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
-  const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
-  constexpr int kSlotsPerThread = kSlotChunk / kAttThreads;
-  int jraw[CSA ? kSlotsPerThread : 1];
-  if (CSA) {
-    const int last = max(n_ent - 1, 0);
-#pragma unroll
-    for (int k = 0; k < kSlotsPerThread; ++k)
-      jraw[k] = n_ent > 0 ? idxrow[min(s0 + tid + kAttThreads * k, last)] : -1;
-  }
-  // a CSA split never spans more than kSlotChunk slots (the launcher splits further), so one
-  // staged table covers every tile of the split
-  const int cbase = s0;
-  if (CSA) {
-#pragma unroll
-    for (int k = 0; k < kSlotsPerThread; ++k) {
-      const int slot = cbase + tid + kAttThreads * k;
-      int r = -1;
-      if (slot < s1) {
-        if (slot < n_ent) r = (jraw[k] >= 0 && jraw[k] < kv_nv) ? jraw[k] : -1;
-        else r = -2 - (int)(r_lo + (slot - n_ent));
-      }
-      srow[tid + kAttThreads * k] = r;
-    }
-  }
   if (tid < a.rope_dim / 2) {
     float cs, sn;
     rope_cs(p, fr, cs, sn);
     rtab[tid] = f32x2{cs, sn};
   }
   __syncthreads();
-  // tile pair pr = tiles 2pr (group 0) and 2pr + 1 (group 1), in buffers 2(pr % 2) + [0, 2)
-  auto issue_pair = [&](int pr) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (2 * pr + k < ntile) issue_tile(2 * pr + k, (2 * pr + k) % kBufs, cbase);
-  };
-  const int npair = (ntile + 1) / 2;
-  if (ntile > 0) {
-    issue_pair(0);
-    if (FP8) { fetch_fp8(0, cbase); store_fp8(0, cbase); }
-  }
   // ---- query fragments (B operand of S^T = K Q^T): head = n, channels 32c + 8g + [0, 8).
   // The rotated query is not a bf16 value: its last two chunks (channels 448..511, which
   // hold the rotated pairs for rope_dim <= 64) are carried as bf16 hi + lo so the logits
@@ -270,19 +267,26 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int pr = 0; pr < npair; ++pr) {
-    // this wave's loads of pair pr are the only ones outstanding; after the barrier the pair
-    // is visible to all and every wave is done with pair pr - 1, whose buffers take pair pr + 1
+  // One tile pair: c0/c1 hold pair pr (buffer ids bcur, bcur + 1), n0/n1 receive pair pr + 1.
+  auto pair_step = [&](int pr, const uint16_t* c0, const uint16_t* c1, uint16_t* n0, uint16_t* n1, int bcur) {
+    // this wave's loads of pair pr are the only tile loads outstanding; after the barrier the
+    // pair is visible to all and every wave is done with pair pr - 1, whose buffers take pair
+    // pr + 1; the row numbers of pair pr + 2 are fetched meanwhile
     wait_vmcnt<0>();
     __syncthreads();
-    if (pr + 1 < npair) {
-      issue_pair(pr + 1);
-      if (FP8) fetch_fp8(pr + 1, cbase);
+    const PairRows rows_cur = pair_rows(pr + 1, idx_next);
+    const bool more = pr + 1 < npair;   // false whenever this group has no tile in pair pr
+    if (more) {
+      mark_pair(pr + 1, rows_cur, bcur ^ 2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) issue_row(pr + 1, rows_cur, k, n0, n1);
+      if (FP8) fetch_fp8(pr + 1, rows_cur);
     }
+    idx_next = pair_idx(pr + 2);
     const int t = 2 * pr + grp;
     if (t < ntile) {
-    const int buf = t % kBufs;
-    const uint16_t* tl = tile[buf];
+    const int buf = bcur + grp;
+    const uint16_t* tl = grp ? c1 : c0;
 
     // S^T = K Q^T for rows 16kb + [0,16) of the tile
     f32x4 sacc[2];
@@ -356,17 +360,23 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
     }
     }
-    if (FP8 && pr + 1 < npair) store_fp8(pr + 1, cbase);
+    if (FP8 && more) store_fp8(pr + 1, rows_cur, n0, n1);
+  };
+  for (int pr = 0; pr < npair; pr += 2) {
+    pair_step(pr, tbA0, tbA1, tbB0, tbB1, 0);
+    if (pr + 1 < npair) pair_step(pr + 1, tbB0, tbB1, tbA0, tbA1, 2);
   }
 
   // ---- merge group 1's state into group 0 through LDS (the tile buffers are free now)
   wait_vmcnt<0>();
   __syncthreads();
   {
-    f32x4* mbuf = reinterpret_cast<f32x4*>(&tile[0][0]);   // [head block][db][lane]: 128 KB
+    // head block hw's 32 KB go to tile buffer hw
+    uint16_t* mb16 = hw == 0 ? tbA0 : (hw == 1 ? tbA1 : (hw == 2 ? tbB0 : tbB1));
+    f32x4* mbuf = reinterpret_cast<f32x4*>(mb16);   // [db][lane]
     if (grp == 1) {
 #pragma unroll
-      for (int db = 0; db < 32; ++db) mbuf[(hw * 32 + db) * kWave + lane] = acc[db];
+      for (int db = 0; db < 32; ++db) mbuf[db * kWave + lane] = acc[db];
       mrg_ml[hw][lane] = f32x2{m_run, l_run};
     }
     __syncthreads();
@@ -376,7 +386,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     const float sa = fast_exp2(m_run - M), sb = fast_exp2(ml[0] - M);
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
-      const f32x4 o = mbuf[(hw * 32 + db) * kWave + lane];
+      const f32x4 o = mbuf[db * kWave + lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * sa + o[i] * sb;
     }
@@ -499,7 +509,6 @@ int attend_nsplit(int rows, int H, int slot_cap, bool csa) {
   const int max_ns = (slot_cap + 2 * kTile - 1) / (2 * kTile);   // at least two tiles per split
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
-  if (csa && ns < (slot_cap + kSlotChunk - 1) / kSlotChunk) ns = (slot_cap + kSlotChunk - 1) / kSlotChunk;
   // round the per-split count up to whole tiles, then recount
   int sps = (slot_cap + ns - 1) / ns;
   sps = (sps + kTile - 1) / kTile * kTile;

@@ -64,19 +64,18 @@ __device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float x) {
 
 // ---------------------------------------------------------------- rotary
 
-// (cos, sin) of pos * inv_freq evaluated in fp64, returned in fp32.  The angle is formed
-// in fp64 and reduced modulo 2*pi first (k = nearest integer to angle / 2pi, then angle -
-// k * 2pi with 2pi split into a 53-bit head and a tail, Cody-Waite style), so sincos always
-// runs on |r| <= pi; for the positions here (k < 2^22) the reduction error is ~1e-16 rad.
+// (cos, sin) of pos * inv_freq, returned in fp32.  The angle is formed in fp64 and reduced
+// modulo 2*pi there (k = nearest integer to angle / 2pi, then angle - k * 2pi with 2pi split
+// into a 53-bit head and a tail, Cody-Waite style; for the positions here, k < 2^22, the
+// reduction error is ~1e-16 rad).  The reduced angle |r| <= pi is then rounded to fp32
+// (error <= 2^-23 rad) and its sine and cosine taken in fp32 (a few fp32 ulps): far below
+// the bf16 rounding of the rotated values.
 __device__ __forceinline__ void rope_cs(int64_t pos, double inv_freq, float& c, float& s) {
   const double ang = (double)pos * inv_freq;
   const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
   double r = fma(-k, 6.283185307179586, ang);                // 2 pi, head
   r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi, tail
-  double sd, cd;
-  sincos(r, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+  sincosf((float)r, &s, &c);
 }
 
 // ---------------------------------------------------------------- XCD-aware block order
