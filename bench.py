@@ -95,12 +95,24 @@ def capture_graphs(layers, torch):
     return graphs
 
 
+def capture_chain(layers, torch):
+    """One HIP graph holding the steps of all layers in order (as a decode step of a model
+    replays all its layers from one graph)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for L in layers:
+            L.run()
+    torch.cuda.synchronize()
+    return g
+
+
 def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layers=30):
     """Time `steps_n` steps rotating over distinct layers; return timings (ms).
 
-    Headline: the step replayed from a HIP graph per layer (launch overhead removed, as a
-    serving loop would run it).  Breakdown: an eager pass with events around each C-ABI
-    call on the launch stream.
+    Headline: layer steps replayed from one HIP graph that chains all rotated layers (as a
+    serving loop replays a model's layers), K steps = K // L chain replays plus K % L
+    single-layer graphs.  Also: one graph per layer step (includes a graph launch per step),
+    and an eager pass with events around each C-ABI call on the launch stream.
     """
     n_layers = max(2, min(max_layers, math.ceil(min_cache_bytes / max(layer_bytes(wl), 1))))
     layers = build_layers(wl, n_layers, "cuda", torch, torch.bfloat16)
@@ -119,6 +131,21 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     g0.record()
     for i in range(steps_n):
         graphs[i % n_layers].replay()
+    g1.record()
+    torch.cuda.synchronize()
+    wall_per_layer_graph = (time.perf_counter() - t0) * 1e3 / steps_n
+    graph_gpu_per_layer_graph = g0.elapsed_time(g1) / steps_n
+    # --- chained graph (headline)
+    chain = capture_chain(layers, torch)
+    for i in range(max(1, warmup // n_layers)):
+        chain.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record()
+    for i in range(steps_n // n_layers):
+        chain.replay()
+    for i in range(steps_n % n_layers):
+        graphs[i].replay()
     g1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps_n
@@ -151,9 +178,11 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     out["step_gpu_median"] = med(per["step_gpu"])
     out["wall_ms_per_step"] = wall
     out["graph_gpu_ms_per_step"] = graph_gpu
+    out["per_layer_graph_wall_ms_per_step"] = wall_per_layer_graph
+    out["per_layer_graph_gpu_ms_per_step"] = graph_gpu_per_layer_graph
     out["eager_wall_ms_per_step"] = eager_wall
     out["layers"] = n_layers
-    del graphs, layers
+    del graphs, chain, layers
     torch.cuda.empty_cache()
     return out
 
@@ -259,9 +288,11 @@ def main():
         roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": calls[dom]["hbm_frac"], "traffic": None,
                 "kernel": "csa_index_topk (k_index_scores + k_topk)" if dom == "index" else "csa_compress"}
-    extra = {"calls": calls, "timing": "value = tokens / wall time of HIP-graph replays (one graph per layer step); "
+    extra = {"calls": calls, "timing": "value = tokens / wall time of layer steps replayed from one HIP graph "
+                                       "chaining the rotated layers; per_layer_graph = one graph launch per step; "
                                        "calls = eager pass with HIP events around each C-ABI call",
              "graph_gpu_ms_per_step": tm["graph_gpu_ms_per_step"], "eager_wall_ms_per_step": tm["eager_wall_ms_per_step"],
+             "per_layer_graph_ms_per_step": tm["per_layer_graph_wall_ms_per_step"],
              "step_gpu_ms": tm["step_gpu"], "step_gpu_median_ms": tm["step_gpu_median"],
              "layers_rotated": tm["layers"], "pages_config_context": {
                  "layers": 61, "csa_layers": 30, "hca_layers": 31, "heads": 128, "head_dim": 512,

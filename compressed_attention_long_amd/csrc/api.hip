@@ -124,11 +124,14 @@ int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_
   return ok();
 }
 
+static size_t index_scores_bytes(int B, int Tq, int cap) {
+  return ((size_t)B * Tq * cap * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t csa_index_topk_workspace_bytes(int B, int Tq, int Hi, int cap, int topk) {
   (void)Hi;
-  (void)topk;
-  if (B <= 0 || Tq <= 0 || cap <= 0) return 0;
-  return (size_t)B * Tq * cap * sizeof(float) + 256;
+  if (B <= 0 || Tq <= 0 || cap <= 0 || topk <= 0) return 0;
+  return index_scores_bytes(B, Tq, cap) + csa::topk_workspace(B * Tq, cap, topk);
 }
 
 int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int B, int Tq, int Hi,
@@ -147,16 +150,19 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int 
   REQUIRE(aligned(q_idx, 16), CSA_EINVAL, "q_idx must be 16-byte aligned");
   const int64_t rows = (int64_t)B * Tq;
   REQUIRE(rows <= 0x7fffffff && (keys->cap + 1023) / 1024 <= 65535, CSA_ENOTSUP, "problem too large");
-  float* scores = scores_out;
-  if (scores == nullptr) {
-    const size_t need = csa_index_topk_workspace_bytes(B, Tq, Hi, keys->cap, topk);
+  // workspace: [scores unless scores_out is given][two-stage top-k candidates of long rows]
+  const size_t sc_bytes = scores_out ? 0 : index_scores_bytes(B, Tq, keys->cap);
+  const csa::TopkPlan plan = csa::topk_plan((int)rows, keys->cap, topk);
+  const size_t cand_bytes = csa::topk_workspace((int)rows, keys->cap, topk);
+  const size_t need = sc_bytes + cand_bytes;
+  if (need > 0) {
     REQUIRE(workspace != nullptr && workspace_bytes >= need, CSA_EWORKSPACE,
             "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
     REQUIRE(aligned(workspace, 256), CSA_EINVAL, "workspace must be 256-byte aligned");
-    scores = static_cast<float*>(workspace);
-  } else {
-    REQUIRE(aligned(scores_out, 16), CSA_EINVAL, "scores_out must be 16-byte aligned");
   }
+  if (scores_out) REQUIRE(aligned(scores_out, 16), CSA_EINVAL, "scores_out must be 16-byte aligned");
+  float* scores = scores_out ? scores_out : static_cast<float*>(workspace);
+  uint8_t* cand = static_cast<uint8_t*>(workspace) + sc_bytes;
   csa::IndexArgs a{};
   a.q_idx = q_idx;
   a.w = w;
@@ -176,6 +182,7 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int 
   a.topk = topk;
   a.scores = scores;
   a.idx_out = idx_out;
+  if (plan.mode == 1) a.cand_key = reinterpret_cast<uint32_t*>(cand);   // carved by the launcher
   hipError_t e = csa::launch_index_scores(a, stream);
   REQUIRE(e == hipSuccess, CSA_EHIP, "index score launch failed: %s", hipGetErrorString(e));
   e = csa::launch_topk(a, stream);

@@ -451,35 +451,68 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   }
 }
 
-// Merge split partials: M = max m_s, Z = sum l_s 2^(m_s - M), o = sum 2^(m_s - M) o_s / Z,
-// then rotate back and store.  grid: rows * H blocks of 128 lanes (4 channels each).
-__global__ void __launch_bounds__(128) k_attend_combine(AttendArgs a) {
-  const int rh = blockIdx.x;               // row * H + head
-  const int row = rh / a.H;
-  const int d0 = threadIdx.x * 4;
+// Merge split partials: M = max(sink, m_s), Z = 2^(sink - M) + sum l_s 2^(m_s - M),
+// o = sum 2^(m_s - M) o_s / Z, then rotate back and store.  A block of 256 lanes merges 4
+// (row, head) pairs, 8 channels per lane; every split's (max, sum) is read before any output
+// partial so that all of a lane's loads are in flight together.
+constexpr int kCombineHeads = 4;
+__global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
+  const int rows = a.B * a.Tq;
+  const int rh = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);   // row * H + head
+  if (rh >= rows * a.H) return;
+  const int row = rh / a.H, head = rh % a.H;
+  const int d0 = (threadIdx.x & 63) * 8;
   const int64_t p = a.q_pos[row];
-  const float sink2 = a.sink[rh % a.H] * kLog2e;
+  const float sink2 = a.sink[head] * kLog2e;
+  const int64_t base = (int64_t)row * a.nsplit * a.H + head;        // partial (row, s, head) = base + s * H
   float M = sink2;
-  for (int s = 0; s < a.nsplit; ++s)
-    M = fmaxf(M, a.part_ml[2 * (((int64_t)row * a.nsplit + s) * a.H + rh % a.H)]);
+  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * a.H)]);
   float Z = exp2f(sink2 - M);
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t pr = ((int64_t)row * a.nsplit + s) * a.H + rh % a.H;
-    const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
-    const float wgt = exp2f(ms - M);
-    Z += ls * wgt;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= a.nsplit; s += 4) {
+    f32x4 v[4][2];
+    float ms[4], ls[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] += wgt * v[i];
+    for (int u = 0; u < 4; ++u) {
+      const int64_t pr = base + (int64_t)(s + u) * a.H;
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * pr);
+      ms[u] = ml[0];
+      ls[u] = ml[1];
+      v[u][0] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
+      v[u][1] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = exp2f(ms[u] - M);
+      Z += ls[u] * w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[i] += w * v[u][0][i];
+        o[4 + i] += w * v[u][1][i];
+      }
+    }
+  }
+  for (; s < a.nsplit; ++s) {
+    const int64_t pr = base + (int64_t)s * a.H;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * pr);
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4);
+    const float w = exp2f(ml[0] - M);
+    Z += ml[1] * w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] += w * v0[i];
+      o[4 + i] += w * v1[i];
+    }
   }
   const float inv = Z > 0.f ? 1.f / Z : 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] *= inv;
+  for (int i = 0; i < 8; ++i) o[i] *= inv;
   const int rot0 = kD - a.rope_dim;
-  if (a.rope_dim > 0 && d0 + 4 > rot0) {
+  if (a.rope_dim > 0 && d0 + 8 > rot0) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
+    for (int k2 = 0; k2 < 4; ++k2) {
       const int d = d0 + 2 * k2;
       if (d >= rot0) {
         float cs, sn;
@@ -492,14 +525,16 @@ __global__ void __launch_bounds__(128) k_attend_combine(AttendArgs a) {
   }
   const int64_t off = (int64_t)rh * kD + d0;
   if (a.out_dtype == CSA_FP32) {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = f32x4{o[0], o[1], o[2], o[3]};
+    float* op = reinterpret_cast<float*>(a.out) + off;
+    *reinterpret_cast<f32x4*>(op) = f32x4{o[0], o[1], o[2], o[3]};
+    *reinterpret_cast<f32x4*>(op + 4) = f32x4{o[4], o[5], o[6], o[7]};
   } else {
-    u32x2 w2;
-    w2[0] = pack_bf16x2(o[0], o[1]);
-    w2[1] = pack_bf16x2(o[2], o[3]);
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w2;
+    u32x4 w4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(o[2 * k], o[2 * k + 1]);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + off) = w4;
   }
-  if (a.lse && threadIdx.x == 0) a.lse[rh] = (M + log2f(Z)) * kLn2;
+  if (a.lse && d0 == 0) a.lse[rh] = (M + log2f(Z)) * kLn2;
 }
 
 int attend_nsplit(int rows, int H, int slot_cap, bool csa) {
@@ -548,7 +583,7 @@ hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nsplit > 1) {
-    hipLaunchKernelGGL(k_attend_combine, dim3(rows * a.H), dim3(128), 0, s, a);
+    hipLaunchKernelGGL(k_attend_combine, dim3((rows * a.H + kCombineHeads - 1) / kCombineHeads), dim3(256), 0, s, a);
     e = hipGetLastError();
   }
   return e;

@@ -84,21 +84,39 @@ __device__ __forceinline__ void pool_block(PoolState& p, const uint16_t* kv, con
   }
 }
 
+// Rotary inputs of a lane's 8 channels, loaded before the pooling so their latency overlaps
+// it: the sequence's position origin and the frequencies of the lane's rotated pairs.
+struct RopeIn {
+  int64_t pos0;
+  double fr[4];
+};
+__device__ __forceinline__ RopeIn rope_in(const CompressArgs& a, int b, int c0) {
+  RopeIn r;
+  r.pos0 = a.pos0[b];
+  const int rot0 = a.C - a.rope_dim;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = c0 + 2 * k;
+    r.fr[k] = (a.rope_dim > 0 && c >= rot0) ? a.inv_freq[(c - rot0) >> 1] : 0.0;
+  }
+  return r;
+}
+
 // Finish one row: normalise, rotate, store.
-__device__ __forceinline__ void finish_row(const PoolState& p, const CompressArgs& a, int b, int row,
-                                           int c0, int lane_in_group) {
+__device__ __forceinline__ void finish_row(const PoolState& p, const CompressArgs& a, const RopeIn& ri, int b,
+                                           int row, int c0) {
   float e[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) e[i] = p.sv[i] / p.s[i];
   const int rot0 = a.C - a.rope_dim;
   if (c0 + 8 > rot0 && a.rope_dim > 0) {
-    int64_t pos = a.pos0[b] + (int64_t)row * a.stride + (a.window - 1);
+    int64_t pos = ri.pos0 + (int64_t)row * a.stride + (a.window - 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       int c = c0 + 2 * k;
       if (c >= rot0) {
         float cs, sn;
-        rope_cs(pos, a.inv_freq[(c - rot0) >> 1], cs, sn);
+        rope_cs(pos, ri.fr[k], cs, sn);
         float x0 = e[2 * k], x1 = e[2 * k + 1];
         e[2 * k] = x0 * cs - x1 * sn;
         e[2 * k + 1] = x0 * sn + x1 * cs;
@@ -134,7 +152,6 @@ __device__ __forceinline__ void finish_row(const PoolState& p, const CompressArg
       a.scales[((int64_t)b * a.cap + row) * nsb + c0 / a.scale_block] = scale;
     }
   }
-  (void)lane_in_group;
 }
 
 // grid: (ceil(n_new / run), B); block: groups of C/8 lanes, one run of rows per group.
@@ -152,6 +169,7 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
   const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
                                 : nullptr;
+  const RopeIn ri = rope_in(a, b, c0);
   if (a.window == 2 * a.stride && a.run > 1) {
     // Overlapping rows: entry i = block i + block i+1 (blocks of `stride` tokens).
     PoolState prev, cur, both;
@@ -161,7 +179,7 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
       pool_reset(cur);
       pool_block(cur, kv, lg, a.ld_tok, (i + 1) * a.stride, a.stride, c0);
       pool_merge(both, prev, cur);
-      finish_row(both, a, b, a.first_row + i, c0, li);
+      finish_row(both, a, ri, b, a.first_row + i, c0);
       prev = cur;
     }
   } else {
@@ -169,15 +187,15 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
       PoolState p;
       pool_reset(p);
       pool_block(p, kv, lg, a.ld_tok, i * a.stride, a.window, c0);
-      finish_row(p, a, b, a.first_row + i, c0, li);
+      finish_row(p, a, ri, b, a.first_row + i, c0);
     }
   }
 }
 
-// Long windows (HCA: 128 tokens per row): one block per (row, 128-channel slice).  The
-// window's tokens are dealt round-robin to 16 groups of 16 lanes (8 channels per lane), so
-// all of a row's loads are in flight at once instead of walking the window serially; the
-// 16 partial softmax states are merged through LDS.  Requires C % 128 == 0 and fp8 scale
+// Long windows (HCA: 128 tokens per row) and decode-sized calls: one block per (row,
+// 128-channel slice).  The window's tokens are dealt round-robin to 16 groups of 16 lanes
+// (8 channels per lane), so all of a row's loads are in flight at once instead of walking
+// the window serially; the 16 partial softmax states are merged through LDS.  Requires C % 128 == 0 and fp8 scale
 // blocks of at most 128 channels (one block never spans two slices).
 constexpr int kSplitGroups = 16;
 constexpr int kSliceC = 128;
@@ -191,6 +209,7 @@ __global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
   const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
                                 : nullptr;
+  const RopeIn ri = rope_in(a, b, c0);
   PoolState p;
   pool_reset(p);
   const int t0 = i * a.stride;
@@ -245,12 +264,15 @@ __global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
     q.s[k] = ss;
     q.sv[k] = sv;
   }
-  finish_row(q, a, b, a.first_row + i, c0, li);
+  finish_row(q, a, ri, b, a.first_row + i, c0);
 }
 
 hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   CompressArgs a = a0;
-  if (a.window >= 2 * kSplitGroups && a.C % kSliceC == 0 && (a.dtype == CSA_BF16 || a.scale_block <= kSliceC)) {
+  // long windows, or few rows (a decode step): every token of a row loads in parallel
+  const long long rows = (long long)a.n_new * a.B;
+  const bool split_ok = a.C % kSliceC == 0 && (a.dtype == CSA_BF16 || a.scale_block <= kSliceC);
+  if (split_ok && (a.window >= 2 * kSplitGroups || (a.window >= 4 && rows <= 512))) {
     if (a.n_new == 0 || a.B == 0) return hipSuccess;
     dim3 grid(a.n_new, a.B, a.C / kSliceC);
     hipLaunchKernelGGL(k_compress_split, grid, dim3(256), 0, s, a);

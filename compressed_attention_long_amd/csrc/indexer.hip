@@ -423,35 +423,20 @@ __device__ __forceinline__ int ordered_ranks(const bool (&f)[NPT], int (&rank)[N
   return tot;
 }
 
+// The selection shared by the one-block and the two-stage top-k.  Thread t holds entries
+// j = i * 1024 + t (i < NPT) of a key array in key[i]; key 0 marks "no entry" (real keys of
+// finite scores are never 0).  Selects the min(k, nvalid) entries with the largest keys,
+// the smaller j winning a tie, and numbers them in ascending j: f[i] says whether entry
+// (i, t) is selected and pos[i] its number.  Returns the number selected.
 template <int NPT>
-__global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
-  __shared__ TopkShared sh;
-  __shared__ OrderShared<NPT> osh;
-  const int row = blockIdx.x;
-  const int b = row / a.Tq;
+__device__ __forceinline__ int select_keys(TopkShared& sh, OrderShared<NPT>& osh, const uint32_t (&key)[NPT],
+                                           int nvalid, int k, bool (&f)[NPT], int (&pos)[NPT]) {
   const int tid = threadIdx.x;
-  const int k = a.topk;
-  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
-  const float* s = a.scores + (int64_t)row * a.cap;
-  int32_t* out = a.idx_out + (int64_t)row * k;
-
-  // Coalesced, unconditional loads (index clamped into the row; entries at or past nvis
-  // are masked by `ok(i)` below).
-  uint32_t key[NPT];
-  {
-    const int last = max(nvis - 1, 0);
-    float v[NPT];
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) v[i] = s[min(i * kTopkThreads + tid, last)];
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) key[i] = okey(v[i]);
-  }
   auto jof = [&](int i) { return i * kTopkThreads + tid; };
-  auto ok = [&](int i) { return jof(i) < nvis; };
-
+  auto ok = [&](int i) { return key[i] != 0u; };
   uint32_t TK = 0xffffffffu;
   int I = -1;
-  const bool take_all = nvis <= k;
+  const bool take_all = nvalid <= k;
   if (!take_all) {
     if (tid == 0) { sh.bstar = 0; sh.above = 0; sh.TK = 0xffffffffu; sh.I = -1; }
     uint32_t klo = 0xffffffffu, khi = 0u;
@@ -496,14 +481,14 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
     if (klo == khi) {
       // all candidates share one key: the need-th smallest index among them
       TK = klo;
-      bool f[NPT];
+      bool g[NPT];
       int rk[NPT];
 #pragma unroll
-      for (int i = 0; i < NPT; ++i) f[i] = ok(i) && key[i] == klo;
-      ordered_ranks<NPT>(f, rk, osh.cnt, sh.wsum);
+      for (int i = 0; i < NPT; ++i) g[i] = ok(i) && key[i] == klo;
+      ordered_ranks<NPT>(g, rk, osh.cnt, sh.wsum);
 #pragma unroll
       for (int i = 0; i < NPT; ++i)
-        if (f[i] && rk[i] == need - 1) sh.I = jof(i);
+        if (g[i] && rk[i] == need - 1) sh.I = jof(i);
       __syncthreads();
       I = sh.I;
     } else {
@@ -533,25 +518,263 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
     }
   }
   // ascending compaction: selected entries numbered in index order
-  bool f[NPT];
-  int pos[NPT];
 #pragma unroll
   for (int i = 0; i < NPT; ++i)
     f[i] = ok(i) && (take_all || key[i] > TK || (key[i] == TK && jof(i) <= I));
-  const int tot = ordered_ranks<NPT>(f, pos, osh.cnt, sh.wsum);
-#pragma unroll
-  for (int i = 0; i < NPT; ++i)
-    if (f[i] && pos[i] < k) out[pos[i]] = jof(i);
-  for (int p2 = min(tot, k) + tid; p2 < k; p2 += kTopkThreads) out[p2] = -1;
+  return ordered_ranks<NPT>(f, pos, osh.cnt, sh.wsum);
 }
 
-hipError_t launch_topk(const IndexArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.Tq), block(kTopkThreads);
-  if (a.cap <= 16 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<16>, grid, block, 0, s, a);
-  else if (a.cap <= 32 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<32>, grid, block, 0, s, a);
-  else if (a.cap <= 48 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<48>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(k_topk, grid, block, 0, s, a);
-  return hipGetLastError();
+// Scores of entries j < n starting at s, read once with coalesced loads (index clamped into
+// the range; entries past n get key 0).
+template <int NPT>
+__device__ __forceinline__ void load_score_keys(const float* s, int n, uint32_t (&key)[NPT]) {
+  const int last = max(n - 1, 0);
+  float v[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) v[i] = s[min(i * kTopkThreads + (int)threadIdx.x, last)];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) key[i] = i * kTopkThreads + (int)threadIdx.x < n ? okey(v[i]) : 0u;
+}
+
+// One block per query row holding the whole row in registers (rows of <= NPT * 1024 entries).
+template <int NPT>
+__global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
+  __shared__ TopkShared sh;
+  __shared__ OrderShared<NPT> osh;
+  const int row = blockIdx.x;
+  const int b = row / a.Tq;
+  const int k = a.topk;
+  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
+  int32_t* out = a.idx_out + (int64_t)row * k;
+  uint32_t key[NPT];
+  load_score_keys<NPT>(a.scores + (int64_t)row * a.cap, nvis, key);
+  bool f[NPT];
+  int pos[NPT];
+  const int tot = select_keys<NPT>(sh, osh, key, nvis, k, f, pos);
+#pragma unroll
+  for (int i = 0; i < NPT; ++i)
+    if (f[i] && pos[i] < k) out[pos[i]] = i * kTopkThreads + (int)threadIdx.x;
+  for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) out[p2] = -1;
+}
+
+// Two-stage top-k for long rows.  Stage 1: block (row, p) selects the top k of entries
+// [p * chunk, (p + 1) * chunk) of the row and writes them (key, row index) in ascending index
+// order to candidate slots [p * k, (p + 1) * k), padded with key 0 / index -1, and its count.
+// Every entry of the row's top k is in the top k of its own chunk (same order restricted to
+// the chunk), so the union of the chunks' selections holds the answer.
+template <int NPT>
+__global__ void __launch_bounds__(kTopkThreads) k_topk_chunk(IndexArgs a) {
+  __shared__ TopkShared sh;
+  __shared__ OrderShared<NPT> osh;
+  const int row = blockIdx.x, pch = blockIdx.y, P = gridDim.y;
+  const int b = row / a.Tq;
+  const int k = a.topk;
+  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
+  const int base = pch * a.chunk;
+  const int n = min(max(nvis - base, 0), a.chunk);
+  uint32_t key[NPT];
+  load_score_keys<NPT>(a.scores + (int64_t)row * a.cap + base, n, key);
+  bool f[NPT];
+  int pos[NPT];
+  const int tot = select_keys<NPT>(sh, osh, key, n, k, f, pos);
+  const int64_t slot0 = ((int64_t)row * P + pch) * k;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i)
+    if (f[i] && pos[i] < k) {
+      a.cand_key[slot0 + pos[i]] = key[i];
+      a.cand_idx[slot0 + pos[i]] = base + i * kTopkThreads + (int)threadIdx.x;
+    }
+  for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) {
+    a.cand_key[slot0 + p2] = 0u;
+    a.cand_idx[slot0 + p2] = -1;
+  }
+  if (threadIdx.x == 0) a.cand_count[(int64_t)row * P + pch] = min(tot, k);
+}
+
+// Later stages: block (row, q) takes candidate chunks [q * group, (q + 1) * group) of the
+// previous stage (chunk c of a row holds its top k in slots [c * k, (c + 1) * k), in
+// ascending row index, padded with key 0) and selects their top k, either as one chunk of
+// the next stage (same layout) or, in the last stage (one block per row), as the output.
+// Slot order is row-index order among real entries, so ties by slot are ties by row index.
+template <int NPT, bool FINAL>
+__global__ void __launch_bounds__(kTopkThreads) k_topk_merge(IndexArgs a, const uint32_t* in_key,
+                                                             const int32_t* in_idx, const int* in_count,
+                                                             int in_chunks, int group, uint32_t* out_key,
+                                                             int32_t* out_idx, int* out_count) {
+  __shared__ TopkShared sh;
+  __shared__ OrderShared<NPT> osh;
+  const int row = blockIdx.x, q = blockIdx.y, out_chunks = gridDim.y;
+  const int k = a.topk;
+  const int c0 = q * group, c1 = min(in_chunks, c0 + group);
+  const int n = (c1 - c0) * k;
+  int nvalid = 0;
+  for (int c = c0; c < c1; ++c) nvalid += in_count[(int64_t)row * in_chunks + c];
+  const int64_t base = ((int64_t)row * in_chunks + c0) * k;
+  uint32_t key[NPT];
+  {
+    const int last = max(n - 1, 0);
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int j = i * kTopkThreads + (int)threadIdx.x;
+      const uint32_t v = in_key[base + min(j, last)];
+      key[i] = j < n ? v : 0u;
+    }
+  }
+  bool f[NPT];
+  int pos[NPT];
+  const int tot = select_keys<NPT>(sh, osh, key, nvalid, k, f, pos);
+  if (FINAL) {
+    int32_t* out = a.idx_out + (int64_t)row * k;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (f[i] && pos[i] < k) out[pos[i]] = in_idx[base + i * kTopkThreads + (int)threadIdx.x];
+    for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) out[p2] = -1;
+  } else {
+    const int64_t ob = ((int64_t)row * out_chunks + q) * k;
+#pragma unroll
+    for (int i = 0; i < NPT; ++i)
+      if (f[i] && pos[i] < k) {
+        out_key[ob + pos[i]] = key[i];
+        out_idx[ob + pos[i]] = in_idx[base + i * kTopkThreads + (int)threadIdx.x];
+      }
+    for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) {
+      out_key[ob + p2] = 0u;
+      out_idx[ob + p2] = -1;
+    }
+    if (threadIdx.x == 0) out_count[(int64_t)row * out_chunks + q] = min(tot, k);
+  }
+}
+
+// Plan of the top-k for rows of up to `cap` entries.  Rows that fit one register-resident
+// block take one block per row.  Longer rows go through stage 1 (chunks of npt1 * 1024
+// entries, `nchunk` per row) and merge stages that each reduce `group` chunks of k
+// candidates (about 8192 candidates per block) to one, until one block per row finishes.
+#ifndef CSA_TOPK_SINGLE_MAX
+#define CSA_TOPK_SINGLE_MAX 16384   // rows up to this length always take one block
+#endif
+constexpr int kMergeCands = 8192;   // candidates per merge block
+static int npt_for(int n) {
+  const int m = (n + kTopkThreads - 1) / kTopkThreads;
+  return m <= 4 ? 4 : (m <= 8 ? 8 : (m <= 16 ? 16 : (m <= 32 ? 32 : 48)));
+}
+TopkPlan topk_plan(int rows, int cap, int k) {
+  TopkPlan pl{};
+  const int per = kTopkThreads;
+  if (cap <= CSA_TOPK_SINGLE_MAX || (cap <= 48 * per && rows >= 128) || k > 48 * per / 2) {
+    pl.mode = cap <= 48 * per ? 0 : 2;
+    return pl;
+  }
+  pl.mode = 1;
+  pl.npt1 = 8;
+  pl.chunk = pl.npt1 * per;
+  pl.nchunk = (cap + pl.chunk - 1) / pl.chunk;
+  pl.group = max(2, kMergeCands / k);
+  if ((long long)rows * pl.nchunk > 65535LL * 1024) pl.mode = 2;
+  return pl;
+}
+
+size_t topk_workspace(int rows, int cap, int k) {
+  const TopkPlan pl = topk_plan(rows, cap, k);
+  if (pl.mode != 1) return 0;
+  // two candidate areas (stage outputs alternate between them): the first holds the stage-1
+  // chunks, the second the first merge stage's
+  const size_t per_chunk = (size_t)k * (sizeof(uint32_t) + sizeof(int32_t)) + sizeof(int);
+  const size_t c2 = (pl.nchunk + pl.group - 1) / pl.group;
+  const size_t bytes = (size_t)rows * (pl.nchunk + c2) * per_chunk + 4 * 256;
+  return (bytes + 255) / 256 * 256;
+}
+
+#define CSA_TOPK_MERGE(NPT, FINAL)                                                                      \
+  hipLaunchKernelGGL((k_topk_merge<NPT, FINAL>), grid, block, 0, s, a, in_key, in_idx, in_count, chunks, \
+                     group, out_key, out_idx, out_count)
+
+static void launch_merge(int npt, bool final_stage, dim3 grid, dim3 block, hipStream_t s, const IndexArgs& a,
+                         const uint32_t* in_key, const int32_t* in_idx, const int* in_count, int chunks,
+                         int group, uint32_t* out_key, int32_t* out_idx, int* out_count) {
+  if (final_stage) {
+    switch (npt) {
+      case 4: CSA_TOPK_MERGE(4, true); break;
+      case 8: CSA_TOPK_MERGE(8, true); break;
+      case 16: CSA_TOPK_MERGE(16, true); break;
+      case 32: CSA_TOPK_MERGE(32, true); break;
+      default: CSA_TOPK_MERGE(48, true); break;
+    }
+  } else {
+    switch (npt) {
+      case 4: CSA_TOPK_MERGE(4, false); break;
+      case 8: CSA_TOPK_MERGE(8, false); break;
+      case 16: CSA_TOPK_MERGE(16, false); break;
+      case 32: CSA_TOPK_MERGE(32, false); break;
+      default: CSA_TOPK_MERGE(48, false); break;
+    }
+  }
+}
+#undef CSA_TOPK_MERGE
+
+hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
+  IndexArgs a = a0;
+  const int rows = a.B * a.Tq;
+  const int k = a.topk;
+  const TopkPlan pl = topk_plan(rows, a.cap, k);
+  const dim3 block(kTopkThreads);
+  if (pl.mode == 0) {
+    const dim3 grid(rows);
+    if (a.cap <= 4 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<4>, grid, block, 0, s, a);
+    else if (a.cap <= 16 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<16>, grid, block, 0, s, a);
+    else if (a.cap <= 32 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<32>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k_topk_reg<48>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
+  if (pl.mode == 2) {
+    hipLaunchKernelGGL(k_topk, dim3(rows), block, 0, s, a);
+    return hipGetLastError();
+  }
+  // candidate areas A (stage-1 chunks) and B (first merge stage), each [keys | indices | counts]
+  const size_t nA = (size_t)rows * pl.nchunk * k;
+  const int c2 = (pl.nchunk + pl.group - 1) / pl.group;
+  const size_t nB = (size_t)rows * c2 * k;
+  auto align = [](uint8_t* p) { return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255)); };
+  uint8_t* w = align(reinterpret_cast<uint8_t*>(a.cand_key));
+  uint32_t* keyA = reinterpret_cast<uint32_t*>(w);
+  int32_t* idxA = reinterpret_cast<int32_t*>(keyA + nA);
+  int* cntA = reinterpret_cast<int*>(idxA + nA);
+  w = align(reinterpret_cast<uint8_t*>(cntA + (size_t)rows * pl.nchunk));
+  uint32_t* keyB = reinterpret_cast<uint32_t*>(w);
+  int32_t* idxB = reinterpret_cast<int32_t*>(keyB + nB);
+  int* cntB = reinterpret_cast<int*>(idxB + nB);
+  a.cand_key = keyA;
+  a.cand_idx = idxA;
+  a.cand_count = cntA;
+  a.chunk = pl.chunk;
+  a.nchunk = pl.nchunk;
+  hipLaunchKernelGGL(k_topk_chunk<8>, dim3(rows, pl.nchunk), block, 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t* in_key = keyA;
+  const int32_t* in_idx = idxA;
+  const int* in_count = cntA;
+  int chunks = pl.nchunk;
+  bool in_A = true;
+  for (;;) {
+    if ((long long)chunks * k <= kMergeCands || chunks <= pl.group) {
+      launch_merge(npt_for(chunks * k), true, dim3(rows, 1), block, s, a, in_key, in_idx, in_count, chunks,
+                   chunks, nullptr, nullptr, nullptr);
+      return hipGetLastError();
+    }
+    const int out_chunks = (chunks + pl.group - 1) / pl.group;
+    uint32_t* ok_ = in_A ? keyB : keyA;
+    int32_t* oi = in_A ? idxB : idxA;
+    int* oc = in_A ? cntB : cntA;
+    launch_merge(npt_for(pl.group * k), false, dim3(rows, out_chunks), block, s, a, in_key, in_idx, in_count,
+                 chunks, pl.group, ok_, oi, oc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    in_key = ok_;
+    in_idx = oi;
+    in_count = oc;
+    chunks = out_chunks;
+    in_A = !in_A;
+  }
 }
 
 }  // namespace csa

@@ -34,7 +34,19 @@ struct IndexArgs {
   int topk;
   float* scores;          // [rows, cap]
   int32_t* idx_out;       // [rows, topk]
+  // chunked top-k (long rows): stage-1 candidates [rows, nchunk, topk] and counts [rows, nchunk];
+  // the launcher carves its candidate areas from cand_key (the workspace part it points to)
+  uint32_t* cand_key;
+  int32_t* cand_idx;
+  int* cand_count;
+  int chunk, nchunk;      // set by the launcher
 };
+struct TopkPlan {
+  int mode;               // 0: one block per row; 1: chunked stages; 2: streaming
+  int chunk, npt1, nchunk, group;
+};
+TopkPlan topk_plan(int rows, int cap, int k);
+size_t topk_workspace(int rows, int cap, int k);   // candidate area of the two-stage plan
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
 hipError_t launch_topk(const IndexArgs& a, hipStream_t s);
 

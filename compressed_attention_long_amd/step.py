@@ -51,6 +51,7 @@ class LayerStep:
                                   wl.stride, scales=ks, scale_block=wl.Di if ks is not None else 0)
             self.idx = torch.empty((B, wl.Tq, wl.topk), dtype=torch.int32, device=dev)
             self.scores = torch.empty((B, wl.Tq, wl.E), dtype=torch.float32, device=dev)
+            self.idx_ws = ops.workspace(ops.index_topk_workspace_bytes(B, wl.Tq, wl.Hi, wl.E, wl.topk), dev)
             ws = ops.csa_attend_workspace_bytes(B, wl.Tq, wl.H, wl.topk, wl.W)
         else:
             self.keys = None
@@ -74,7 +75,7 @@ class LayerStep:
     def index(self, stream=None):
         wl = self.wl
         ops.index_topk(self.t["q_idx"], self.t["w"], self.t["q_pos"], self.keys, wl.topk, self.idx,
-                       scores_out=self.scores, stream=stream)
+                       scores_out=self.scores, workspace=self.idx_ws, stream=stream)
 
     def attend(self, stream=None):
         wl = self.wl

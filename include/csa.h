@@ -147,7 +147,10 @@ int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_
  *   topk       1 .. keys->cap, at most 4096
  *   idx_out    device int32 [B, Tq, topk]
  *   scores_out device fp32 [B, Tq, keys->cap] or NULL; invisible entries hold -inf.
- *   workspace  at least csa_index_topk_workspace_bytes(...) bytes, 256-byte aligned.
+ *   workspace  at least csa_index_topk_workspace_bytes(...) bytes, 256-byte aligned:
+ *              the scores when scores_out is NULL, and for rows longer than 16384
+ *              entries the candidate lists of a two-stage selection (the top k of
+ *              each chunk of the row, then the top k of those).
  * Requires Hi % 16 == 0 (Hi <= 64), 16-byte aligned q_idx and key rows.
  */
 int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos,

@@ -83,6 +83,13 @@ def test_index_topk_validation():
     assert index(k, ws=FAKE + 16, wsb=need)[0] == L.CSA_EINVAL     # misaligned workspace
     assert index(k, q=None)[0] == L.CSA_EINVAL
     assert index(k, B=0)[0] == L.CSA_OK
+    # rows longer than 16384 entries select in two stages, whose candidates need a workspace
+    # even when the scores go to scores_out
+    long_keys = cache(C=128, cap=100000)
+    assert index(long_keys, topk=1024, scores=FAKE)[0] == L.CSA_EWORKSPACE
+    # (a row that fits one block passes validation; without a GPU the launch itself then fails)
+    assert index(cache(C=128, cap=16384), topk=1024, scores=FAKE)[0] not in (L.CSA_EWORKSPACE, L.CSA_EINVAL,
+                                                                              L.CSA_ENOTSUP)
 
 
 def attend(kv, win, topk=16, H=128, W=128, ws=None, wsb=0, out_dtype=L.CSA_FP32, rope=64, hca=False, B=32):
@@ -117,3 +124,4 @@ def test_workspace_sizes_scale_with_work():
     b = L.hca_attend_workspace_bytes(16, 1, 128, 4096, 128)
     assert a > 0 and b > 0
     assert L.index_topk_workspace_bytes(32, 1, 64, 16383, 1024) >= 32 * 16383 * 4
+    assert L.index_topk_workspace_bytes(4, 1, 64, 262143, 1024) >= 4 * 262143 * 4 + 4 * 32 * 1024 * 8

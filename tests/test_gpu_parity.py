@@ -114,7 +114,8 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (3, 1, 64, 3010, [3000, 2500, 10], True, 1024, "end"),     # ragged caches, one row with < k visible
     (2, 5, 16, 700, [700, 650], False, 100, "causal"),         # prefill rows: causal visibility
     (1, 2, 48, 1500, [1500], True, 1, "end"),                  # k = 1, Hi not a multiple of 64
-    (2, 1, 64, 20000, [20000, 19999], True, 1024, "end"),      # spans many blocks
+    (2, 1, 64, 20000, [20000, 19999], True, 1024, "end"),      # spans many blocks; two-stage top-k
+    (2, 1, 64, 70000, [70000, 500], True, 1024, "end"),        # two-stage, 9 chunks; one row with < k visible
 ])
 def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
     d = ci.Draw(200 + cap, "cpu")
@@ -130,7 +131,8 @@ def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
     q_pos = torch.tensor(qp, dtype=torch.int64, device=DEV)
     idx = torch.empty((B, Tq, topk), dtype=torch.int32, device=DEV)
     scores = torch.empty((B, Tq, cap), dtype=torch.float32, device=DEV)
-    ops.index_topk(q_idx.to(DEV), w.to(DEV), q_pos, keys, topk, idx, scores_out=scores)
+    ws = ops.workspace(ops.index_topk_workspace_bytes(B, Tq, Hi, cap, topk), DEV)
+    ops.index_topk(q_idx.to(DEV), w.to(DEV), q_pos, keys, topk, idx, scores_out=scores, workspace=ws)
     torch.cuda.synchronize()
     sg, ig = scores.cpu().numpy(), idx.cpu().numpy()
     for b in range(B):
@@ -139,21 +141,23 @@ def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
             so = O.index_scores(np64(q_idx[b, t]), np64(w[b, t]), kref[b])
             check_scores(sg[b, t], so, vis, f"b={b} t={t}")
             check_topk(ig[b, t], sg[b, t], so, vis, topk, f"b={b} t={t}")
-    # workspace instead of scores_out gives the same selection
-    ws = ops.workspace(ops.index_topk_workspace_bytes(B, Tq, Hi, cap, topk), DEV)
+    # scores in the workspace instead of scores_out gives the same selection
     idx2 = torch.empty_like(idx)
     ops.index_topk(q_idx.to(DEV), w.to(DEV), q_pos, keys, topk, idx2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
 
 
-def test_topk_all_scores_tied():
-    # zero indexer queries: every visible score is 0, so the k smallest indices win
-    B, cap, topk = 2, 5000, 777
-    keys, _ = _keys_cache(B, cap, False, 11, [5000, 4000], [1, 1])
+@pytest.mark.parametrize("cap", [5000, 50000])
+def test_topk_all_scores_tied(cap):
+    # zero indexer queries: every visible score is 0, so the k smallest indices win (with
+    # cap 50000 the selection runs in two stages and the tie spans its chunks)
+    B, topk = 2, 777
+    nv = [cap, cap - 1000]
+    keys, _ = _keys_cache(B, cap, False, 11, nv, [1, 1])
     q_idx = torch.zeros((B, 1, 64, 128), dtype=torch.bfloat16, device=DEV)
     w = torch.ones((B, 1, 64), dtype=torch.float32, device=DEV)
-    q_pos = torch.tensor([[1 + 4 * 4999 + 7], [1 + 4 * 3999 + 7]], dtype=torch.int64, device=DEV)
+    q_pos = torch.tensor([[1 + 4 * (nv[0] - 1) + 7], [1 + 4 * (nv[1] - 1) + 7]], dtype=torch.int64, device=DEV)
     idx = torch.empty((B, 1, topk), dtype=torch.int32, device=DEV)
     ops.index_topk(q_idx, w, q_pos, keys, topk, idx, workspace=ops.workspace(
         ops.index_topk_workspace_bytes(B, 1, 64, cap, topk), DEV))
@@ -179,7 +183,8 @@ def test_topk_clustered_scores():
     q_pos = torch.tensor([[1 + 4 * (cap - 1) + 7]], dtype=torch.int64, device=DEV)
     idx = torch.empty((1, 1, topk), dtype=torch.int32, device=DEV)
     scores = torch.empty((1, 1, cap), dtype=torch.float32, device=DEV)
-    ops.index_topk(q_idx.to(DEV), w, q_pos, keys, topk, idx, scores_out=scores)
+    ops.index_topk(q_idx.to(DEV), w, q_pos, keys, topk, idx, scores_out=scores,
+                   workspace=ops.workspace(ops.index_topk_workspace_bytes(1, 1, 1, cap, topk), DEV))
     torch.cuda.synchronize()
     sg = scores[0, 0].cpu().numpy()
     ref = 1.0 + np64(kt[0, :, 1])
