@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
       u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * c);
       r[4 * c] = v[0]; r[4 * c + 1] = v[1]; r[4 * c + 2] = v[2]; r[4 * c + 3] = v[3];
     }
-    if (FP8) r[KW] = __float_as_uint(sbase[j]);
+    if constexpr (FP8) r[KW] = __float_as_uint(sbase[j]);
   };
 
   // kDepth tiles in flight per wave: the loads of tile t + kDepth are issued as tile t is
@@ -198,8 +198,8 @@ constexpr int kCandMax = 512;
 
 struct TopkShared {
   int hist[kTopkBins];
-  uint32_t ckey[kCandMax];
-  int cidx[kCandMax];
+  alignas(16) uint32_t ckey[kCandMax + 4];   // + 4: padding for 16-byte reads of the tail
+  alignas(16) int cidx[kCandMax + 4];
   int wsum[kTopkThreads / 64];
   uint32_t wmin[kTopkThreads / 64], wmax[kTopkThreads / 64];
   int ccount;
@@ -390,125 +390,216 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
 // smallest index among tied keys) number the selected entries in index order with wave
 // ballots plus one scan over the per-(i, wave) counts.  Used when the row has at most
 // NPT * 1024 entries.
-template <int NPT>
-struct OrderShared {
-  int cnt[NPT * (kTopkThreads / 64)];
-};
-
-// For per-thread flags f[i] (entry j = i * 1024 + tid), the rank of each flagged entry among
-// all flagged entries in index order; returns the total.  Two barriers.
-template <int NPT>
-__device__ __forceinline__ int ordered_ranks(const bool (&f)[NPT], int (&rank)[NPT], int* cnt, int* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int NW = kTopkThreads / 64;
-  uint64_t m[NPT];
+// ---- wave-wide reductions without LDS: DPP within rows of 16 lanes (quad swaps, half-row
+// and row mirrors), then the gfx950 lane-swap permutes across rows and wave halves.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xf, 0xf, false);
+}
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+  auto op = [](uint32_t p, uint32_t q) { return MAX ? max(p, q) : min(p, q); };
+  x = op(x, dpp_u32<0xB1>(x));    // quad_perm [1,0,3,2]
+  x = op(x, dpp_u32<0x4E>(x));    // quad_perm [2,3,0,1]
+  x = op(x, dpp_u32<0x141>(x));   // row_half_mirror
+  x = op(x, dpp_u32<0x140>(x));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op(b[0], b[1]);
+}
+// inclusive prefix sum across the 64 lanes
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    m[i] = __ballot(f[i]);
-    if (lane == 0) cnt[i * NW + wave] = __popcll(m[i]);
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
   }
-  __syncthreads();
-  // exclusive scan of cnt[] (index order = (i, wave) lexicographic) by the first NPT*NW threads
-  const int t = threadIdx.x;
-  const int v = t < NPT * NW ? cnt[t] : 0;
-  int tot;
-  const int pre = block_excl_scan(v, wsum, tot);
-  if (t < NPT * NW) cnt[t] = pre;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) {
-    const uint32_t lo = (uint32_t)m[i], hi = (uint32_t)(m[i] >> 32);
-    rank[i] = cnt[i * NW + wave] + (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
-  }
-  return tot;
+  return x;
 }
 
-// The selection shared by the one-block and the two-stage top-k.  Thread t holds entries
-// j = i * 1024 + t (i < NPT) of a key array in key[i]; key 0 marks "no entry" (real keys of
-// finite scores are never 0).  Selects the min(k, nvalid) entries with the largest keys,
-// the smaller j winning a tie, and numbers them in ascending j: f[i] says whether entry
-// (i, t) is selected and pos[i] its number.  Returns the number selected.
-template <int NPT>
-__device__ __forceinline__ int select_keys(TopkShared& sh, OrderShared<NPT>& osh, const uint32_t (&key)[NPT],
-                                           int nvalid, int k, bool (&f)[NPT], int (&pos)[NPT]) {
-  const int tid = threadIdx.x;
-  auto jof = [&](int i) { return i * kTopkThreads + tid; };
+// Shared state of one selection by a block of T lanes holding NPT keys each.  The histogram
+// has one padding word per 32 bins so that wave 0 can read 32 consecutive bins per lane
+// without bank conflicts.
+template <int T, int NPT>
+struct SelShared {
+  static constexpr int W = T / 64;
+  uint32_t hist[kTopkBins + kTopkBins / 32];
+  alignas(16) uint32_t ckey[kCandMax + 4];   // + 4: padding for 16-byte reads of the tail
+  alignas(16) int cidx[kCandMax + 4];
+  int cnt[NPT * W];
+  uint32_t red[2 * W];
+  int ccount, bstar, above, bcnt, total;
+  uint32_t TK;
+  int I;
+};
+__device__ __forceinline__ int hslot(int b) { return b + (b >> 5); }
+
+// Number the flagged entries (i, t) -- entry j = i * T + t, flag = bit i of `bits` -- in
+// ascending j: per-(i, wave) counts, one in-order exclusive scan of them by wave 0, then each
+// lane's offset within its wave; emit(i, number) for every flagged entry.  Two barriers.
+// Returns the total.  (Flags live as bits of one 64-bit value per lane: an array of bools
+// would occupy a 64-bit lane mask per element.)
+template <int T, int NPT, class Emit>
+__device__ __forceinline__ int sel_ranks(SelShared<T, NPT>& sh, uint64_t bits, Emit&& emit) {
+  constexpr int W = T / 64, N = NPT * W, PER = (N + 63) / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const uint64_t m = __ballot((bits >> i) & 1);
+    if (lane == 0) sh.cnt[i * W + wave] = __popcll(m);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int v[PER], sum = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = lane * PER + e;
+      v[e] = idx < N ? sh.cnt[idx] : 0;
+      sum += v[e];
+    }
+    const int incl = wave_incl_scan(sum);
+    int run = incl - sum;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int idx = lane * PER + e;
+      if (idx < N) sh.cnt[idx] = run;
+      run += v[e];
+    }
+    if (lane == 63) sh.total = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) {
+    const bool on = (bits >> i) & 1;
+    const uint64_t m = __ballot(on);
+    if (on)
+      emit(i, sh.cnt[i * W + wave] +
+                  (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)));
+  }
+  return sh.total;
+}
+
+// The selection shared by all top-k kernels.  Lane t of the block holds entries
+// j = i * T + t (i < NPT) of a key array in key[i]; key 0 marks "no entry" (keys of finite
+// scores are never 0).  Selects the min(k, nvalid) entries with the largest keys, the
+// smaller j winning a tie, numbers them in ascending j and calls emit(i, number) for each.
+// Returns the number selected.
+//
+// Keys are counted in 2048 equal-width bins over the current key range [klo, khi]; the bin
+// holding the k-th largest key becomes the next range.  Widths shrink from < 2^32 to
+// < 2^21, < 2^10 and 1, so after at most three rounds the range is a single key; the
+// rounds stop early once the bin holds <= kCandMax keys, which are then ranked exactly.
+template <int T, int NPT, class Emit>
+__device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t (&key)[NPT], int nvalid,
+                                           int k, Emit&& emit) {
+  constexpr int W = T / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto jof = [&](int i) { return i * T + tid; };
   auto ok = [&](int i) { return key[i] != 0u; };
   uint32_t TK = 0xffffffffu;
   int I = -1;
   const bool take_all = nvalid <= k;
   if (!take_all) {
-    if (tid == 0) { sh.bstar = 0; sh.above = 0; sh.TK = 0xffffffffu; sh.I = -1; }
     uint32_t klo = 0xffffffffu, khi = 0u;
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
       if (ok(i)) { klo = min(klo, key[i]); khi = max(khi, key[i]); }
-    block_minmax(klo, khi, sh);
-    int above = 0;
-    for (int iter = 0; iter < 4 && klo < khi; ++iter) {
-      for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0;
-      __syncthreads();
+    klo = wave_reduce_u32<false>(klo);
+    khi = wave_reduce_u32<true>(khi);
+    if (lane == 0) { sh.red[wave] = klo; sh.red[W + wave] = khi; }
+    for (int b = tid; b < kTopkBins + kTopkBins / 32; b += T) sh.hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int w2 = 0; w2 < W; ++w2) { klo = min(klo, sh.red[w2]); khi = max(khi, sh.red[W + w2]); }
+    int above = 0, cnt = 0;
+    for (int round = 0; round < 3 && klo < khi; ++round) {
       const uint32_t range = khi - klo;
       const int shift = max(0, 32 - __clz((int)range) - 11);
 #pragma unroll
       for (int i = 0; i < NPT; ++i)
-        if (ok(i) && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[(key[i] - klo) >> shift], 1);
+        if (ok(i) && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[hslot((key[i] - klo) >> shift)], 1u);
       __syncthreads();
-      const int u = kTopkThreads - 1 - tid;
-      const int hA = sh.hist[2 * u + 1], hB = sh.hist[2 * u];
-      int tot;
-      const int pre = block_excl_scan(hA + hB, sh.wsum, tot);
-      const int need = k - above;
-      if (pre < need && pre + hA >= need) { sh.bstar = 2 * u + 1; sh.above = pre; }
-      else if (pre + hA < need && pre + hA + hB >= need) { sh.bstar = 2 * u; sh.above = pre + hA; }
-      __syncthreads();
-      const int bstar = min(max(sh.bstar, 0), kTopkBins - 1);
-      const int cnt = sh.hist[bstar];
-      above += sh.above;
-      uint32_t nlo = 0xffffffffu, nhi = 0u;
+      if (wave == 0) {
+        // lane l owns bins 2047 - 32l - e (e < 32): the bins in descending key order
+        int c[32], sum = 0;
 #pragma unroll
-      for (int i = 0; i < NPT; ++i)
-        if (ok(i) && key[i] >= klo && key[i] <= khi && (int)((key[i] - klo) >> shift) == bstar) {
-          nlo = min(nlo, key[i]);
-          nhi = max(nhi, key[i]);
+        for (int e = 0; e < 32; ++e) {
+          c[e] = (int)sh.hist[hslot(kTopkBins - 1 - (32 * lane + e))];
+          sum += c[e];
         }
-      block_minmax(nlo, nhi, sh);
+        const int incl = wave_incl_scan(sum);
+        const int pre = incl - sum;
+        const int need = k - above;
+        if (pre < need && need <= incl) {
+          int run = pre;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) {
+            if (run < need && run + c[e] >= need) {
+              sh.bstar = kTopkBins - 1 - (32 * lane + e);
+              sh.above = run;
+              sh.bcnt = c[e];
+            }
+            run += c[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e) sh.hist[hslot(32 * lane + e)] = 0;   // clear for the next round
+      }
+      __syncthreads();
+      const int bstar = sh.bstar;
+      above += sh.above;
+      cnt = sh.bcnt;
+      const uint32_t nlo = klo + ((uint32_t)bstar << shift);
+      khi = min(khi, nlo + ((1u << shift) - 1u));
       klo = nlo;
-      khi = nhi;
       if (cnt <= kCandMax) break;
     }
     const int need = k - above;
     if (klo == khi) {
-      // all candidates share one key: the need-th smallest index among them
+      // one key value left: the need-th smallest index among the entries holding it
       TK = klo;
-      bool g[NPT];
-      int rk[NPT];
+      uint64_t g = 0;
 #pragma unroll
-      for (int i = 0; i < NPT; ++i) g[i] = ok(i) && key[i] == klo;
-      ordered_ranks<NPT>(g, rk, osh.cnt, sh.wsum);
-#pragma unroll
-      for (int i = 0; i < NPT; ++i)
-        if (g[i] && rk[i] == need - 1) sh.I = jof(i);
+      for (int i = 0; i < NPT; ++i) g |= (uint64_t)(ok(i) && key[i] == klo) << i;
+      sel_ranks<T, NPT>(sh, g, [&](int i, int r) {
+        if (r == need - 1) sh.I = jof(i);
+      });
       __syncthreads();
       I = sh.I;
     } else {
+      // at most kCandMax keys in [klo, khi]: collect them (one slot reservation per wave and
+      // index i), then rank each among all by (key desc, index asc)
       if (tid == 0) sh.ccount = 0;
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < NPT; ++i)
-        if (ok(i) && key[i] >= klo && key[i] <= khi) {
-          const int slot = atomicAdd(&sh.ccount, 1);
-          if (slot < kCandMax) { sh.ckey[slot] = key[i]; sh.cidx[slot] = jof(i); }
-        }
+      for (int i = 0; i < NPT; ++i) {
+        const bool c = ok(i) && key[i] >= klo && key[i] <= khi;
+        const uint64_t m = __ballot(c);
+        if (m == 0) continue;
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sh.ccount, __popcll(m));
+        base = __shfl(base, 0, kWave);
+        const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (c && slot < kCandMax) { sh.ckey[slot] = key[i]; sh.cidx[slot] = jof(i); }
+      }
       __syncthreads();
       const int c = min(sh.ccount, kCandMax);
-      for (int ci = tid; ci < c; ci += kTopkThreads) {
+      if (tid < 4) { sh.ckey[c + tid] = 0u; sh.cidx[c + tid] = 0x7fffffff; }
+      __syncthreads();
+      const int c4 = (c + 3) >> 2;
+      for (int ci = tid; ci < c; ci += T) {
         const uint32_t v = sh.ckey[ci];
         const int ji = sh.cidx[ci];
         int rank = 0;
-        for (int o = 0; o < c; ++o) {
-          const uint32_t vo = sh.ckey[o];
-          rank += (vo > v || (vo == v && sh.cidx[o] < ji)) ? 1 : 0;
+#pragma unroll 4
+        for (int o4 = 0; o4 < c4; ++o4) {
+          const u32x4 vo = *reinterpret_cast<const u32x4*>(&sh.ckey[4 * o4]);
+          const u32x4 jo = *reinterpret_cast<const u32x4*>(&sh.cidx[4 * o4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rank += (vo[e] > v || (vo[e] == v && (int)jo[e] < ji)) ? 1 : 0;
         }
         if (rank == need - 1) { sh.TK = v; sh.I = ji; }
       }
@@ -518,54 +609,50 @@ __device__ __forceinline__ int select_keys(TopkShared& sh, OrderShared<NPT>& osh
     }
   }
   // ascending compaction: selected entries numbered in index order
+  uint64_t f = 0;
 #pragma unroll
   for (int i = 0; i < NPT; ++i)
-    f[i] = ok(i) && (take_all || key[i] > TK || (key[i] == TK && jof(i) <= I));
-  return ordered_ranks<NPT>(f, pos, osh.cnt, sh.wsum);
+    f |= (uint64_t)(ok(i) && (take_all || key[i] > TK || (key[i] == TK && jof(i) <= I))) << i;
+  return sel_ranks<T, NPT>(sh, f, emit);
 }
 
 // Scores of entries j < n starting at s, read once with coalesced loads (index clamped into
 // the range; entries past n get key 0).
-template <int NPT>
+template <int T, int NPT>
 __device__ __forceinline__ void load_score_keys(const float* s, int n, uint32_t (&key)[NPT]) {
   const int last = max(n - 1, 0);
   float v[NPT];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) v[i] = s[min(i * kTopkThreads + (int)threadIdx.x, last)];
+  for (int i = 0; i < NPT; ++i) v[i] = s[min(i * T + (int)threadIdx.x, last)];
 #pragma unroll
-  for (int i = 0; i < NPT; ++i) key[i] = i * kTopkThreads + (int)threadIdx.x < n ? okey(v[i]) : 0u;
+  for (int i = 0; i < NPT; ++i) key[i] = i * T + (int)threadIdx.x < n ? okey(v[i]) : 0u;
 }
 
-// One block per query row holding the whole row in registers (rows of <= NPT * 1024 entries).
-template <int NPT>
-__global__ void __launch_bounds__(kTopkThreads) k_topk_reg(IndexArgs a) {
-  __shared__ TopkShared sh;
-  __shared__ OrderShared<NPT> osh;
+// One block per query row holding the whole row in registers (rows of <= T * NPT entries).
+template <int T, int NPT>
+__global__ void __launch_bounds__(T) k_topk_reg(IndexArgs a) {
+  __shared__ SelShared<T, NPT> sh;
   const int row = blockIdx.x;
   const int b = row / a.Tq;
   const int k = a.topk;
   const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   int32_t* out = a.idx_out + (int64_t)row * k;
   uint32_t key[NPT];
-  load_score_keys<NPT>(a.scores + (int64_t)row * a.cap, nvis, key);
-  bool f[NPT];
-  int pos[NPT];
-  const int tot = select_keys<NPT>(sh, osh, key, nvis, k, f, pos);
-#pragma unroll
-  for (int i = 0; i < NPT; ++i)
-    if (f[i] && pos[i] < k) out[pos[i]] = i * kTopkThreads + (int)threadIdx.x;
-  for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) out[p2] = -1;
+  load_score_keys<T, NPT>(a.scores + (int64_t)row * a.cap, nvis, key);
+  const int tot = select_keys<T, NPT>(sh, key, nvis, k, [&](int i, int pos) {
+    if (pos < k) out[pos] = i * T + (int)threadIdx.x;
+  });
+  for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += T) out[p2] = -1;
 }
 
-// Two-stage top-k for long rows.  Stage 1: block (row, p) selects the top k of entries
+// Chunked top-k for long rows.  Stage 1: block (row, p) selects the top k of entries
 // [p * chunk, (p + 1) * chunk) of the row and writes them (key, row index) in ascending index
 // order to candidate slots [p * k, (p + 1) * k), padded with key 0 / index -1, and its count.
 // Every entry of the row's top k is in the top k of its own chunk (same order restricted to
 // the chunk), so the union of the chunks' selections holds the answer.
-template <int NPT>
-__global__ void __launch_bounds__(kTopkThreads) k_topk_chunk(IndexArgs a) {
-  __shared__ TopkShared sh;
-  __shared__ OrderShared<NPT> osh;
+template <int T, int NPT>
+__global__ void __launch_bounds__(T) k_topk_chunk(IndexArgs a) {
+  __shared__ SelShared<T, NPT> sh;
   const int row = blockIdx.x, pch = blockIdx.y, P = gridDim.y;
   const int b = row / a.Tq;
   const int k = a.topk;
@@ -573,18 +660,15 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_chunk(IndexArgs a) {
   const int base = pch * a.chunk;
   const int n = min(max(nvis - base, 0), a.chunk);
   uint32_t key[NPT];
-  load_score_keys<NPT>(a.scores + (int64_t)row * a.cap + base, n, key);
-  bool f[NPT];
-  int pos[NPT];
-  const int tot = select_keys<NPT>(sh, osh, key, n, k, f, pos);
+  load_score_keys<T, NPT>(a.scores + (int64_t)row * a.cap + base, n, key);
   const int64_t slot0 = ((int64_t)row * P + pch) * k;
-#pragma unroll
-  for (int i = 0; i < NPT; ++i)
-    if (f[i] && pos[i] < k) {
-      a.cand_key[slot0 + pos[i]] = key[i];
-      a.cand_idx[slot0 + pos[i]] = base + i * kTopkThreads + (int)threadIdx.x;
+  const int tot = select_keys<T, NPT>(sh, key, n, k, [&](int i, int pos) {
+    if (pos < k) {
+      a.cand_key[slot0 + pos] = key[i];
+      a.cand_idx[slot0 + pos] = base + i * T + (int)threadIdx.x;
     }
-  for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) {
+  });
+  for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += T) {
     a.cand_key[slot0 + p2] = 0u;
     a.cand_idx[slot0 + p2] = -1;
   }
@@ -596,13 +680,11 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_chunk(IndexArgs a) {
 // ascending row index, padded with key 0) and selects their top k, either as one chunk of
 // the next stage (same layout) or, in the last stage (one block per row), as the output.
 // Slot order is row-index order among real entries, so ties by slot are ties by row index.
-template <int NPT, bool FINAL>
-__global__ void __launch_bounds__(kTopkThreads) k_topk_merge(IndexArgs a, const uint32_t* in_key,
-                                                             const int32_t* in_idx, const int* in_count,
-                                                             int in_chunks, int group, uint32_t* out_key,
-                                                             int32_t* out_idx, int* out_count) {
-  __shared__ TopkShared sh;
-  __shared__ OrderShared<NPT> osh;
+template <int T, int NPT, bool FINAL>
+__global__ void __launch_bounds__(T) k_topk_merge(IndexArgs a, const uint32_t* in_key, const int32_t* in_idx,
+                                                  const int* in_count, int in_chunks, int group,
+                                                  uint32_t* out_key, int32_t* out_idx, int* out_count) {
+  __shared__ SelShared<T, NPT> sh;
   const int row = blockIdx.x, q = blockIdx.y, out_chunks = gridDim.y;
   const int k = a.topk;
   const int c0 = q * group, c1 = min(in_chunks, c0 + group);
@@ -615,29 +697,27 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_merge(IndexArgs a, const 
     const int last = max(n - 1, 0);
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int j = i * kTopkThreads + (int)threadIdx.x;
+      const int j = i * T + (int)threadIdx.x;
       const uint32_t v = in_key[base + min(j, last)];
       key[i] = j < n ? v : 0u;
     }
   }
-  bool f[NPT];
-  int pos[NPT];
-  const int tot = select_keys<NPT>(sh, osh, key, nvalid, k, f, pos);
+  int32_t* out = a.idx_out + (int64_t)row * k;
+  const int64_t ob = ((int64_t)row * out_chunks + q) * k;
+  const int tot = select_keys<T, NPT>(sh, key, nvalid, k, [&](int i, int pos) {
+    if (pos >= k) return;
+    const int32_t gi = in_idx[base + i * T + (int)threadIdx.x];
+    if (FINAL) {
+      out[pos] = gi;
+    } else {
+      out_key[ob + pos] = key[i];
+      out_idx[ob + pos] = gi;
+    }
+  });
   if (FINAL) {
-    int32_t* out = a.idx_out + (int64_t)row * k;
-#pragma unroll
-    for (int i = 0; i < NPT; ++i)
-      if (f[i] && pos[i] < k) out[pos[i]] = in_idx[base + i * kTopkThreads + (int)threadIdx.x];
-    for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) out[p2] = -1;
+    for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += T) out[p2] = -1;
   } else {
-    const int64_t ob = ((int64_t)row * out_chunks + q) * k;
-#pragma unroll
-    for (int i = 0; i < NPT; ++i)
-      if (f[i] && pos[i] < k) {
-        out_key[ob + pos[i]] = key[i];
-        out_idx[ob + pos[i]] = in_idx[base + i * kTopkThreads + (int)threadIdx.x];
-      }
-    for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += kTopkThreads) {
+    for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += T) {
       out_key[ob + p2] = 0u;
       out_idx[ob + p2] = -1;
     }
@@ -646,30 +726,30 @@ __global__ void __launch_bounds__(kTopkThreads) k_topk_merge(IndexArgs a, const 
 }
 
 // Plan of the top-k for rows of up to `cap` entries.  Rows that fit one register-resident
-// block take one block per row.  Longer rows go through stage 1 (chunks of npt1 * 1024
-// entries, `nchunk` per row) and merge stages that each reduce `group` chunks of k
-// candidates (about 8192 candidates per block) to one, until one block per row finishes.
+// block take one block per row.  Longer rows go through stage 1 (chunks of 8192 entries,
+// `nchunk` per row) and merge stages that each reduce `group` chunks of k candidates (8192
+// candidates per block) to one, until one block per row finishes; that needs k <= 4096.
+// Anything else uses the streaming kernel.
 #ifndef CSA_TOPK_SINGLE_MAX
 #define CSA_TOPK_SINGLE_MAX 16384   // rows up to this length always take one block
 #endif
+constexpr int kChunk = 8192;        // stage-1 entries per block
 constexpr int kMergeCands = 8192;   // candidates per merge block
-static int npt_for(int n) {
-  const int m = (n + kTopkThreads - 1) / kTopkThreads;
-  return m <= 4 ? 4 : (m <= 8 ? 8 : (m <= 16 ? 16 : (m <= 32 ? 32 : 48)));
-}
 TopkPlan topk_plan(int rows, int cap, int k) {
   TopkPlan pl{};
-  const int per = kTopkThreads;
-  if (cap <= CSA_TOPK_SINGLE_MAX || (cap <= 48 * per && rows >= 128) || k > 48 * per / 2) {
-    pl.mode = cap <= 48 * per ? 0 : 2;
+  if (cap <= CSA_TOPK_SINGLE_MAX || (cap <= 65536 && rows >= 128)) {
+    pl.mode = 0;
+    return pl;
+  }
+  if (k > kMergeCands / 2) {
+    pl.mode = cap <= 65536 ? 0 : 2;
     return pl;
   }
   pl.mode = 1;
-  pl.npt1 = 8;
-  pl.chunk = pl.npt1 * per;
-  pl.nchunk = (cap + pl.chunk - 1) / pl.chunk;
-  pl.group = max(2, kMergeCands / k);
-  if ((long long)rows * pl.nchunk > 65535LL * 1024) pl.mode = 2;
+  pl.chunk = kChunk;
+  pl.nchunk = (cap + kChunk - 1) / kChunk;
+  pl.group = kMergeCands / k;
+  if ((long long)rows > 0x7fffffffLL || pl.nchunk > 65535) pl.mode = 2;
   return pl;
 }
 
@@ -684,56 +764,49 @@ size_t topk_workspace(int rows, int cap, int k) {
   return (bytes + 255) / 256 * 256;
 }
 
-#define CSA_TOPK_MERGE(NPT, FINAL)                                                                      \
-  hipLaunchKernelGGL((k_topk_merge<NPT, FINAL>), grid, block, 0, s, a, in_key, in_idx, in_count, chunks, \
-                     group, out_key, out_idx, out_count)
-
-static void launch_merge(int npt, bool final_stage, dim3 grid, dim3 block, hipStream_t s, const IndexArgs& a,
+static void launch_merge(int n, bool final_stage, dim3 grid, hipStream_t s, const IndexArgs& a,
                          const uint32_t* in_key, const int32_t* in_idx, const int* in_count, int chunks,
                          int group, uint32_t* out_key, int32_t* out_idx, int* out_count) {
+  const dim3 block(1024);
+#define CSA_TOPK_MERGE(NPT, FIN)                                                                          \
+  hipLaunchKernelGGL((k_topk_merge<1024, NPT, FIN>), grid, block, 0, s, a, in_key, in_idx, in_count, chunks, \
+                     group, out_key, out_idx, out_count)
   if (final_stage) {
-    switch (npt) {
-      case 4: CSA_TOPK_MERGE(4, true); break;
-      case 8: CSA_TOPK_MERGE(8, true); break;
-      case 16: CSA_TOPK_MERGE(16, true); break;
-      case 32: CSA_TOPK_MERGE(32, true); break;
-      default: CSA_TOPK_MERGE(48, true); break;
-    }
+    if (n <= 4096) CSA_TOPK_MERGE(4, true);
+    else CSA_TOPK_MERGE(8, true);
   } else {
-    switch (npt) {
-      case 4: CSA_TOPK_MERGE(4, false); break;
-      case 8: CSA_TOPK_MERGE(8, false); break;
-      case 16: CSA_TOPK_MERGE(16, false); break;
-      case 32: CSA_TOPK_MERGE(32, false); break;
-      default: CSA_TOPK_MERGE(48, false); break;
-    }
+    if (n <= 4096) CSA_TOPK_MERGE(4, false);
+    else CSA_TOPK_MERGE(8, false);
   }
-}
 #undef CSA_TOPK_MERGE
+}
 
 hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
   IndexArgs a = a0;
   const int rows = a.B * a.Tq;
   const int k = a.topk;
   const TopkPlan pl = topk_plan(rows, a.cap, k);
-  const dim3 block(kTopkThreads);
   if (pl.mode == 0) {
     const dim3 grid(rows);
-    if (a.cap <= 4 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<4>, grid, block, 0, s, a);
-    else if (a.cap <= 16 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<16>, grid, block, 0, s, a);
-    else if (a.cap <= 32 * kTopkThreads) hipLaunchKernelGGL(k_topk_reg<32>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(k_topk_reg<48>, grid, block, 0, s, a);
+    if (a.cap <= 4096) hipLaunchKernelGGL((k_topk_reg<1024, 4>), grid, dim3(1024), 0, s, a);
+    else if (a.cap <= 8192) hipLaunchKernelGGL((k_topk_reg<1024, 8>), grid, dim3(1024), 0, s, a);
+    else if (a.cap <= 16384) hipLaunchKernelGGL((k_topk_reg<1024, 16>), grid, dim3(1024), 0, s, a);
+    else if (a.cap <= 32768) hipLaunchKernelGGL((k_topk_reg<1024, 32>), grid, dim3(1024), 0, s, a);
+    else if (a.cap <= 49152) hipLaunchKernelGGL((k_topk_reg<1024, 48>), grid, dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL((k_topk_reg<1024, 64>), grid, dim3(1024), 0, s, a);
     return hipGetLastError();
   }
   if (pl.mode == 2) {
-    hipLaunchKernelGGL(k_topk, dim3(rows), block, 0, s, a);
+    hipLaunchKernelGGL(k_topk, dim3(rows), dim3(kTopkThreads), 0, s, a);
     return hipGetLastError();
   }
   // candidate areas A (stage-1 chunks) and B (first merge stage), each [keys | indices | counts]
   const size_t nA = (size_t)rows * pl.nchunk * k;
   const int c2 = (pl.nchunk + pl.group - 1) / pl.group;
   const size_t nB = (size_t)rows * c2 * k;
-  auto align = [](uint8_t* p) { return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255)); };
+  auto align = [](uint8_t* p) {
+    return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255));
+  };
   uint8_t* w = align(reinterpret_cast<uint8_t*>(a.cand_key));
   uint32_t* keyA = reinterpret_cast<uint32_t*>(w);
   int32_t* idxA = reinterpret_cast<int32_t*>(keyA + nA);
@@ -747,7 +820,7 @@ hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
   a.cand_count = cntA;
   a.chunk = pl.chunk;
   a.nchunk = pl.nchunk;
-  hipLaunchKernelGGL(k_topk_chunk<8>, dim3(rows, pl.nchunk), block, 0, s, a);
+  hipLaunchKernelGGL((k_topk_chunk<1024, kChunk / 1024>), dim3(rows, pl.nchunk), dim3(1024), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t* in_key = keyA;
@@ -756,17 +829,17 @@ hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
   int chunks = pl.nchunk;
   bool in_A = true;
   for (;;) {
-    if ((long long)chunks * k <= kMergeCands || chunks <= pl.group) {
-      launch_merge(npt_for(chunks * k), true, dim3(rows, 1), block, s, a, in_key, in_idx, in_count, chunks,
-                   chunks, nullptr, nullptr, nullptr);
+    if (chunks <= pl.group) {
+      launch_merge(chunks * k, true, dim3(rows, 1), s, a, in_key, in_idx, in_count, chunks, chunks, nullptr,
+                   nullptr, nullptr);
       return hipGetLastError();
     }
     const int out_chunks = (chunks + pl.group - 1) / pl.group;
     uint32_t* ok_ = in_A ? keyB : keyA;
     int32_t* oi = in_A ? idxB : idxA;
     int* oc = in_A ? cntB : cntA;
-    launch_merge(npt_for(pl.group * k), false, dim3(rows, out_chunks), block, s, a, in_key, in_idx, in_count,
-                 chunks, pl.group, ok_, oi, oc);
+    launch_merge(pl.group * k, false, dim3(rows, out_chunks), s, a, in_key, in_idx, in_count, chunks,
+                 pl.group, ok_, oi, oc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     in_key = ok_;
