@@ -453,8 +453,8 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
 
 // Merge split partials: M = max(sink, m_s), Z = 2^(sink - M) + sum l_s 2^(m_s - M),
 // o = sum 2^(m_s - M) o_s / Z, then rotate back and store.  A block of 256 lanes merges 4
-// (row, head) pairs, 8 channels per lane; every split's (max, sum) is read before any output
-// partial so that all of a lane's loads are in flight together.
+// (row, head) pairs, 8 channels per lane; splits are merged online, four per round, so that a
+// round's (max, sum) and output loads are all in flight together.
 constexpr int kCombineHeads = 4;
 __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
   const int rows = a.B * a.Tq;
@@ -465,26 +465,31 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
   const int64_t p = a.q_pos[row];
   const float sink2 = a.sink[head] * kLog2e;
   const int64_t base = (int64_t)row * a.nsplit * a.H + head;        // partial (row, s, head) = base + s * H
-  float M = sink2;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * a.H)]);
-  float Z = exp2f(sink2 - M);
+  // online merge, 4 splits per round: each round's (max, sum) and output loads go out together
+  float M = sink2, Z = 1.f;   // Z relative to 2^M
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 4 <= a.nsplit; s += 4) {
+  for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
     f32x4 v[4][2];
     float ms[4], ls[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int64_t pr = base + (int64_t)(s + u) * a.H;
+      const int64_t pr = base + (int64_t)min(s0 + u, a.nsplit - 1) * a.H;
       const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * pr);
-      ms[u] = ml[0];
+      ms[u] = s0 + u < a.nsplit ? ml[0] : kNegBig;
       ls[u] = ml[1];
       v[u][0] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
       v[u][1] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4);
     }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, ms[u]);
+    const float r = exp2f(M - Mn);
+    Z *= r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= r;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float w = exp2f(ms[u] - M);
+      const float w = exp2f(ms[u] - Mn);   // 0 for the padding of a partial round
       Z += ls[u] * w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -492,19 +497,7 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
         o[4 + i] += w * v[u][1][i];
       }
     }
-  }
-  for (; s < a.nsplit; ++s) {
-    const int64_t pr = base + (int64_t)s * a.H;
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * pr);
-    const f32x4 v0 = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
-    const f32x4 v1 = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4);
-    const float w = exp2f(ml[0] - M);
-    Z += ml[1] * w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[i] += w * v0[i];
-      o[4 + i] += w * v1[i];
-    }
+    M = Mn;
   }
   const float inv = Z > 0.f ? 1.f / Z : 0.f;
 #pragma unroll
