@@ -107,6 +107,8 @@ def capture_chain(layers, torch):
 
 
 def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layers=30):
+    if wl.Tq > 1:
+        max_layers = 2      # prefill: each step's own tensors (q, scores, output) exceed the 256 MB MALL
     """Time `steps_n` steps rotating over distinct layers; return timings (ms).
 
     Headline: layer steps replayed from one HIP graph that chains all rotated layers (as a
@@ -187,6 +189,60 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     return out
 
 
+def compressor_bulk(torch, reps=3):
+    """csa_compress over whole raw streams (the compressor's HBM benchmark): kv and pooling
+    logits read once, entries written once.  Inputs tile one seeded 64K-token random block
+    (the kernel has no data-dependent control flow).  Shapes: the 65K CSA decode batch
+    (32 x 65,536 tokens), the Flash 1M batch with fp8 entries (4 x 1,048,576) and HCA at 1M
+    (4 of the 16 sequences of the HCA decode batch; the per-sequence work is identical)."""
+    import math as _m
+    from compressed_attention_long_amd import _lib as ops
+    from compressed_attention_long_amd.step import rope_inv_freq
+    dev = "cuda"
+    inv = rope_inv_freq(160000.0, 64, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    blk = 65536
+    base_kv = torch.randn((1, blk, 512), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    base_z = torch.randn((1, blk, 512), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = {}
+    for name, B, T, window, stride, fp8 in [("csa_65k_b32", 32, 65536, 8, 4, False),
+                                            ("csa_1m_b4_fp8", 4, 1 << 20, 8, 4, True),
+                                            ("hca_1m_b4", 4, 1 << 20, 128, 128, False)]:
+        kv = torch.empty((B, T, 512), dtype=torch.bfloat16, device=dev)
+        z = torch.empty_like(kv)
+        kv.view(B, T // blk, blk, 512).copy_(base_kv.expand(B, T // blk, blk, 512).reshape(B, T // blk, blk, 512))
+        z.view(B, T // blk, blk, 512).copy_(base_z.expand(B, T // blk, blk, 512).reshape(B, T // blk, blk, 512))
+        E = (T - window) // stride + 1
+        nv = torch.full((B,), E, dtype=torch.int32, device=dev)
+        p0 = torch.ones((B,), dtype=torch.int64, device=dev)
+        if fp8:
+            cache = ops.Cache(torch.empty((B, E, 512), dtype=torch.uint8, device=dev), nv, p0, window, stride,
+                              scales=torch.empty((B, E, 8), dtype=torch.float32, device=dev), scale_block=64)
+            out_bytes = B * E * (512 + 32)
+        else:
+            cache = ops.Cache(torch.empty((B, E, 512), dtype=torch.bfloat16, device=dev), nv, p0, window, stride)
+            out_bytes = B * E * 1024
+        in_bytes = 2 * B * T * 1024
+        ops.compress(kv, z, cache, 0, E, inv, 64)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ops.compress(kv, z, cache, 0, E, inv, 64)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        t = sorted(ts)[len(ts) // 2]
+        gbs = (in_bytes + out_bytes) / (t * 1e-3) / 1e9
+        out[name] = {"ms": t, "bytes": in_bytes + out_bytes, "GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                     "entries": B * E}
+        del kv, z, cache
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the same workload: whole decode steps of
     single sequences (compress the new entry, index, select, attend), as many as fit
@@ -239,9 +295,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v4pro_csa_decode_65k")
-    ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8",
+    ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8,v4pro_csa_prefill_4k_on_131k",
                     help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compressor-bulk", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -309,6 +366,9 @@ def main():
             e2["index_ms"] = t2["index"]
             e2["index_GB_per_s"] = c2["index_bytes"] / (t2["index"] * 1e-3) / 1e9
         extra[name] = e2
+    if not args.no_compressor_bulk:
+        print("[bench] compressor over whole raw streams", file=sys.stderr, flush=True)
+        extra["compressor_bulk"] = compressor_bulk(torch)
     base = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
