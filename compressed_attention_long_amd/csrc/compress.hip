@@ -23,64 +23,23 @@ struct PoolState {
   float m[8], s[8], sv[8];
 };
 
+// Hardware exp2 (v_exp_f32, about 1 ulp; results below 2^-126 flush to zero, which only
+// drops weights that small relative to the running maximum).
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ void pool_reset(PoolState& p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) { p.m[i] = kNegBig; p.s[i] = 0.f; p.sv[i] = 0.f; }
-}
-
-// Fold one raw token (8 channels: values v, logits already multiplied by log2 e) into p.
-__device__ __forceinline__ void pool_add(PoolState& p, const float* v, const float* z2) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float mn = fmaxf(p.m[i], z2[i]);
-    float a = exp2f(p.m[i] - mn);
-    float b = exp2f(z2[i] - mn);
-    p.s[i] = p.s[i] * a + b;
-    p.sv[i] = p.sv[i] * a + b * v[i];
-    p.m[i] = mn;
-  }
 }
 
 __device__ __forceinline__ void pool_merge(PoolState& out, const PoolState& x, const PoolState& y) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float mn = fmaxf(x.m[i], y.m[i]);
-    float a = exp2f(x.m[i] - mn), b = exp2f(y.m[i] - mn);
+    float a = fexp2(x.m[i] - mn), b = fexp2(y.m[i] - mn);
     out.m[i] = mn;
     out.s[i] = x.s[i] * a + y.s[i] * b;
     out.sv[i] = x.sv[i] * a + y.sv[i] * b;
-  }
-}
-
-// Add one block of `n` raw tokens starting at token row `t0` into p.  Loads are issued
-// kU tokens at a time before the (serially dependent) softmax updates consume them.
-constexpr int kU = 8;
-__device__ __forceinline__ void pool_block(PoolState& p, const uint16_t* kv, const uint16_t* lg,
-                                           int64_t ld_tok, int t0, int n, int c0) {
-  for (int t = 0; t < n; t += kU) {
-    u32x4 wv[kU], wz[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (t + u < n) {
-        wv[u] = *reinterpret_cast<const u32x4*>(kv + (int64_t)(t0 + t + u) * ld_tok + c0);
-        wz[u] = lg ? *reinterpret_cast<const u32x4*>(lg + (int64_t)(t0 + t + u) * ld_tok + c0)
-                   : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (t + u < n) {
-        float v[8], z[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16lo_to_f32(wv[u][i]);
-          v[2 * i + 1] = bf16hi_to_f32(wv[u][i]);
-          z[2 * i] = bf16lo_to_f32(wz[u][i]) * kLog2e;
-          z[2 * i + 1] = bf16hi_to_f32(wz[u][i]) * kLog2e;
-        }
-        pool_add(p, v, z);
-      }
-    }
   }
 }
 
@@ -90,6 +49,7 @@ struct RopeIn {
   int64_t pos0;
   double fr[4];
 };
+
 __device__ __forceinline__ RopeIn rope_in(const CompressArgs& a, int b, int c0) {
   RopeIn r;
   r.pos0 = a.pos0[b];
@@ -100,6 +60,73 @@ __device__ __forceinline__ RopeIn rope_in(const CompressArgs& a, int b, int c0) 
     r.fr[k] = (a.rope_dim > 0 && c >= rot0) ? a.inv_freq[(c - rot0) >> 1] : 0.0;
   }
   return r;
+}
+
+// A block of up to kB tokens of one lane's 8 channels (kv and logits), held in registers so
+// that the next block's loads can be in flight while the current one is pooled.
+constexpr int kB = 4;
+struct RawBlock {
+  u32x4 v[kB], z[kB];
+};
+// tokens t0 + u * tstride, u < n
+__device__ __forceinline__ void load_block(RawBlock& r, const uint16_t* kv, const uint16_t* lg, int64_t ld_tok,
+                                           int64_t t0, int n, int c0, int tstride = 1) {
+#pragma unroll
+  for (int u = 0; u < kB; ++u) {
+    if (u < n) {
+      const int64_t t = t0 + (int64_t)u * tstride;
+      r.v[u] = *reinterpret_cast<const u32x4*>(kv + t * ld_tok + c0);
+      r.z[u] = lg ? *reinterpret_cast<const u32x4*>(lg + t * ld_tok + c0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+// Fold the n tokens of a register block into p: one maximum over the block, then one
+// exponential per token and one rescale of the running state (1 + n exponentials per
+// channel instead of 2n).
+__device__ __forceinline__ void pool_regs(PoolState& p, const RawBlock& r, int n) {
+  float z[kB][8];
+#pragma unroll
+  for (int u = 0; u < kB; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[u][2 * i] = u < n ? bf16lo_to_f32(r.z[u][i]) * kLog2e : kNegBig;
+      z[u][2 * i + 1] = u < n ? bf16hi_to_f32(r.z[u][i]) * kLog2e : kNegBig;
+    }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float bm = z[0][c];
+#pragma unroll
+    for (int u = 1; u < kB; ++u) bm = fmaxf(bm, z[u][c]);
+    const float mn = fmaxf(p.m[c], bm);
+    const float al = fexp2(p.m[c] - mn);
+    float s = p.s[c] * al, sv = p.sv[c] * al;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (u < n) {
+        const float v = (c & 1) ? bf16hi_to_f32(r.v[u][c >> 1]) : bf16lo_to_f32(r.v[u][c >> 1]);
+        const float w = fexp2(z[u][c] - mn);
+        s += w;
+        sv += w * v;
+      }
+    }
+    p.s[c] = s;
+    p.sv[c] = sv;
+    p.m[c] = mn;
+  }
+}
+
+// Add the n raw tokens starting at token row t0 into p, kB at a time, the loads of the next
+// block in flight while the current one is pooled.
+__device__ __forceinline__ void pool_block(PoolState& p, const uint16_t* kv, const uint16_t* lg,
+                                           int64_t ld_tok, int t0, int n, int c0) {
+  RawBlock r0, r1;
+  load_block(r0, kv, lg, ld_tok, t0, min(kB, n), c0);
+  for (int t = 0; t < n; t += kB) {
+    const int m = min(kB, n - t);
+    if (t + kB < n) load_block(r1, kv, lg, ld_tok, t0 + t + kB, min(kB, n - t - kB), c0);
+    pool_regs(p, r0, m);
+    r0 = r1;
+  }
 }
 
 // Finish one row: normalise, rotate, store.
@@ -170,8 +197,26 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
   const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
                                 : nullptr;
   const RopeIn ri = rope_in(a, b, c0);
-  if (a.window == 2 * a.stride && a.run > 1) {
-    // Overlapping rows: entry i = block i + block i+1 (blocks of `stride` tokens).
+  if (a.window == 2 * a.stride && a.run > 1 && a.stride <= kB) {
+    // Overlapping rows: entry i = block i + block i+1 (blocks of `stride` tokens).  The
+    // loads of block i + 2 are issued before block i + 1 is pooled.
+    const int st = a.stride;
+    PoolState prev, cur, both;
+    RawBlock r0, r1;
+    load_block(r0, kv, lg, a.ld_tok, first * st, st, c0);
+    load_block(r1, kv, lg, a.ld_tok, (first + 1) * st, st, c0);
+    pool_reset(prev);
+    pool_regs(prev, r0, st);
+    for (int i = first; i < last; ++i) {
+      if (i + 1 < last) load_block(r0, kv, lg, a.ld_tok, (i + 2) * st, st, c0);
+      pool_reset(cur);
+      pool_regs(cur, r1, st);
+      pool_merge(both, prev, cur);
+      finish_row(both, a, ri, b, a.first_row + i, c0);
+      prev = cur;
+      r1 = r0;
+    }
+  } else if (a.window == 2 * a.stride && a.run > 1) {
     PoolState prev, cur, both;
     pool_reset(prev);
     pool_block(prev, kv, lg, a.ld_tok, first * a.stride, a.stride, c0);
@@ -213,32 +258,13 @@ __global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
   PoolState p;
   pool_reset(p);
   const int t0 = i * a.stride;
-  // group g takes tokens g, g + 16, g + 32, ... of the window, kU of them per load round
+  // group g takes tokens g, g + 16, g + 32, ... of the window, kB of them per load round
   const int mine = g < a.window ? (a.window - 1 - g) / kSplitGroups + 1 : 0;
-  for (int u0 = 0; u0 < mine; u0 += kU) {
-    u32x4 wv[kU], wz[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (u0 + u < mine) {
-        const int64_t t = t0 + g + (int64_t)(u0 + u) * kSplitGroups;
-        wv[u] = *reinterpret_cast<const u32x4*>(kv + t * a.ld_tok + c0);
-        wz[u] = lg ? *reinterpret_cast<const u32x4*>(lg + t * a.ld_tok + c0) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (u0 + u < mine) {
-        float v[8], z[8];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[2 * k] = bf16lo_to_f32(wv[u][k]);
-          v[2 * k + 1] = bf16hi_to_f32(wv[u][k]);
-          z[2 * k] = bf16lo_to_f32(wz[u][k]) * kLog2e;
-          z[2 * k + 1] = bf16hi_to_f32(wz[u][k]) * kLog2e;
-        }
-        pool_add(p, v, z);
-      }
-    }
+  for (int u0 = 0; u0 < mine; u0 += kB) {
+    RawBlock r;
+    const int m = min(kB, mine - u0);
+    load_block(r, kv, lg, a.ld_tok, (int64_t)t0 + g + (int64_t)u0 * kSplitGroups, m, c0, kSplitGroups);
+    pool_regs(p, r, m);
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -256,7 +282,7 @@ __global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
     for (int h = 0; h < kSplitGroups; ++h) m = fmaxf(m, sm_m[h][cs + k]);
     float ss = 0.f, sv = 0.f;
     for (int h = 0; h < kSplitGroups; ++h) {
-      const float f = exp2f(sm_m[h][cs + k] - m);
+      const float f = fexp2(sm_m[h][cs + k] - m);
       ss += sm_s[h][cs + k] * f;
       sv += sm_v[h][cs + k] * f;
     }

@@ -56,7 +56,7 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 
 // ---------------------------------------------------------------- scores
 
-constexpr int kIdxTilesPerWave = 16;     // 16 entries per tile
+constexpr int kIdxTilesPerWave = 32;     // 16 entries per tile
 constexpr int kIdxWaves = 4;
 constexpr int kDepth = 4;                // score-tile loads in flight per wave
 constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
