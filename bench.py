@@ -243,6 +243,57 @@ def compressor_bulk(torch, reps=3):
     return out
 
 
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_bytes_csa_decode_65k.md")
+
+
+CALL_SOURCES = {"attend": "attend.hip", "index": "indexer.hip", "compress": "compress.hip"}
+
+
+def source_digest(call):
+    """sha256 over the sources of one C-ABI call's kernels: counter-derived traffic is only reported
+    for the code it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (CALL_SOURCES[call], "api.hip", "common.hpp", "internal.hpp"):
+        with open(os.path.join(ROOT, "compressed_attention_long_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, call):
+    """HBM bytes per call from the committed counter summary (FETCH_SIZE x calibration + WRITE_SIZE),
+    or None when the summary is missing, covers another workload/call, or the kernels changed since."""
+    try:
+        with open(PMC_SUMMARY) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    d = json.loads(line[len("traffic-json: "):])
+                    if d.get("workload") == workload and d.get("call") == call and d.get("sources") == source_digest(call):
+                        return d["bytes_per_call"]
+    except OSError:
+        pass
+    return None
+
+
+def pmc_probe(wl, torch, layers_n=4, reps=2):
+    """Workload for hardware-counter passes: a plain 256 MiB device copy three times (calibrates
+    FETCH_SIZE / WRITE_SIZE against a known byte count), then `reps` eager steps over `layers_n`
+    distinct layers, every C-ABI call launched on its own."""
+    src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    layers = build_layers(wl, layers_n, "cuda", torch, torch.bfloat16)
+    for _ in range(reps):
+        for L in layers:
+            L.run()
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_probe": wl.name, "copy_bytes_each_way": 256 << 20, "layers": layers_n, "reps": reps,
+                      "sources": {c: source_digest(c) for c in CALL_SOURCES}}), flush=True)
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The fp64 oracle on a bounded sample of the same workload: whole decode steps of
     single sequences (compress the new entry, index, select, attend), as many as fit
@@ -300,6 +351,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compressor-bulk", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run only the hardware-counter workload (calibration copy + eager steps) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -314,6 +367,9 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
 
     wl = ci.WORKLOADS[args.workload]
+    if args.pmc_probe:
+        pmc_probe(wl, torch)
+        return
     print(f"[bench] workload {wl.name}: timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr,
           flush=True)
     tm = time_workload(wl, args.steps, args.warmup, torch)
@@ -338,12 +394,12 @@ def main():
     dom = max(calls, key=lambda k: calls[k]["ms"])
     if dom == "attend":
         roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": calls[dom]["mfma_frac"], "traffic": None,
+                "unit": "TFLOP/s", "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom),
                 "kernel": "csa_attend (k_attend + k_attend_combine)",
                 "hbm_GB_per_s": calls[dom]["GB_per_s"], "hbm_frac": calls[dom]["hbm_frac"]}
     else:
         roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": calls[dom]["hbm_frac"], "traffic": None,
+                "frac": calls[dom]["hbm_frac"], "traffic": measured_traffic(wl.name, dom),
                 "kernel": "csa_index_topk (k_index_scores + k_topk)" if dom == "index" else "csa_compress"}
     extra = {"calls": calls, "timing": "value = tokens / wall time of layer steps replayed from one HIP graph "
                                        "chaining the rotated layers; per_layer_graph = one graph launch per step; "
