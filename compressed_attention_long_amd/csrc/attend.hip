@@ -53,6 +53,25 @@ __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int wi
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups holding one head) with
+// the gfx950 lane-swap permutes, no LDS round trip.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which softmax weights tolerate.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 typedef __attribute__((address_space(3))) void lds_void;
@@ -73,9 +92,9 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tbA1[kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t tbB0[kTile * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t tbB1[kTile * kPitch];
-  __shared__ int tvalid[kBufs][kTile];
+  __shared__ __attribute__((aligned(4))) uint8_t tvalid[kBufs][kTile];
   __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
-  __shared__ f32x2 mrg_ml[kGroupWaves][kWave];  // group 1's (max, sum) per lane, for the merge
+  __shared__ f32x4 mrg_ml[kGroupWaves][kWave];  // group 1's (max, sum, normaliser) per lane, for the merge
 
   const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const uint32_t total = gridDim.x;
@@ -205,22 +224,25 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   };
 
   // ---- prologue: the first two pairs' row numbers are loaded first (they gate the first
-  // tile loads) and the first pair's rows go out as soon as they arrive; the query
-  // fragments follow, and the rotation table is built while they are in flight.
+  // tile loads), then the query fragments; the first pair's rows go out as soon as the
+  // numbers arrive, and the rotation table is built while everything is in flight.
   const int npair = (ntile + 1) / 2;
-  const PairRows rows0 = pair_rows(0, pair_idx(0));
+  const int idx0 = pair_idx(0);
   int idx_next = pair_idx(1);
+  // the query loads go out before the first tile loads, which wait for the indices: in-order
+  // completion then lets the query rotation start while those tiles are still in flight
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + min(head, a.H - 1)) * kD;
+  u32x4 qraw[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
   const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
+  const PairRows rows0 = pair_rows(0, idx0);
   if (ntile > 0) {
     mark_pair(0, rows0, 0);
 #pragma unroll
     for (int k = 0; k < 8; ++k) issue_row(0, rows0, k, tbA0, tbA1);
     if (FP8) { fetch_fp8(0, rows0); store_fp8(0, rows0, tbA0, tbA1); }
   }
-  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + min(head, a.H - 1)) * kD;
-  u32x4 qraw[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
   if (tid < a.rope_dim / 2) {
     float cs, sn;
     rope_cs(p, fr, cs, sn);
@@ -261,8 +283,11 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
 
   // ---- online softmax state (per lane: head n; the 4 lanes of a head hold equal m).  The
   // reference maximum starts at the first tile's maximum (so a dominant row there gets weight
-  // exactly 1); the sink joins once, in the epilogue or in the split merge.
-  float m_run = kNegBig, l_run = 0.f;
+  // exactly 1); the sink joins once, in the epilogue or in the split merge.  l_run is the
+  // exact fp32 sum of the weights (for lse); n_run sums the weights as rounded to bf16 for
+  // the PV product and normalises the output, so the rounding of a dominant weight cancels
+  // between numerator and denominator.
+  float m_run = kNegBig, l_run = 0.f, n_run = 0.f;
   f32x4 acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -306,17 +331,19 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     float sv[8];
     int vmask = 0;
     float tmax = kNegBig;
+    // valid flags of rows 16kb + 4g + [0, 4): one 32-bit LDS read per kb
+    const uint32_t vf0 = *reinterpret_cast<const uint32_t*>(&tvalid[buf][4 * g]);
+    const uint32_t vf1 = *reinterpret_cast<const uint32_t*>(&tvalid[buf][16 + 4 * g]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * kb + i;
-        const int ok = tvalid[buf][16 * kb + 4 * g + i];
+        const bool ok = ((kb ? vf1 : vf0) >> (8 * i)) & 0xffu;
         sv[e] = sacc[kb][i] * a.scale_log2;
         if (ok) { vmask |= 1 << e; tmax = fmaxf(tmax, sv[e]); }
       }
-    tmax = wave_max_xor(tmax, 16);
-    tmax = wave_max_xor(tmax, 32);
+    tmax = max_lane_groups(tmax);
     // Lazy rescaling: the reference maximum m_run only moves when a tile's maximum exceeds it
     // by more than kRescale (log2 units), so the 128 output accumulators are rescaled rarely;
     // in between, weights exp2(s - m_run) stay below 2^kRescale, well inside bf16 and fp32.
@@ -325,6 +352,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       const float m_new = grow ? tmax : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
+      n_run *= alpha;
       // nothing accumulated yet (first tile with rows): the accumulators are zero already
       if (__any(grow && m_run > kNegBig)) {
 #pragma unroll
@@ -346,6 +374,8 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     pw[2] = pack_bf16x2(pv[4], pv[5]);
     pw[3] = pack_bf16x2(pv[6], pv[7]);
     const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) n_run += bf16lo_to_f32(pw[k]) + bf16hi_to_f32(pw[k]);
 
     // O^T += V^T P^T: A operand (channel 16db + n, rows 16r + 4g + j) via transposing loads
     const int L = lane & 15;
@@ -377,11 +407,11 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     if (grp == 1) {
 #pragma unroll
       for (int db = 0; db < 32; ++db) mbuf[db * kWave + lane] = acc[db];
-      mrg_ml[hw][lane] = f32x2{m_run, l_run};
+      mrg_ml[hw][lane] = f32x4{m_run, l_run, n_run, 0.f};
     }
     __syncthreads();
     if (grp == 1) return;
-    const f32x2 ml = mrg_ml[hw][lane];
+    const f32x4 ml = mrg_ml[hw][lane];
     const float M = fmaxf(m_run, ml[0]);
     const float sa = fast_exp2(m_run - M), sb = fast_exp2(ml[0] - M);
 #pragma unroll
@@ -391,22 +421,23 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * sa + o[i] * sb;
     }
     l_run = l_run * sa + ml[1] * sb;
+    n_run = n_run * sa + ml[2] * sb;
     m_run = M;
   }
 
   // ---- epilogue
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
+  float l_tot = sum_lane_groups(l_run);
+  const float n_tot = sum_lane_groups(n_run);
   if (!head_ok) return;
   if (a.nsplit == 1) {
     // fold in the sink: Z = l 2^(m - M) + 2^(sink - M), M = max(m, sink)
     const float sink2 = a.sink[head] * kLog2e;
     const float M = fmaxf(m_run, sink2);
     const float sc = exp2f(m_run - M);
-    l_tot = l_tot * sc + exp2f(sink2 - M);
+    const float es = exp2f(sink2 - M);
+    l_tot = l_tot * sc + es;
     m_run = M;
-    const float inv = sc / l_tot;
+    const float inv = sc / (n_tot * sc + es);
     const int rot0 = kD - a.rope_dim;
 #pragma unroll
     for (int db = 0; db < 32; ++db) {
@@ -445,14 +476,15 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     for (int db = 0; db < 32; ++db)
       *reinterpret_cast<f32x4*>(a.part_o + pr * kD + 16 * db + 4 * g) = acc[db];
     if (g == 0) {
-      a.part_ml[2 * pr] = m_run;
-      a.part_ml[2 * pr + 1] = l_tot;
+      *reinterpret_cast<f32x4*>(a.part_ml + 4 * pr) = f32x4{m_run, n_tot, l_tot, 0.f};
     }
   }
 }
 
-// Merge split partials: M = max(sink, m_s), Z = 2^(sink - M) + sum l_s 2^(m_s - M),
-// o = sum 2^(m_s - M) o_s / Z, then rotate back and store.  A block of 256 lanes merges 4
+// Merge split partials: M = max(sink, m_s), o = sum 2^(m_s - M) o_s / Zo with
+// Zo = 2^(sink - M) + sum n_s 2^(m_s - M) (n_s: the sum of the weights as rounded for the
+// split's PV product), lse = M + log2(2^(sink - M) + sum l_s 2^(m_s - M)) with the exact
+// sums l_s; then rotate back and store.  A block of 256 lanes merges 4
 // (row, head) pairs, 8 channels per lane; splits are merged online, four per round, so that a
 // round's (max, sum) and output loads are all in flight together.
 constexpr int kCombineHeads = 4;
@@ -466,17 +498,18 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
   const float sink2 = a.sink[head] * kLog2e;
   const int64_t base = (int64_t)row * a.nsplit * a.H + head;        // partial (row, s, head) = base + s * H
   // online merge, 4 splits per round: each round's (max, sum) and output loads go out together
-  float M = sink2, Z = 1.f;   // Z relative to 2^M
+  float M = sink2, Z = 1.f, Zo = 1.f;   // relative to 2^M
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
     f32x4 v[4][2];
-    float ms[4], ls[4];
+    float ms[4], ns[4], ls[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t pr = base + (int64_t)min(s0 + u, a.nsplit - 1) * a.H;
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * pr);
+      const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 4 * pr);
       ms[u] = s0 + u < a.nsplit ? ml[0] : kNegBig;
-      ls[u] = ml[1];
+      ns[u] = ml[1];
+      ls[u] = ml[2];
       v[u][0] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
       v[u][1] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4);
     }
@@ -485,12 +518,14 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
     for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, ms[u]);
     const float r = exp2f(M - Mn);
     Z *= r;
+    Zo *= r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= r;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float w = exp2f(ms[u] - Mn);   // 0 for the padding of a partial round
       Z += ls[u] * w;
+      Zo += ns[u] * w;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         o[i] += w * v[u][0][i];
@@ -499,7 +534,7 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
     }
     M = Mn;
   }
-  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  const float inv = Zo > 0.f ? 1.f / Zo : 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] *= inv;
   const int rot0 = kD - a.rope_dim;
@@ -553,7 +588,7 @@ static int attend_sps(int nsplit, int slot_cap) {
 size_t attend_workspace(int rows, int H, int slot_cap, bool csa) {
   const int ns = attend_nsplit(rows, H, slot_cap, csa);
   if (ns <= 1) return 0;
-  return (size_t)rows * ns * H * (kD + 2) * sizeof(float) + 256;
+  return (size_t)rows * ns * H * (kD + 4) * sizeof(float) + 256;
 }
 
 hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {

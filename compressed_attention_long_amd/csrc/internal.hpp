@@ -79,7 +79,7 @@ struct AttendArgs {
   // split-KV partials
   int nsplit, slot_cap, slots_per_split;
   float* part_o;          // [rows, nsplit, H, 512]
-  float* part_ml;         // [rows, nsplit, H, 2]
+  float* part_ml;         // [rows, nsplit, H, 4]: reference max, normaliser, exact sum, pad
 };
 int attend_nsplit(int rows, int H, int slot_cap, bool csa);
 size_t attend_workspace(int rows, int H, int slot_cap, bool csa);
