@@ -175,6 +175,135 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- scores, many query rows
+
+// Prefill chunks (many query rows per sequence): every query row scores the same keys, so a
+// block takes 16 consecutive query rows of one sequence (two per wave, eight waves) and
+// streams the sequence's keys once through LDS, 128 keys per double-buffered chunk, instead
+// of once per query row.  Each key fragment read from LDS then feeds 2 rows x HB head
+// blocks of MFMAs, and the contraction is MFMA-bound rather than bound by key traffic.
+// Keys are staged with the 16-byte segments of key r rotated by r (slot = segment ^ (r & 15)),
+// so that the 16 keys of an MFMA tile read one segment each from 16 different bank groups.
+// bf16 keys; the query and channel permutation are those of k_index_scores.
+constexpr int kMqWaves = 8;
+constexpr int kMqRows = 2 * kMqWaves;     // query rows per block
+constexpr int kMqChunk = 128;             // keys per LDS chunk (32 KB of bf16 keys)
+
+template <int HB>
+__global__ void __launch_bounds__(kMqWaves * 64, 1) k_index_scores_mq(IndexArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[kMqChunk * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[kMqChunk * 256];
+  const int groups = (a.Tq + kMqRows - 1) / kMqRows;
+  const int b = blockIdx.x / groups;
+  const int t0 = (blockIdx.x % groups) * kMqRows;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+
+  // visible entries: of every row of the block (the loop runs to the largest), and of this
+  // wave's two rows
+  const int64_t pos0 = a.pos0[b];
+  const int nv = a.n_valid[b];
+  int nvis_max = 0;
+  for (int r = 0; r < kMqRows; ++r) {
+    const int t = t0 + r;
+    if (t < a.Tq) nvis_max = max(nvis_max, visible_rows(a.q_pos[(int64_t)b * a.Tq + t], pos0, a.window, a.stride, nv, a.cap));
+  }
+  int row[2], nvis[2];
+  bool rok[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int t = t0 + 2 * wave + r;
+    rok[r] = t < a.Tq;
+    row[r] = b * a.Tq + min(t, a.Tq - 1);
+    nvis[r] = rok[r] ? visible_rows(a.q_pos[row[r]], pos0, a.window, a.stride, nv, a.cap) : 0;
+  }
+
+  // query fragments (A operand): row r, head hb*16 + n, channels 32g + 8s + [0, 8)
+  bf16x8 qf[2][HB][4];
+  float wv[2][HB][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q_idx) + (int64_t)row[r] * a.Hi * a.Di;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int h = hb * 16 + n;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(q + (int64_t)min(h, a.Hi - 1) * a.Di + 32 * g + 8 * s);
+        if (h >= a.Hi) v = u32x4{0u, 0u, 0u, 0u};
+        qf[r][hb][s] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = hb * 16 + 4 * g + i;
+        const float wl = a.w[(int64_t)row[r] * a.Hi + min(hh, a.Hi - 1)];
+        wv[r][hb][i] = hh < a.Hi ? wl : 0.f;
+      }
+    }
+  }
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)b * a.cap * 256;
+  const int jlast = max(nvis_max - 1, 0);
+  const int nchunk = (nvis_max + kMqChunk - 1) / kMqChunk;
+  // chunk c: 32 loads of 1 KB (4 keys each), four per wave
+  auto issue_chunk = [&](int c, uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      const int kl = blk * 4 + (lane >> 4);          // key within the chunk
+      const int j = min(c * kMqChunk + kl, jlast);
+      const int seg = (lane & 15) ^ (kl & 15);       // this lane's slot holds segment seg
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kbase + (int64_t)j * 256 + 16 * seg),
+                                       (__attribute__((address_space(3))) void*)&buf[blk * 1024], 16, 0, 0);
+    }
+  };
+  auto chunk_step = [&](int c, const uint8_t* cur, uint8_t* nxt) {
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): this wave's part of chunk c
+    __syncthreads();                                    // all parts; everyone is done with c - 1
+    if (c + 1 < nchunk) issue_chunk(c + 1, nxt);
+#pragma unroll 2
+    for (int tt = 0; tt < kMqChunk / 16; ++tt) {
+      const int kl = 16 * tt + n;
+      bf16x8 kf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[s] = *reinterpret_cast<const bf16x8*>(&cur[kl * 256 + 16 * ((4 * g + s) ^ n)]);
+      f32x4 acc[2][HB];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          acc[r][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc[r][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[r][hb][s], kf[s], acc[r][hb], 0, 0, 0);
+        }
+      const int j = c * kMqChunk + kl;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        float sc = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc += wv[r][hb][i] * relu(acc[r][hb][i]);
+        sc = sum_lane_groups(sc);
+        if (g == 0 && rok[r] && j < a.cap) a.scores[(int64_t)row[r] * a.cap + j] = j < nvis[r] ? sc : -INFINITY;
+      }
+    }
+  };
+  if (nchunk > 0) issue_chunk(0, kb0);
+  for (int c = 0; c < nchunk; c += 2) {
+    chunk_step(c, kb0, kb1);
+    if (c + 1 < nchunk) chunk_step(c + 1, kb1, kb0);
+  }
+  // entries past the last chunk score -inf
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (rok[r])
+      for (int j = nchunk * kMqChunk + lane; j < a.cap; j += 64) a.scores[(int64_t)row[r] * a.cap + j] = -INFINITY;
+}
+
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   const int rows = a.B * a.Tq;
   dim3 grid(rows, (a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
@@ -184,6 +313,14 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   if (HB == hb) {                                                                              \
     if (f8) hipLaunchKernelGGL((k_index_scores<hb, true>), grid, dim3(256), 0, s, a);          \
     else hipLaunchKernelGGL((k_index_scores<hb, false>), grid, dim3(256), 0, s, a);            \
+  }
+  if (!f8 && a.Tq >= kMqRows && a.Di == 128) {
+    const dim3 gmq(a.B * ((a.Tq + kMqRows - 1) / kMqRows));
+#define CSA_IDX_MQ(hb) \
+    if (HB == hb) hipLaunchKernelGGL((k_index_scores_mq<hb>), gmq, dim3(kMqWaves * 64), 0, s, a);
+    CSA_IDX_MQ(1) CSA_IDX_MQ(2) CSA_IDX_MQ(3) CSA_IDX_MQ(4)
+#undef CSA_IDX_MQ
+    return hipGetLastError();
   }
   CSA_IDX_LAUNCH(1) CSA_IDX_LAUNCH(2) CSA_IDX_LAUNCH(3) CSA_IDX_LAUNCH(4)
 #undef CSA_IDX_LAUNCH

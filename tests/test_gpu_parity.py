@@ -116,6 +116,8 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (1, 2, 48, 1500, [1500], True, 1, "end"),                  # k = 1, Hi not a multiple of 64
     (2, 1, 64, 20000, [20000, 19999], True, 1024, "end"),      # spans many blocks; two-stage top-k
     (2, 1, 64, 70000, [70000, 500], True, 1024, "end"),        # two-stage, 9 chunks; one row with < k visible
+    (2, 37, 64, 3000, [3000, 2100], False, 256, "causal"),     # multi-row kernel: ragged row groups, causal
+    (1, 16, 40, 1300, [1290], False, 64, "causal"),            # multi-row kernel, heads not a multiple of 16
 ])
 def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
     d = ci.Draw(200 + cap, "cpu")
