@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(kMqWaves * 64, 1) k_index_scores_mq(IndexArgs 
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0): this wave's part of chunk c
     __syncthreads();                                    // all parts; everyone is done with c - 1
     if (c + 1 < nchunk) issue_chunk(c + 1, nxt);
-#pragma unroll 2
+#pragma unroll 4
     for (int tt = 0; tt < kMqChunk / 16; ++tt) {
       const int kl = 16 * tt + n;
       bf16x8 kf[4];
@@ -658,31 +658,37 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
       for (int i = 0; i < NPT; ++i)
         if (ok(i) && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[hslot((key[i] - klo) >> shift)], 1u);
       __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 2047 - 32l - e (e < 32): the bins in descending key order
-        int c[32], sum = 0;
+      {
+        // thread t owns bins 2047 - BPT t - e (e < BPT): the bins in descending key order.
+        // Every wave scans its bins; the wave totals give each thread its prefix.
+        constexpr int BPT = kTopkBins / T;
+        int c[BPT], sum = 0;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          c[e] = (int)sh.hist[hslot(kTopkBins - 1 - (32 * lane + e))];
+        for (int e = 0; e < BPT; ++e) {
+          c[e] = (int)sh.hist[hslot(kTopkBins - 1 - (BPT * tid + e))];
           sum += c[e];
         }
         const int incl = wave_incl_scan(sum);
-        const int pre = incl - sum;
+        if (lane == 63) sh.red[wave] = (uint32_t)incl;   // the min/max scratch is free by now
+#pragma unroll
+        for (int e = 0; e < BPT; ++e) sh.hist[hslot(kTopkBins - 1 - (BPT * tid + e))] = 0;   // next round
+        __syncthreads();
+        int pre = incl - sum;
+#pragma unroll
+        for (int w2 = 0; w2 < W; ++w2) pre += w2 < wave ? (int)sh.red[w2] : 0;
         const int need = k - above;
-        if (pre < need && need <= incl) {
+        if (pre < need && need <= pre + sum) {
           int run = pre;
 #pragma unroll
-          for (int e = 0; e < 32; ++e) {
+          for (int e = 0; e < BPT; ++e) {
             if (run < need && run + c[e] >= need) {
-              sh.bstar = kTopkBins - 1 - (32 * lane + e);
+              sh.bstar = kTopkBins - 1 - (BPT * tid + e);
               sh.above = run;
               sh.bcnt = c[e];
             }
             run += c[e];
           }
         }
-#pragma unroll
-        for (int e = 0; e < 32; ++e) sh.hist[hslot(32 * lane + e)] = 0;   // clear for the next round
       }
       __syncthreads();
       const int bstar = sh.bstar;
