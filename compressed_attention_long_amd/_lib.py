@@ -22,6 +22,7 @@ CSA_BF16, CSA_FP8_E4M3, CSA_FP32 = 0, 1, 2
 # Entry points declared in include/csa.h, in declaration order.
 EXPORTS = (
     "csa_compress",
+    "csa_compress_batch",
     "csa_index_topk",
     "csa_index_topk_workspace_bytes",
     "csa_attend",
@@ -54,6 +55,22 @@ class CCache(ctypes.Structure):
     ]
 
 
+class CCompressCall(ctypes.Structure):
+    _fields_ = [
+        ("kv", ctypes.c_void_p),
+        ("logits", ctypes.c_void_p),
+        ("ld_tok", ctypes.c_int64),
+        ("ld_seq", ctypes.c_int64),
+        ("B", ctypes.c_int32),
+        ("T_raw", ctypes.c_int32),
+        ("first_row", ctypes.c_int32),
+        ("n_new", ctypes.c_int32),
+        ("out", ctypes.POINTER(CCache)),
+        ("inv_freq", ctypes.c_void_p),
+        ("rope_dim", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -61,6 +78,7 @@ _PC = ctypes.POINTER(CCache)
 
 _SIGS = {
     "csa_compress": (_i32, [_vp, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _PC, _vp, _i32, _vp]),
+    "csa_compress_batch": (_i32, [ctypes.POINTER(CCompressCall), _i32, _vp]),
     "csa_index_topk": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _PC, _i32, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "csa_attend": (_i32, [_vp, _vp, _i32, _i32, _i32, _PC, _vp, _i32, _PC, _i32, _vp, _vp, _i32, _f32,
@@ -164,6 +182,25 @@ def compress(kv: torch.Tensor, logits: Optional[torch.Tensor], out: Cache, first
     rc = load().csa_compress(kv.data_ptr(), _ptr(logits), kv.stride(1), kv.stride(0), B, T, first_row, n_new,
                              ctypes.byref(c), _ptr(inv_freq), rope_dim, _stream(stream))
     _check("csa_compress", rc)
+
+
+def compress_batch(calls, stream=None):
+    """csa_compress_batch: calls = [(kv, logits, out, first_row, n_new, inv_freq, rope_dim), ...],
+    each as for compress(); one launch when every call is small."""
+    n = len(calls)
+    arr = (CCompressCall * max(n, 1))()
+    keep = []
+    for i, (kv, logits, out, first_row, n_new, inv_freq, rope_dim) in enumerate(calls):
+        assert kv.dtype == torch.bfloat16 and kv.stride(-1) == 1
+        if logits is not None:
+            assert logits.dtype == torch.bfloat16 and logits.stride() == kv.stride()
+        c = out.struct()
+        keep.append(c)
+        B, T, _ = kv.shape
+        arr[i] = CCompressCall(kv.data_ptr(), _ptr(logits), kv.stride(1), kv.stride(0), B, T, first_row, n_new,
+                               ctypes.pointer(c), _ptr(inv_freq), rope_dim)
+    rc = load().csa_compress_batch(arr, n, _stream(stream))
+    _check("csa_compress_batch", rc)
 
 
 def index_topk_workspace_bytes(B, Tq, Hi, cap, topk) -> int:

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "internal.hpp"
 
@@ -70,13 +71,20 @@ const char* csa_last_error(void) { return g_err.c_str(); }
 
 int csa_abi_version(void) { return 1; }
 
-int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_seq, int B, int T_raw,
-                 int first_row, int n_new, const csa_cache_t* out, const double* inv_freq, int rope_dim,
-                 hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks one csa_compress call and fills its launch arguments; `empty` when there is nothing
+// to do (B == 0 or n_new == 0).
+int compress_args(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_seq, int B, int T_raw,
+                  int first_row, int n_new, const csa_cache_t* out, const double* inv_freq, int rope_dim,
+                  csa::CompressArgs& a, bool& empty) {
+  empty = true;
   int rc = check_cache(out, "out", false);
   if (rc) return rc;
   REQUIRE(B >= 0 && n_new >= 0, CSA_EINVAL, "B and n_new must be >= 0 (got %d, %d)", B, n_new);
-  if (B == 0 || n_new == 0) return ok();
+  if (B == 0 || n_new == 0) return CSA_OK;
   REQUIRE(kv != nullptr, CSA_EINVAL, "kv is NULL");
   REQUIRE(logits != nullptr || out->window == 1, CSA_EINVAL, "logits is NULL (allowed only when window == 1)");
   const int C = out->C;
@@ -99,7 +107,7 @@ int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_
   }
   rc = check_rope(inv_freq, rope_dim, C);
   if (rc) return rc;
-  csa::CompressArgs a{};
+  a = csa::CompressArgs{};
   a.kv = kv;
   a.logits = out->window == 1 ? nullptr : logits;
   a.ld_tok = ld_tok;
@@ -119,7 +127,46 @@ int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_
   a.stride = out->stride;
   a.inv_freq = inv_freq;
   a.rope_dim = rope_dim;
+  empty = false;
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_seq, int B, int T_raw,
+                 int first_row, int n_new, const csa_cache_t* out, const double* inv_freq, int rope_dim,
+                 hipStream_t stream) {
+  csa::CompressArgs a;
+  bool empty;
+  const int rc = compress_args(kv, logits, ld_tok, ld_seq, B, T_raw, first_row, n_new, out, inv_freq, rope_dim,
+                               a, empty);
+  if (rc) return rc;
+  if (empty) return ok();
   hipError_t e = csa::launch_compress(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "compress launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int csa_compress_batch(const csa_compress_call_t* calls, int n_calls, hipStream_t stream) {
+  REQUIRE(n_calls >= 0, CSA_EINVAL, "n_calls must be >= 0 (got %d)", n_calls);
+  REQUIRE(n_calls == 0 || calls != nullptr, CSA_EINVAL, "calls is NULL");
+  std::vector<csa::CompressArgs> todo;
+  for (int i = 0; i < n_calls; ++i) {
+    const csa_compress_call_t& c = calls[i];
+    csa::CompressArgs a;
+    bool empty;
+    const int rc = compress_args(c.kv, c.logits, c.ld_tok, c.ld_seq, c.B, c.T_raw, c.first_row, c.n_new, c.out,
+                                 c.inv_freq, c.rope_dim, a, empty);
+    if (rc) {
+      g_err = "call " + std::to_string(i) + ": " + g_err;
+      return rc;
+    }
+    if (!empty) todo.push_back(a);
+  }
+  if (todo.empty()) return ok();
+  hipError_t e = csa::launch_compress_batch(todo.data(), (int)todo.size(), stream);
   REQUIRE(e == hipSuccess, CSA_EHIP, "compress launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -245,12 +245,12 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
 constexpr int kSplitGroups = 16;
 constexpr int kSliceC = 128;
 
-__global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
+// One block of the split layout: row i of sequence b, channel slice z.
+__device__ __forceinline__ void compress_split_block(const CompressArgs& a, int i, int b, int z) {
   __shared__ float sm_m[kSplitGroups][kSliceC], sm_s[kSplitGroups][kSliceC], sm_v[kSplitGroups][kSliceC];
   const int li = threadIdx.x & 15, g = threadIdx.x >> 4;
-  const int i = blockIdx.x, b = blockIdx.y;
   const int cs = li * 8;                                    // channel within the slice
-  const int c0 = blockIdx.z * kSliceC + cs;
+  const int c0 = z * kSliceC + cs;
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
   const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
                                 : nullptr;
@@ -293,12 +293,73 @@ __global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
   finish_row(q, a, ri, b, a.first_row + i, c0);
 }
 
+__global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
+  compress_split_block(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Several calls in one launch (a step's new entries and its raw-window write): block L
+// belongs to call c when start[c] <= L < start[c + 1], and within it to (row, sequence,
+// slice) in that order of significance.  The call is selected by a uniform branch so that
+// its arguments stay in scalar registers.
+constexpr int kBatchMax = 4;
+struct CompressBatch {
+  CompressArgs a[kBatchMax];
+  int start[kBatchMax + 1];
+  int n;
+};
+__global__ void __launch_bounds__(256) k_compress_split_batch(CompressBatch bt) {
+  const int L = blockIdx.x;
+  int c = 0;
+  while (c + 1 < bt.n && L >= bt.start[c + 1]) ++c;
+  auto run = [&](const CompressArgs& a) {
+    const int r = L - bt.start[c];
+    const int nz = a.C / kSliceC;
+    const int z = r % nz, rb = r / nz;
+    compress_split_block(a, rb / a.B, rb % a.B, z);
+  };
+  switch (c) {
+    case 0: run(bt.a[0]); break;
+    case 1: run(bt.a[1]); break;
+    case 2: run(bt.a[2]); break;
+    default: run(bt.a[3]); break;
+  }
+}
+
+// Calls that the split layout serves: 128-channel slices, and either long windows or few
+// rows (every token of a row then loads in parallel).
+static bool split_layout(const CompressArgs& a, bool any_window) {
+  const long long rows = (long long)a.n_new * a.B;
+  const bool split_ok = a.C % kSliceC == 0 && (a.dtype == CSA_BF16 || a.scale_block <= kSliceC);
+  return split_ok && (a.window >= 2 * kSplitGroups || ((any_window || a.window >= 4) && rows <= 512));
+}
+
+hipError_t launch_compress_batch(const CompressArgs* a, int n, hipStream_t s) {
+  bool fuse = n >= 2 && n <= kBatchMax;
+  for (int i = 0; fuse && i < n; ++i) fuse = split_layout(a[i], true) && a[i].n_new > 0 && a[i].B > 0;
+  if (!fuse) {
+    for (int i = 0; i < n; ++i) {
+      const hipError_t e = launch_compress(a[i], s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  CompressBatch bt{};
+  bt.n = n;
+  long long total = 0;
+  for (int i = 0; i < n; ++i) {
+    bt.a[i] = a[i];
+    bt.start[i] = (int)total;
+    total += (long long)a[i].n_new * a[i].B * (a[i].C / kSliceC);
+  }
+  bt.start[n] = (int)total;
+  hipLaunchKernelGGL(k_compress_split_batch, dim3((unsigned)total), dim3(256), 0, s, bt);
+  return hipGetLastError();
+}
+
 hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   CompressArgs a = a0;
   // long windows, or few rows (a decode step): every token of a row loads in parallel
-  const long long rows = (long long)a.n_new * a.B;
-  const bool split_ok = a.C % kSliceC == 0 && (a.dtype == CSA_BF16 || a.scale_block <= kSliceC);
-  if (split_ok && (a.window >= 2 * kSplitGroups || (a.window >= 4 && rows <= 512))) {
+  if (split_layout(a, false)) {
     if (a.n_new == 0 || a.B == 0) return hipSuccess;
     dim3 grid(a.n_new, a.B, a.C / kSliceC);
     hipLaunchKernelGGL(k_compress_split, grid, dim3(256), 0, s, a);

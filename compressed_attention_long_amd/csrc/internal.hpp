@@ -20,6 +20,8 @@ struct CompressArgs {
   int run;   // rows per lane group (set by the launcher)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+// several compress calls: one launch when all are small, else one launch each
+hipError_t launch_compress_batch(const CompressArgs* a, int n, hipStream_t s);
 
 struct IndexArgs {
   const void* q_idx;      // bf16 [rows, Hi, Di]

@@ -65,12 +65,13 @@ class LayerStep:
         self.new_raw = self.kv_raw[:, self.kv_raw.shape[1] - meta["new_tok"]:]
 
     def compress(self, stream=None):
+        """The completed entries and the raw-window write, in one batched call."""
         m = self.meta
+        calls = []
         if m["n_new_entries"] > 0:
-            ops.compress(self.kv_raw, self.z_raw, self.kv, m["E_pre"], m["n_new_entries"], self.inv_freq,
-                         self.wl.R, stream)
-        ops.compress(self.new_raw, None, self.win, m["win_first_new"], m["new_tok"], self.inv_freq, self.wl.R,
-                     stream)
+            calls.append((self.kv_raw, self.z_raw, self.kv, m["E_pre"], m["n_new_entries"], self.inv_freq, self.wl.R))
+        calls.append((self.new_raw, None, self.win, m["win_first_new"], m["new_tok"], self.inv_freq, self.wl.R))
+        ops.compress_batch(calls, stream)
 
     def index(self, stream=None):
         wl = self.wl

@@ -125,6 +125,34 @@ int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_
                  const double* inv_freq, int rope_dim, hipStream_t stream);
 
 /*
+ * csa_compress_batch — several csa_compress calls in one go.
+ *
+ * Source: as csa_compress.  A step of one layer compresses twice from the same
+ * raw tokens: the entries its tokens complete (CSA/HCA rows of "DeepSeek-V4-Pro
+ * vs Inkling") and the new raw tokens of the sliding window (window == stride
+ * == 1).  The result is that of calling csa_compress with the fields of
+ * calls[0], calls[1], ... in order; calls must not write the same rows of one
+ * cache.  Every call is checked before anything is launched (the first failing
+ * call's error is reported, prefixed with its position).  When every call is
+ * small (at most 512 rows of rows x sequences, or windows of at least 32
+ * tokens) and there are at most 4 of them, they run as a single kernel launch;
+ * otherwise each runs as csa_compress would.
+ *
+ *   calls    host array of n_calls descriptors (read before the call returns).
+ */
+typedef struct {
+  const void* kv;
+  const void* logits;
+  int64_t ld_tok, ld_seq;
+  int B, T_raw, first_row, n_new;
+  const csa_cache_t* out;
+  const double* inv_freq;
+  int rope_dim;
+} csa_compress_call_t;
+
+int csa_compress_batch(const csa_compress_call_t* calls, int n_calls, hipStream_t stream);
+
+/*
  * csa_index_topk — lightning-indexer scores and top-k selection.
  *
  * Source: CSA row of "DeepSeek-V4-Pro vs Inkling" (64 indexer heads of dim
@@ -151,7 +179,7 @@ int csa_compress(const void* kv, const void* logits, int64_t ld_tok, int64_t ld_
  *              the scores when scores_out is NULL, and for rows longer than 16384
  *              entries the candidate lists of a two-stage selection (the top k of
  *              each chunk of the row, then the top k of those).
- * Requires Hi % 16 == 0 (Hi <= 64), 16-byte aligned q_idx and key rows.
+ * Requires 1 <= Hi <= 64, 16-byte aligned q_idx and key rows.
  */
 int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos,
                    int B, int Tq, int Hi, const csa_cache_t* keys, int topk,

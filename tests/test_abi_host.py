@@ -64,6 +64,20 @@ def test_compress_validation():
     assert rc == L.CSA_OK and msg == ""
 
 
+def test_compress_batch_validation():
+    lib = L.load()
+    c = cache()
+    empty = L.CCompressCall(FAKE, FAKE, 512, 512 * 64, 1, 64, 0, 0, ctypes.pointer(c), FAKE, 64)
+    bad = L.CCompressCall(None, FAKE, 512, 512 * 64, 1, 64, 0, 4, ctypes.pointer(c), FAKE, 64)
+    arr = (L.CCompressCall * 2)(empty, bad)
+    rc, msg = rc_msg(lib.csa_compress_batch(arr, 2, None))
+    assert rc == L.CSA_EINVAL and msg.startswith("call 1:") and "kv" in msg
+    assert rc_msg(lib.csa_compress_batch(arr, 1, None)) == (L.CSA_OK, "")   # only empty calls: no launch
+    assert lib.csa_compress_batch(None, 0, None) == L.CSA_OK
+    assert lib.csa_compress_batch(None, 1, None) == L.CSA_EINVAL
+    assert lib.csa_compress_batch(arr, -1, None) == L.CSA_EINVAL
+
+
 def index(keys, topk=16, B=1, Tq=1, Hi=64, ws=None, wsb=0, scores=None, q=FAKE):
     lib = L.load()
     return rc_msg(lib.csa_index_topk(q, FAKE, FAKE, B, Tq, Hi, ctypes.byref(keys), topk, FAKE, scores, ws, wsb, None))

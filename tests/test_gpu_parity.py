@@ -91,6 +91,48 @@ def test_compress_parity(window, stride, dtype, B, n_new, first, R):
             assert torch.all(out[b, :first] == 0xAA) and torch.all(out[b, first + n_new:] == 0xAA)
 
 
+@pytest.mark.parametrize("window,stride,dtype,B,n_ent,n_win", [
+    (8, 4, "bf16", 32, 1, 1),         # CSA decode step: one entry and one window row, one launch
+    (128, 128, "bf16", 16, 1, 1),     # HCA decode step
+    (8, 4, "fp8", 4, 1, 4),           # fp8 entries, four window rows
+    (8, 4, "bf16", 1, 1024, 4096),    # prefill chunk: too many rows for one launch (a launch per call)
+])
+def test_compress_batch_equals_separate_calls(window, stride, dtype, B, n_ent, n_win):
+    """csa_compress_batch writes exactly what the same csa_compress calls write one by one."""
+    d = ci.Draw(700 + n_ent + window, "cpu")
+    T = (n_ent - 1) * stride + window
+    kv = d.normal((B, T, 512)).to(DEV)
+    z = d.normal((B, T, 512)).to(DEV)
+    new = kv[:, T - n_win:]
+    pos0 = torch.tensor([5 + 1000 * b for b in range(B)], dtype=torch.int64, device=DEV)
+    first_e, first_w = 3, 128
+    cap_e, cap_w = first_e + n_ent + 1, first_w + n_win
+
+    def caches():
+        if dtype == "bf16":
+            e = ops.Cache(torch.zeros((B, cap_e, 512), dtype=torch.bfloat16, device=DEV),
+                          torch.full((B,), cap_e, dtype=torch.int32, device=DEV), pos0, window, stride)
+        else:
+            e = ops.Cache(torch.zeros((B, cap_e, 512), dtype=torch.uint8, device=DEV),
+                          torch.full((B,), cap_e, dtype=torch.int32, device=DEV), pos0, window, stride,
+                          scales=torch.zeros((B, cap_e, 8), dtype=torch.float32, device=DEV), scale_block=64)
+        w = ops.Cache(torch.zeros((B, cap_w, 512), dtype=torch.bfloat16, device=DEV),
+                      torch.full((B,), cap_w, dtype=torch.int32, device=DEV), pos0 + 7, 1, 1)
+        return e, w
+
+    fg, _ = inv_freq_pair(64)
+    e1, w1 = caches()
+    ops.compress(kv, z, e1, first_e, n_ent, fg, 64)
+    ops.compress(new, None, w1, first_w, n_win, fg, 64)
+    e2, w2 = caches()
+    ops.compress_batch([(kv, z, e2, first_e, n_ent, fg, 64), (new, None, w2, first_w, n_win, fg, 64)])
+    torch.cuda.synchronize()
+    assert torch.equal(e1.data, e2.data) and torch.equal(w1.data, w2.data)
+    if dtype == "fp8":
+        assert torch.equal(e1.scales, e2.scales)
+    assert torch.count_nonzero(w2.data[:, first_w:].view(torch.int16)) > 0
+
+
 # ---------------------------------------------------------------- indexer + top-k
 
 def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
