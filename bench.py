@@ -197,9 +197,9 @@ def compressor_bulk(torch, reps=3):
     (4 of the 16 sequences of the HCA decode batch; the per-sequence work is identical)."""
     import math as _m
     from compressed_attention_long_amd import _lib as ops
-    from compressed_attention_long_amd.step import rope_inv_freq
+    from compressed_attention_long_amd.rope import yarn_inv_freq
     dev = "cuda"
-    inv = rope_inv_freq(160000.0, 64, dev)
+    inv = yarn_inv_freq(160000.0, 64, 16.0, 65536, dev)   # the model's table
     g = torch.Generator(device=dev)
     g.manual_seed(4242)
     blk = 65536
@@ -307,7 +307,12 @@ def cpu_baseline(wl, budget_s=12.0):
     except Exception:
         cores = os.cpu_count() or 1
     t, meta = ci.step_tensors(wl, "cpu")
-    f = O.rope_inv_freq(160000.0, wl.R)
+    if wl.yarn_factor > 1.0:
+        f = O.yarn_inv_freq(160000.0, wl.R, wl.yarn_factor, wl.yarn_base_len)
+        scale = O.yarn_logit_scale(wl.yarn_factor) / math.sqrt(wl.D)
+    else:
+        f = O.rope_inv_freq(160000.0, wl.R)
+        scale = 1 / math.sqrt(wl.D)
     E = wl.E
     ent_pos = O.entry_positions(wl.pos0, E, wl.window, wl.stride)
     win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
@@ -329,10 +334,10 @@ def cpu_baseline(wl, budget_s=12.0):
                 t["k_idx"][b].numpy(), t["k_idx_scale"][b].numpy(), wl.Di)
             O.csa_query(t["q"][b, 0].double().numpy(), qp, t["q_idx"][b, 0].double().numpy(),
                         t["w"][b, 0].double().numpy(), kv, ent_pos, keys, win, win_pos, t["sink"].double().numpy(),
-                        wl.topk, 1 / math.sqrt(wl.D), f, wl.W)
+                        wl.topk, scale, f, wl.W)
         else:
             O.hca_query(t["q"][b, 0].double().numpy(), qp, kv, ent_pos, win, win_pos, t["sink"].double().numpy(),
-                        1 / math.sqrt(wl.D), f, wl.W)
+                        scale, f, wl.W)
         n_done += 1
     dt = time.perf_counter() - t0
     return {"value": n_done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",

@@ -19,12 +19,7 @@ import numpy as np
 import torch
 
 from . import _lib as ops
-
-
-def rope_inv_freq(theta: float, rope_dim: int, device) -> torch.Tensor:
-    """theta ** (-2i / rope_dim) for i < rope_dim / 2, fp64 (base 160,000 on the pages)."""
-    i = np.arange(rope_dim // 2, dtype=np.float64)
-    return torch.from_numpy(np.power(theta, -2.0 * i / rope_dim)).to(device)
+from .rope import rope_inv_freq, yarn_inv_freq, yarn_logit_scale
 
 
 class LayerStep:
@@ -38,8 +33,14 @@ class LayerStep:
         dev = tensors["q"].device
         self.device = dev
         B = wl.B
-        self.inv_freq = rope_inv_freq(theta, wl.R, dev)
-        self.scale = 1.0 / math.sqrt(wl.D) if softmax_scale is None else softmax_scale
+        if wl.yarn_factor > 1.0:
+            # the model's table: YaRN over the base context, with its attention temperature
+            self.inv_freq = yarn_inv_freq(theta, wl.R, wl.yarn_factor, wl.yarn_base_len, dev)
+            default_scale = yarn_logit_scale(wl.yarn_factor) / math.sqrt(wl.D)
+        else:
+            self.inv_freq = rope_inv_freq(theta, wl.R, dev)
+            default_scale = 1.0 / math.sqrt(wl.D)
+        self.scale = default_scale if softmax_scale is None else softmax_scale
         kv = tensors["kv_cache"]
         self.kv = ops.Cache(kv, tensors["kv_n_valid"], tensors["kv_pos0"], wl.window, wl.stride,
                             scales=tensors.get("kv_cache_scale"),

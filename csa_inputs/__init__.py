@@ -61,6 +61,8 @@ class Workload:
     idx_dtype: str = "bf16"   # indexer key storage: "bf16" | "fp8" (one scale per key)
     pos0: int = 1             # position of raw token 0
     compress_each_step: bool = True
+    yarn_factor: float = 1.0  # rotary table: YaRN factor over yarn_base_len (1: plain table)
+    yarn_base_len: int = 65536
 
     @property
     def window(self) -> int:
@@ -86,16 +88,18 @@ class Workload:
         return self.pos0 + self.N - 1
 
 
-# The five workloads: a tiny parity case and the four page-shaped throughput cases.
+# The five workloads: a tiny parity case and the four page-shaped throughput cases.  The
+# page-shaped ones use the model's rotary table (YaRN factor 16 over 65,536 tokens: DeepSeek-V4-Pro
+# vs Inkling, partial-RoPE row); the tiny case states plain partial RoPE with base 160,000.
 WORKLOADS = {
     "tiny_csa_decode": Workload("tiny_csa_decode", "csa", B=1, N=4096, H=8, topk=256, Hi=8),
     "v4pro_csa_decode_65k": Workload("v4pro_csa_decode_65k", "csa", B=32, N=65536, H=128,
-                                     idx_dtype="fp8"),
-    "v4pro_hca_decode_1m": Workload("v4pro_hca_decode_1m", "hca", B=16, N=1048576, H=128),
+                                     idx_dtype="fp8", yarn_factor=16.0),
+    "v4pro_hca_decode_1m": Workload("v4pro_hca_decode_1m", "hca", B=16, N=1048576, H=128, yarn_factor=16.0),
     "v4pro_csa_prefill_4k_on_131k": Workload("v4pro_csa_prefill_4k_on_131k", "csa", B=1,
-                                             N=131072 + 4096, H=128, Tq=4096),
+                                             N=131072 + 4096, H=128, Tq=4096, yarn_factor=16.0),
     "v4flash_csa_decode_1m_fp8": Workload("v4flash_csa_decode_1m_fp8", "csa", B=4, N=1048576,
-                                          H=64, kv_dtype="fp8", idx_dtype="fp8"),
+                                          H=64, kv_dtype="fp8", idx_dtype="fp8", yarn_factor=16.0),
 }
 
 

@@ -35,8 +35,10 @@ Readings where the pages are silent are listed beside the function that takes
 them (pairing of rotated dims, position of an entry, window edge, tie order,
 fp8 format).  Parity unpinned against the pages: the entry position (last raw
 token), the adjacent pairing of rotated dims, the default softmax scale
-1/sqrt(512), one indexer key per entry shared by all indexer heads, and the
-window edge (p - 128, p].  The tests pin each of these conventions as written,
+1/sqrt(512), one indexer key per entry shared by all indexer heads, the window
+edge (p - 128, p], and the YaRN ramp limits (1 and 32 turns) and temperature
+(0.1 ln s + 1), which the pages leave to the published method.  The tests pin each of
+these conventions as written,
 but no value on the pages fixes them.  All floating point is fp64 except where a reading says that a
 quantisation decision is taken in fp32 (the kernel's precision).
 """
@@ -151,6 +153,41 @@ def rope_inv_freq(theta=ROPE_THETA, rope_dim=ROPE_DIM):
     """
     i = np.arange(rope_dim // 2, dtype=np.float64)
     return np.power(np.float64(theta), -2.0 * i / rope_dim)
+
+
+def yarn_inv_freq(theta=ROPE_THETA, rope_dim=ROPE_DIM, factor=16.0, base_len=65536, alpha=1.0, beta=32.0):
+    """YaRN frequencies for positions past the base context (fp64).
+
+    The pages state YaRN with factor 16 over a 65,536-token base, base 160,000, up to
+    1,048,576 positions ("DeepSeek-V4-Pro vs Inkling", Component-by-component table,
+    partial-RoPE row).  Everything else is the YaRN method as published ("NTK-by-parts"):
+    pair i has wavelength 2*pi/f_i and turns r_i = base_len / wavelength times over the
+    base context; with ramp g = 0 below alpha turns, 1 above beta turns and linear in
+    between, the new frequency is (1 - g) * f_i / factor + g * f_i.  Reading (parity
+    unpinned): alpha = 1 and beta = 32, the values the method recommends; no page gives them.
+    """
+    out = np.empty(rope_dim // 2, dtype=np.float64)
+    for i in range(rope_dim // 2):
+        f = np.float64(theta) ** (-2.0 * i / rope_dim)
+        wavelength = 2.0 * np.pi / f
+        turns = base_len / wavelength
+        if turns < alpha:
+            g = 0.0
+        elif turns > beta:
+            g = 1.0
+        else:
+            g = (turns - alpha) / (beta - alpha)
+        out[i] = (1.0 - g) * f / factor + g * f
+    return out
+
+
+def yarn_logit_scale(factor=16.0):
+    """YaRN attention temperature as a multiplier of the logits: sqrt(1/t) = 0.1 ln(factor) + 1
+    (the published method; parity unpinned: the pages give only the factor)."""
+    if factor <= 1.0:
+        return 1.0
+    m = 0.1 * np.log(np.float64(factor)) + 1.0
+    return float(m * m)
 
 
 def rope(x, pos, inv_freq):

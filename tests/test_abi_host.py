@@ -139,3 +139,16 @@ def test_workspace_sizes_scale_with_work():
     assert a > 0 and b > 0
     assert L.index_topk_workspace_bytes(32, 1, 64, 16383, 1024) >= 32 * 16383 * 4
     assert L.index_topk_workspace_bytes(4, 1, 64, 262143, 1024) >= 4 * 262143 * 4 + 4 * 32 * 1024 * 8
+
+
+def test_rotary_tables_agree_with_the_oracle():
+    """Host logic: the tables handed to the kernels equal the oracle's own, written separately."""
+    import numpy as np
+    from compressed_attention_long_amd import rope
+    from oracle import csa_oracle as O
+    np.testing.assert_allclose(rope.rope_inv_freq(160000.0, 64, "cpu").numpy(), O.rope_inv_freq(160000.0, 64),
+                               rtol=1e-15, atol=0)
+    np.testing.assert_allclose(rope.yarn_inv_freq(160000.0, 64, 16.0, 65536, "cpu").numpy(),
+                               O.yarn_inv_freq(160000.0, 64, 16.0, 65536), rtol=1e-14, atol=0)
+    assert abs(rope.yarn_logit_scale(16.0) - O.yarn_logit_scale(16.0)) < 1e-15
+    assert rope.yarn_logit_scale(1.0) == 1.0

@@ -19,6 +19,18 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
+def oracle_table(wl):
+    """The oracle's own rotary table for the workload (YaRN for the page-shaped workloads)."""
+    if wl.yarn_factor > 1.0:
+        return O.yarn_inv_freq(160000.0, wl.R, wl.yarn_factor, wl.yarn_base_len)
+    return O.rope_inv_freq(160000.0, wl.R)
+
+
+def oracle_scale(wl):
+    """The oracle's softmax scale: 1/sqrt(512), times the YaRN temperature for YaRN workloads."""
+    return O.yarn_logit_scale(wl.yarn_factor) / np.sqrt(wl.D) if wl.yarn_factor > 1.0 else 1 / np.sqrt(wl.D)
+
+
 def run_step(name):
     wl = ci.WORKLOADS[name]
     print(f"\n[gpu case] full-size step {name}", flush=True)
@@ -30,7 +42,7 @@ def run_step(name):
 
 
 def check_rows(wl, t, meta, step, samples):
-    fo = O.rope_inv_freq(160000.0, wl.R)
+    fo = oracle_table(wl)
     kv_block = wl.kv_scale_block
     ent_pos_all = O.entry_positions(wl.pos0, wl.E, wl.window, wl.stride)
     win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
@@ -54,14 +66,14 @@ def check_rows(wl, t, meta, step, samples):
         else:
             kv_rows = stored_rows(step.kv.data[b], sc_b, kv_block)
             X = oracle_rows_hca(kv_rows, ent_pos_all, win_rows, win_pos, qp, wl.W)
-        o, l = O.attend(np64(t["q"][b, tq]), qp, X, sink, step.scale, fo)
+        o, l = O.attend(np64(t["q"][b, tq]), qp, X, sink, oracle_scale(wl), fo)
         check_attention(np64(step.out[b, tq]), o, f"{wl.name} b={b} t={tq}")
         np.testing.assert_allclose(step.lse[b, tq].cpu().numpy(), l, atol=1e-4)
 
 
 def check_new_entry(wl, t, meta, step, b):
     """The entries this step compressed, against the oracle on the same raw rows."""
-    fo = O.rope_inv_freq(160000.0, wl.R)
+    fo = oracle_table(wl)
     first = meta["E_pre"]
     n = meta["n_new_entries"]
     ent, _ = O.compress(np64(t["kv_raw"][b]), np64(t["z_raw"][b]), wl.window, wl.stride,

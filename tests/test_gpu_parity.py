@@ -13,7 +13,7 @@ import torch
 
 import csa_inputs as ci
 from compressed_attention_long_amd import _lib as ops
-from compressed_attention_long_amd.step import rope_inv_freq
+from compressed_attention_long_amd.rope import rope_inv_freq, yarn_inv_freq
 from oracle import csa_oracle as O
 
 from gpu_common import (LSE_TOL, check_attention, check_bf16_rows, check_scores, check_topk, np64,
@@ -30,7 +30,10 @@ def _announce(request):
     torch.cuda.synchronize()
 
 
-def inv_freq_pair(R=64):
+def inv_freq_pair(R=64, yarn=False):
+    """(table for the kernels, the oracle's own table): plain base 160,000, or YaRN 16 over 65,536."""
+    if yarn:
+        return yarn_inv_freq(160000.0, R, 16.0, 65536, DEV), O.yarn_inv_freq(160000.0, R, 16.0, 65536)
     return rope_inv_freq(160000.0, R, DEV), O.rope_inv_freq(160000.0, R)
 
 
@@ -45,8 +48,14 @@ def inv_freq_pair(R=64):
     (8, 4, "fp8", 2, 333, 0, 64),        # fp8 cache, per-64 scales
     (128, 128, "fp8", 1, 5, 2, 64),
     (8, 4, "bf16", 1, 50, 0, 0),         # no rotation
+    (8, 4, "bf16", 2, 37, 3, "yarn"),    # the model's table (YaRN 16 over 65,536), positions near 1M
+    (128, 128, "fp8", 2, 5, 0, "yarn"),
+    (1, 1, "bf16", 2, 60, 1, "yarn"),
 ])
 def test_compress_parity(window, stride, dtype, B, n_new, first, R):
+    yarn = R == "yarn"
+    if yarn:
+        R = 64
     d = ci.Draw(100 + n_new + window, "cpu")
     T = (n_new - 1) * stride + window + 3
     kv = d.normal((B, T, 512))
@@ -66,7 +75,7 @@ def test_compress_parity(window, stride, dtype, B, n_new, first, R):
     sg = scales.to(DEV) if scales is not None else None
     cache = ops.Cache(dg, torch.full((B,), cap, dtype=torch.int32, device=DEV), pos0.to(DEV), window, stride,
                       scales=sg, scale_block=sb if dtype == "fp8" else 0)
-    fg, fo = inv_freq_pair(R) if R else (None, np.zeros(0))
+    fg, fo = inv_freq_pair(R, yarn) if R else (None, np.zeros(0))
     ops.compress(kv.to(DEV), z.to(DEV) if window > 1 else None, cache, first, n_new, fg, R)
     torch.cuda.synchronize()
     out = dg.cpu()
@@ -241,7 +250,7 @@ def test_topk_clustered_scores():
 # ---------------------------------------------------------------- attention
 
 def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, qmul, seed, out_dtype="fp32",
-                 win_start=None, kv_gain=None):
+                 win_start=None, kv_gain=None, pos_base=1, yarn=False):
     d = ci.Draw(seed, "cpu")
     q = d.normal((B, Tq, H, 512), std=qmul / math.sqrt(512))
     sink = d.normal((H,), dtype=torch.float32)
@@ -258,7 +267,7 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
         kv_ref = np64(kvt)
     if mode == "hca":
         kv.window, kv.stride = 128, 128
-    kv_pos0 = [1 + 1000 * b for b in range(B)]
+    kv_pos0 = [pos_base + 1000 * b for b in range(B)]
     kv.pos0 = torch.tensor(kv_pos0, dtype=torch.int64, device=DEV)
     ent_pos = [O.entry_positions(kv_pos0[b], cap, kv.window, kv.stride) for b in range(B)]
     # query positions: the newest token sits right after the last valid entry (prefill rows step back)
@@ -269,7 +278,7 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     win = ops.Cache(wt.to(DEV), torch.tensor([win_cap] * B, dtype=torch.int32, device=DEV),
                     torch.tensor(wpos0, dtype=torch.int64, device=DEV), 1, 1)
     q_pos = torch.tensor(qp, dtype=torch.int64, device=DEV)
-    fg, fo = inv_freq_pair(64)
+    fg, fo = inv_freq_pair(64, yarn)
     odt = torch.float32 if out_dtype == "fp32" else torch.bfloat16
     out = torch.empty((B, Tq, H, 512), dtype=odt, device=DEV)
     lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
@@ -333,6 +342,18 @@ def test_attend_scores_far_above_first_tile(mode):
     gain = np.where(np.arange(cap) < 400, 0.01, 3.0)
     topk = 1024 if mode == "csa" else 0
     _attend_case(mode, 1, 1, 128, cap, [cap], False, topk, 128, 129, 1.0, 8.0, seed=31, kv_gain=gain)
+
+
+@pytest.mark.parametrize("mode,cap,n_valid,topk", [
+    ("csa", 3000, [3000, 2500], 1024),
+    ("hca", 300, [300, 280], 0),
+])
+def test_attend_parity_yarn_near_1m(mode, cap, n_valid, topk):
+    """The model's rotary table (YaRN 16 over 65,536) and temperature, with queries near position 1,048,576."""
+    scale = O.yarn_logit_scale(16.0) / math.sqrt(512)
+    pos_base = 1048576 - cap * (4 if mode == "csa" else 128) - 2000
+    _attend_case(mode, 2, 1, 128, cap, n_valid, False, topk, 128, 129, scale, 1.0, seed=61, pos_base=pos_base,
+                 yarn=True)
 
 
 def test_attend_window_cut_by_stream_start():

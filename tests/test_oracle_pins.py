@@ -384,3 +384,58 @@ def test_bf16_round_matches_library():
     # exact ties go to the even neighbour
     assert O.bf16_round(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
     assert O.bf16_round(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+
+
+# ---------------------------------------------------------------- YaRN table (partial-RoPE row: factor 16 over 65,536)
+
+def test_yarn_factor_one_is_the_plain_table():
+    # (1 - g) f + g f on the ramp pairs: equal to f up to one rounding
+    np.testing.assert_allclose(O.yarn_inv_freq(160000.0, 64, factor=1.0, base_len=65536),
+                               O.rope_inv_freq(160000.0, 64), rtol=4e-16, atol=0)
+
+
+def test_yarn_regimes_follow_the_wavelengths():
+    # a pair keeps its frequency when it turns more than 32 times over the base context and is
+    # divided by the factor when it turns less than once; solving base_len * theta^(-2i/64) / (2 pi)
+    # = turns for i gives the two index limits without the ramp formula
+    theta, d, L, s = 160000.0, 64, 65536, 16.0
+    f = O.rope_inv_freq(theta, d)
+    y = O.yarn_inv_freq(theta, d, factor=s, base_len=L)
+    i_keep = (d / 2) * math.log(L / (2 * math.pi * 32)) / math.log(theta)    # turns == 32
+    i_interp = (d / 2) * math.log(L / (2 * math.pi)) / math.log(theta)       # turns == 1
+    assert 10 < i_keep < i_interp < 31                                        # all three regimes occur
+    for i in range(d // 2):
+        if i < i_keep:
+            assert y[i] == f[i]
+        elif i > i_interp:
+            assert y[i] == f[i] / s
+        else:
+            assert f[i] / s < y[i] < f[i]
+
+
+def test_yarn_interpolated_pairs_map_the_longest_context_onto_the_base():
+    # at the largest position (1,048,576 = 16 x 65,536) an interpolated pair turns exactly as far as
+    # the plain table does at the end of the base context
+    f = O.rope_inv_freq(160000.0, 64)
+    y = O.yarn_inv_freq(160000.0, 64, factor=16.0, base_len=65536)
+    slow = np.where(65536 * f / (2 * math.pi) < 1.0)[0]
+    assert len(slow) > 0
+    np.testing.assert_array_equal(1048576 * y[slow], 65536 * f[slow])
+
+
+def test_yarn_table_is_monotone_and_between_the_limits():
+    f = O.rope_inv_freq(160000.0, 64)
+    y = O.yarn_inv_freq(160000.0, 64, factor=16.0, base_len=65536)
+    assert np.all(np.diff(y) < 0)
+    assert np.all(y <= f) and np.all(y >= f / 16.0)
+
+
+def test_yarn_temperature_laws():
+    # sqrt(scale) - 1 is proportional to ln(factor): no temperature at factor 1, and squaring the
+    # factor doubles the excess
+    assert O.yarn_logit_scale(1.0) == 1.0
+    for s in (2.0, 4.0, 16.0):
+        a = math.sqrt(O.yarn_logit_scale(s)) - 1.0
+        b = math.sqrt(O.yarn_logit_scale(s * s)) - 1.0
+        assert a > 0 and abs(b - 2 * a) < 1e-12
+    assert O.yarn_logit_scale(16.0) > O.yarn_logit_scale(4.0)
