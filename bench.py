@@ -189,6 +189,38 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     return out
 
 
+def time_reuse(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30):
+    """Reuse layers (CSA2: KV and top-k selection computed in one layer and reused by others):
+    one csa_attend per layer with the layer's own queries and sink over a computed layer's
+    caches and selection.  Replayed from one HIP graph chaining the reuse layers of the rotated
+    computed layers; returns ms per reuse-layer step."""
+    import csa_inputs as ci
+    from compressed_attention_long_amd.step import ReuseStep
+    n_layers = max(2, min(30, math.ceil(min_cache_bytes / max(layer_bytes(wl), 1))))
+    layers = build_layers(wl, n_layers, "cuda", torch, torch.bfloat16)
+    for L in layers:
+        L.run()                       # the computed layers' caches and selections
+    reuse = []
+    for i, L in enumerate(layers):
+        r = ci.reuse_tensors(wl, "cuda", seed=ci.seed_for(wl.name) + 31337 * (i + 1))
+        reuse.append(ReuseStep(L, r["q"], r["sink"]))
+    for i in range(warmup):
+        reuse[i % n_layers].run()
+    torch.cuda.synchronize()
+    chain = capture_chain(reuse, torch)
+    chain.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps_n // n_layers)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        chain.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / (reps * n_layers)
+    del chain, reuse, layers
+    torch.cuda.empty_cache()
+    return ms
+
+
 def compressor_bulk(torch, reps=3):
     """csa_compress over whole raw streams (the compressor's HBM benchmark): kv and pooling
     logits read once, entries written once.  Inputs tile one seeded 64K-token random block
@@ -351,7 +383,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v4pro_csa_decode_65k")
-    ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8,v4pro_csa_prefill_4k_on_131k",
+    ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8,v4pro_csa_prefill_4k_on_131k,"
+                                       "v41flash_csa2_decode_1m_fp8",
                     help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compressor-bulk", action="store_true")
@@ -426,6 +459,11 @@ def main():
         if w2.mode == "csa":
             e2["index_ms"] = t2["index"]
             e2["index_GB_per_s"] = c2["index_bytes"] / (t2["index"] * 1e-3) / 1e9
+        if w2.reuse > 0:
+            tr = time_reuse(w2, max(10, args.steps // 2), args.warmup, torch)
+            avg = (t2["wall_ms_per_step"] + w2.reuse * tr) / (1 + w2.reuse)
+            e2.update({"reuse_ms_per_step": tr, "reuse_layers_per_computed": w2.reuse, "layer_avg_ms": avg,
+                       "tokens_per_s_layer_avg": w2.B * w2.Tq / (avg / 1e3)})
         extra[name] = e2
     if not args.no_compressor_bulk:
         print("[bench] compressor over whole raw streams", file=sys.stderr, flush=True)

@@ -93,3 +93,24 @@ class LayerStep:
         if self.wl.mode == "csa":
             self.index(stream)
         self.attend(stream)
+
+
+class ReuseStep:
+    """A layer that reuses a computed layer's KV cache, window and top-k selection and brings
+    only its own queries and sink (the CSA2 "Reuse" layers: KV and the top-512 selection are
+    computed in 3 of 18 layers and reused by the rest; DeepSeek-V4.1-Flash vs Inkling, CSA2
+    encoder layers row).  Its step is one csa_attend call."""
+
+    def __init__(self, full: LayerStep, q: torch.Tensor, sink: torch.Tensor, out_dtype=torch.bfloat16):
+        wl = full.wl
+        assert wl.mode == "csa", "reuse applies to selected-entry (CSA) layers"
+        self.full, self.wl, self.q, self.sink = full, wl, q, sink
+        dev = q.device
+        self.att_ws = ops.workspace(ops.csa_attend_workspace_bytes(wl.B, wl.Tq, wl.H, wl.topk, wl.W), dev)
+        self.out = torch.empty((wl.B, wl.Tq, wl.H, wl.D), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((wl.B, wl.Tq, wl.H), dtype=torch.float32, device=dev)
+
+    def run(self, stream=None):
+        f, wl = self.full, self.wl
+        ops.csa_attend(self.q, f.t["q_pos"], f.kv, f.idx, f.win, wl.W, self.sink, f.inv_freq, wl.R, f.scale,
+                       self.out, self.lse, self.att_ws, stream)

@@ -63,13 +63,20 @@ class Workload:
     compress_each_step: bool = True
     yarn_factor: float = 1.0  # rotary table: YaRN factor over yarn_base_len (1: plain table)
     yarn_base_len: int = 65536
+    pool_window: int = 0      # compression geometry override (0: the mode's own)
+    pool_stride: int = 0
+    reuse: int = 0            # layers that reuse one computed layer's KV and selection (CSA2)
 
     @property
     def window(self) -> int:
+        if self.pool_window:
+            return self.pool_window
         return 8 if self.mode == "csa" else 128
 
     @property
     def stride(self) -> int:
+        if self.pool_stride:
+            return self.pool_stride
         return 4 if self.mode == "csa" else 128
 
     def n_entries(self, n_raw: Optional[int] = None) -> int:
@@ -100,6 +107,12 @@ WORKLOADS = {
                                              N=131072 + 4096, H=128, Tq=4096, yarn_factor=16.0),
     "v4flash_csa_decode_1m_fp8": Workload("v4flash_csa_decode_1m_fp8", "csa", B=4, N=1048576,
                                           H=64, kv_dtype="fp8", idx_dtype="fp8", yarn_factor=16.0),
+    # CSA2 (DeepSeek-V4.1-Flash vs Inkling, CSA2 encoder layers row): entries pool 2 raw tokens,
+    # top-512; KV and selection computed in 3 of 18 layers and reused by the other 15 (5 per
+    # computed layer).  fp8 KV stands in for the page's FP4 cache.
+    "v41flash_csa2_decode_1m_fp8": Workload("v41flash_csa2_decode_1m_fp8", "csa", B=4, N=1048576, H=64,
+                                            topk=512, kv_dtype="fp8", idx_dtype="fp8", yarn_factor=16.0,
+                                            pool_window=2, pool_stride=2, reuse=5),
 }
 
 
@@ -253,3 +266,12 @@ def step_tensors(wl: Workload, device="cpu", seed: Optional[int] = None):
     meta = dict(E=E, E_pre=E_pre, n_new_entries=n_new_entries, raw_first=raw_first, T_raw=T_raw,
                 win_cap=win_cap, win_first_new=wl.W, new_tok=new_tok)
     return t, meta
+
+
+def reuse_tensors(wl: Workload, device="cpu", seed: Optional[int] = None):
+    """The new inputs of a layer that reuses another layer's KV and selection (CSA2 "Reuse"
+    layers): its own queries q [B, Tq, H, D] ~ N(0, 1/D) and sink logits [H] ~ N(0, 1)."""
+    seed = seed_for(wl.name) + 500009 if seed is None else seed
+    d = Draw(seed, device)
+    return {"q": d.normal((wl.B, wl.Tq, wl.H, wl.D), std=1.0 / math.sqrt(wl.D)),
+            "sink": d.normal((wl.H,), dtype=torch.float32)}

@@ -112,3 +112,27 @@ def test_v4pro_csa_prefill_4k_on_131k():
     wl, t, meta, step = run_step("v4pro_csa_prefill_4k_on_131k")
     check_new_entry(wl, t, meta, step, 0)
     check_rows(wl, t, meta, step, [(0, 0), (0, 1), (0, 2047), (0, 4095)])
+
+
+def test_v41flash_csa2_decode_1m_fp8_with_reuse():
+    """CSA2 at 1M: entries pool 2 tokens, top-512 of 524,288, fp8 KV; then a reuse layer (its own
+    queries and sink over the computed layer's KV and selection)."""
+    from compressed_attention_long_amd.step import ReuseStep
+    wl, t, meta, step = run_step("v41flash_csa2_decode_1m_fp8")
+    check_rows(wl, t, meta, step, [(0, 0), (3, 0)])
+    check_new_entry(wl, t, meta, step, 1)
+    r = ci.reuse_tensors(wl, DEV)
+    rs = ReuseStep(step, r["q"], r["sink"], out_dtype=torch.float32)
+    rs.run()
+    torch.cuda.synchronize()
+    fo = oracle_table(wl)
+    win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
+    for b in (0, 2):
+        qp = int(t["q_pos"][b, 0])
+        ig = step.idx[b, 0].cpu().numpy()
+        sel = torch.from_numpy(ig[ig >= 0].astype(np.int64)).to(DEV)
+        kv_sel = stored_rows(step.kv.data[b][sel], step.kv.scales[b][sel], wl.kv_scale_block)
+        X = oracle_rows_csa(kv_sel, np.arange(len(sel)), np64(step.win.data[b]), win_pos, qp, wl.W, len(sel))
+        o, l = O.attend(np64(r["q"][b, 0]), qp, X, np64(r["sink"]), oracle_scale(wl), fo)
+        check_attention(np64(rs.out[b, 0]), o, f"reuse layer b={b}")
+        np.testing.assert_allclose(rs.lse[b, 0].cpu().numpy(), l, atol=1e-4)

@@ -51,6 +51,8 @@ def inv_freq_pair(R=64, yarn=False):
     (8, 4, "bf16", 2, 37, 3, "yarn"),    # the model's table (YaRN 16 over 65,536), positions near 1M
     (128, 128, "fp8", 2, 5, 0, "yarn"),
     (1, 1, "bf16", 2, 60, 1, "yarn"),
+    (2, 2, "bf16", 3, 700, 2, "yarn"),   # CSA2 geometry: 2 tokens per entry, no overlap
+    (2, 2, "fp8", 2, 1, 5, "yarn"),      # CSA2 decode-step entry, fp8
 ])
 def test_compress_parity(window, stride, dtype, B, n_new, first, R):
     yarn = R == "yarn"
@@ -169,6 +171,7 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (2, 1, 64, 70000, [70000, 500], True, 1024, "end"),        # two-stage, 9 chunks; one row with < k visible
     (2, 37, 64, 3000, [3000, 2100], False, 256, "causal"),     # multi-row kernel: ragged row groups, causal
     (1, 16, 40, 1300, [1290], False, 64, "causal"),            # multi-row kernel, heads not a multiple of 16
+    (1, 1, 64, 140000, [140000], True, 512, "end"),            # CSA2 selection: top-512 of a long row (chunked)
 ])
 def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
     d = ci.Draw(200 + cap, "cpu")
@@ -323,6 +326,7 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     ("csa", 2, 3, 64, 900, [900, 40], True, 300, 128, 140, 1 / math.sqrt(512), 1.0),   # fp8 KV, < k visible
     ("csa", 1, 1, 16, 500, [500], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),        # window only
     ("csa", 4, 64, 64, 600, [600] * 4, False, 200, 128, 200, 0.1, 2.0),               # 256 rows: no split
+    ("csa", 4, 1, 64, 6000, [6000, 5000, 512, 100], True, 512, 128, 129, 1 / math.sqrt(512), 4.0),  # CSA2: top-512, fp8
     ("hca", 2, 1, 128, 700, [700, 300], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),
     # fp8 rows are staged in LDS as bf16 (code x scale rounded): sharper softmax than this
     # exceeds the bar (CPU emulation of that rounding: 1.1% at scale 1, 5.8% at scale 1 with q x 4)

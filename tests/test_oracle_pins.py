@@ -40,7 +40,7 @@ def test_oracle_constants_are_the_pages():
 def test_entry_counts_golden():
     g = json.load(open(os.path.join(GOLD, "entry_counts.json")))
     for c in g["cases"]:
-        w, s = (8, 4) if c["mode"] == "csa" else (128, 128)
+        w, s = {"csa": (8, 4), "csa2": (2, 2), "hca": (128, 128)}[c["mode"]]
         assert O.n_entries(c["n_raw"], w, s) == c["entries"], c
         # the vectorised pooling produces exactly that many rows on small streams
         if c["n_raw"] <= 4096:
@@ -269,10 +269,10 @@ def _tiny_stream(seed, T, D=16, H=2, Hi=3, Di=8):
                 sink=r.standard_normal(H))
 
 
-def _csa_from_stream(s, pos0, k, W, scale, f, q_pos=None):
+def _csa_from_stream(s, pos0, k, W, scale, f, q_pos=None, window=8, stride=4):
     T = s["kv"].shape[0]
     q_pos = pos0 + T - 1 if q_pos is None else q_pos
-    ent, ep = O.compress(s["kv"], s["z"], 8, 4, pos0, f)
+    ent, ep = O.compress(s["kv"], s["z"], window, stride, pos0, f)
     win, wp = O.compress(s["kv"], s["z"], 1, 1, pos0, f)
     E = ent.shape[0]
     return O.csa_query(s["q"], q_pos, s["q_idx"], s["w"], ent, ep, s["keys"][:E], win, wp,
@@ -327,6 +327,21 @@ def test_whole_csa_step_matches_brute_force(seed, T, k, W, R, pos0):
                                        list(s["sink"]), k, W, scale, fb)
     assert list(sel) == selb
     np.testing.assert_allclose(sc[:len(scb)], scb, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed,T,k,W", [(24, 16, 3, 4), (25, 33, 4, 5)])
+def test_whole_csa2_step_matches_brute_force(seed, T, k, W):
+    """CSA2 geometry: entries pool 2 raw tokens into 1 (window = stride = 2)."""
+    s = _tiny_stream(seed, T, D=8, H=2)
+    f = O.rope_inv_freq(160000.0, 4)
+    o, lse, sel, sc, vis = _csa_from_stream(s, 3, k, W, 0.6, f, window=2, stride=2)
+    lst = lambda a: [list(map(float, r)) for r in a]
+    ob, lb, selb, scb = brute.csa_step(lst(s["kv"]), lst(s["z"]), 3, lst(s["q"]), 3 + T - 1,
+                                       lst(s["q_idx"]), list(s["w"]), lst(s["keys"]),
+                                       list(s["sink"]), k, W, 0.6, brute.inv_freq(160000.0, 4), 2, 2)
+    assert list(sel) == selb
     np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse, lb, rtol=1e-12)
 
