@@ -107,7 +107,7 @@ def capture_chain(layers, torch):
 
 
 def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layers=30):
-    if wl.Tq > 1:
+    if wl.Tq >= 64:
         max_layers = 2      # prefill: each step's own tensors (q, scores, output) exceed the 256 MB MALL
     """Time `steps_n` steps rotating over distinct layers; return timings (ms).
 
@@ -384,7 +384,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v4pro_csa_decode_65k")
     ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8,v4pro_csa_prefill_4k_on_131k,"
-                                       "v41flash_csa2_decode_1m_fp8",
+                                       "v41flash_csa2_decode_1m_fp8,v4pro_csa_decode_65k_mtp4",
                     help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compressor-bulk", action="store_true")

@@ -107,6 +107,10 @@ WORKLOADS = {
                                              N=131072 + 4096, H=128, Tq=4096, yarn_factor=16.0),
     "v4flash_csa_decode_1m_fp8": Workload("v4flash_csa_decode_1m_fp8", "csa", B=4, N=1048576,
                                           H=64, kv_dtype="fp8", idx_dtype="fp8", yarn_factor=16.0),
+    # multi-token decode: 4 query tokens per sequence (verifying draft tokens, as the MTP and
+    # speculative-decoding components of the pages do) through the same step, causal within the 4
+    "v4pro_csa_decode_65k_mtp4": Workload("v4pro_csa_decode_65k_mtp4", "csa", B=32, N=65536, H=128, Tq=4,
+                                          idx_dtype="fp8", yarn_factor=16.0),
     # CSA2 (DeepSeek-V4.1-Flash vs Inkling, CSA2 encoder layers row): entries pool 2 raw tokens,
     # top-512; KV and selection computed in 3 of 18 layers and reused by the other 15 (5 per
     # computed layer).  fp8 KV stands in for the page's FP4 cache.

@@ -114,6 +114,14 @@ def test_v4pro_csa_prefill_4k_on_131k():
     check_rows(wl, t, meta, step, [(0, 0), (0, 1), (0, 2047), (0, 4095)])
 
 
+def test_v4pro_csa_decode_65k_mtp4():
+    """Four query tokens per sequence (draft verification): each sees entries and window rows
+    up to its own position only."""
+    wl, t, meta, step = run_step("v4pro_csa_decode_65k_mtp4")
+    check_new_entry(wl, t, meta, step, 9)
+    check_rows(wl, t, meta, step, [(0, 0), (0, 3), (21, 1), (31, 2)])
+
+
 def test_v41flash_csa2_decode_1m_fp8_with_reuse():
     """CSA2 at 1M: entries pool 2 tokens, top-512 of 524,288, fp8 KV; then a reuse layer (its own
     queries and sink over the computed layer's KV and selection)."""
