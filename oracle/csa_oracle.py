@@ -37,7 +37,8 @@ fp8 format).  Parity unpinned against the pages: the entry position (last raw
 token), the adjacent pairing of rotated dims, the default softmax scale
 1/sqrt(512), one indexer key per entry shared by all indexer heads, the window
 edge (p - 128, p], and the YaRN ramp limits (1 and 32 turns) and temperature
-(0.1 ln s + 1), which the pages leave to the published method.  The tests pin each of
+(0.1 ln s + 1), which the pages leave to the published method, and the FP4 cache
+format (OCP MXFP4: E2M1 elements, power-of-two scales per 32 channels).  The tests pin each of
 these conventions as written,
 but no value on the pages fixes them.  All floating point is fp64 except where a reading says that a
 quantisation decision is taken in fp32 (the kernel's precision).
@@ -138,6 +139,82 @@ def fp8_block_dequantize(codes, scales, block):
     s = np.repeat(np.asarray(scales, dtype=np.float64), block, axis=-1)
     assert s.shape[-1] == C
     return v * s
+
+
+FP4_E2M1_MAX = 6.0
+MX_BLOCK = 32
+
+
+def fp4_e2m1_decode(codes):
+    """OCP FP4 E2M1 code (low 4 bits) -> fp64 value: sign bit 3, exponent bits 2..1
+    (bias 1), mantissa bit 0; exponent 0 holds 0 and the subnormal 0.5.  The magnitudes are
+    0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c >> 3, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    v = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return sign * v
+
+
+def fp4_e2m1_encode(x):
+    """fp64 -> E2M1 code, round to nearest even, saturating at +-6.
+
+    Reading (FP4 format): the pages name an FP4 KV cache quantized after RoPE
+    ("DeepSeek-V4.1-Flash vs Inkling", partial-RoPE row) and MXFP4 in training; the
+    element format taken is OCP E2M1 with round-to-nearest-even and saturation.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.minimum(np.abs(x), FP4_E2M1_MAX)
+    ulp = np.where(ax < 2.0, 0.5, np.where(ax < 4.0, 1.0, 2.0))   # grid spacing of the binade
+    r = np.minimum(np.rint(ax / ulp) * ulp, FP4_E2M1_MAX)           # rint: ties to even
+    mags = fp4_e2m1_decode(np.arange(8))
+    code = np.argmin(np.abs(r[..., None] - mags), axis=-1).astype(np.int64)   # r is on the grid
+    code = code | np.where(np.signbit(x) & (r != 0), 8, 0)
+    return code.astype(np.uint8)
+
+
+def mxfp4_block_quantize(x, block=MX_BLOCK):
+    """Quantize rows of `x` [..., C] to E2M1 codes with one power-of-two scale per block.
+
+    Reading (FP4 format): OCP MXFP4 blocks of 32 channels; the block's scale is
+    2^(floor(log2(amax)) - 2), which puts the largest magnitude in [4, 8) before rounding
+    (values above 6 saturate); a block of zeros gets scale 1 and codes 0.  As for fp8, the
+    decision is taken in fp32 (x rounded to fp32, amax and the scaling in fp32).  Returns the
+    codes [..., C] (one per byte) and the fp32 scales [..., C / block].
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    C = x32.shape[-1]
+    xb = x32.reshape(x32.shape[:-1] + (C // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    _, ex = np.frexp(amax.astype(np.float64))                      # amax = m * 2^ex, m in [0.5, 1)
+    e = np.clip(ex - 1 - 2, -127, 127)
+    scale = np.where(amax > 0, np.ldexp(np.float32(1.0), e), np.float32(1.0)).astype(np.float32)
+    y = (xb / scale[..., None]).astype(np.float32)                 # exact: division by a power of two
+    codes = fp4_e2m1_encode(y.astype(np.float64))
+    return codes.reshape(x32.shape), scale
+
+
+def mxfp4_block_dequantize(codes, scales, block=MX_BLOCK):
+    """codes [..., C] (one E2M1 code per entry) x scales [..., C/block] -> fp64 values."""
+    v = fp4_e2m1_decode(codes)
+    s = np.repeat(np.asarray(scales, dtype=np.float64), block, axis=-1)
+    assert s.shape[-1] == v.shape[-1]
+    return v * s
+
+
+def fp4_pack(codes):
+    """Two E2M1 codes per byte: channel 2k in the low nibble, 2k + 1 in the high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def fp4_unpack(packed):
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -454,3 +454,58 @@ def test_yarn_temperature_laws():
         b = math.sqrt(O.yarn_logit_scale(s * s)) - 1.0
         assert a > 0 and abs(b - 2 * a) < 1e-12
     assert O.yarn_logit_scale(16.0) > O.yarn_logit_scale(4.0)
+
+
+# ---------------------------------------------------------------- FP4 (MXFP4) cache format
+
+def test_fp4_decode_matches_the_format_table():
+    g = json.load(open(os.path.join(GOLD, "fp4_e2m1.json")))
+    v = O.fp4_e2m1_decode(np.arange(16))
+    np.testing.assert_array_equal(v, np.array(g["values"]))
+    assert np.all(np.signbit(v[8:])) and not np.any(np.signbit(v[:8]))
+
+
+def test_fp4_encode_round_trip_ties_and_saturation():
+    grid = O.fp4_e2m1_decode(np.arange(16))
+    want = np.arange(16)
+    want[8] = 0                                                            # -0 encodes as +0
+    assert np.array_equal(O.fp4_e2m1_encode(grid), want)
+    # midpoints between neighbours go to the neighbour with the even code
+    mags = grid[:8]
+    for a in range(7):
+        mid = 0.5 * (mags[a] + mags[a + 1])
+        want = a if a % 2 == 0 else a + 1
+        assert O.fp4_e2m1_encode(mid) == want and O.fp4_e2m1_encode(-mid) == (want | 8 if want else 0)
+    # nearest value off the midpoints, saturation past 6
+    x = rng(5).uniform(-7, 7, 2000)
+    got = O.fp4_e2m1_decode(O.fp4_e2m1_encode(x))
+    best = grid[np.argmin(np.abs(x[:, None] - grid[None, :]), axis=1)]
+    np.testing.assert_array_equal(np.abs(got), np.abs(best))
+    assert O.fp4_e2m1_decode(O.fp4_e2m1_encode(100.0)) == 6.0 and O.fp4_e2m1_decode(O.fp4_e2m1_encode(-9.0)) == -6.0
+
+
+def test_mxfp4_block_scales_are_powers_of_two_placing_amax_in_4_to_8():
+    x = rng(6).normal(size=(7, 128)) * np.exp(rng(7).uniform(-8, 8, size=(7, 1)))
+    x[3, 32:64] = 0.0
+    codes, sc = O.mxfp4_block_quantize(x, 32)
+    assert sc.shape == (7, 4) and sc.dtype == np.float32
+    m, e = np.frexp(sc.astype(np.float64))
+    assert np.all(m == 0.5)                                    # powers of two
+    amax = np.abs(x.astype(np.float32).astype(np.float64)).reshape(7, 4, 32).max(-1)
+    ratio = amax / sc
+    nz = amax > 0
+    assert np.all((ratio[nz] >= 4) & (ratio[nz] < 8))
+    assert sc[3, 1] == 1.0 and np.all(codes[3, 32:64] == 0)   # a block of zeros
+    # error: half a grid step where |x|/scale <= 6, the saturation gap above
+    v = O.mxfp4_block_dequantize(codes, sc, 32)
+    y = np.abs(x) / np.repeat(sc, 32, axis=-1)
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    bound = np.where(y <= 6, 0.5 * step, y - 6 + 1e-9) * np.repeat(sc, 32, axis=-1)
+    assert np.all(np.abs(v - x) <= bound * (1 + 1e-6) + 1e-30)
+
+
+def test_fp4_pack_order():
+    c = np.array([[1, 2, 3, 4, 15, 0]], dtype=np.uint8)
+    p = O.fp4_pack(c)
+    assert list(p[0]) == [0x21, 0x43, 0x0F]
+    assert np.array_equal(O.fp4_unpack(p), c)
