@@ -31,27 +31,39 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "CSA/HCA decode tokens/s + indexer HBM GB/s at 65K/1M ctx; % of roofline"
 
 
+def kv_row_bytes(wl):
+    """Bytes of one stored compressed-KV row: bf16 values, fp8 codes + fp32 scale per block, or
+    fp4 codes (two per byte) + fp32 scale per 32 channels."""
+    if wl.kv_dtype == "fp8":
+        return wl.D + 4 * wl.D // wl.kv_scale_block
+    if wl.kv_dtype == "fp4":
+        return wl.D // 2 + 4 * wl.D // wl.kv_scale_block
+    return 2 * wl.D
+
+
 def algorithmic_costs(wl):
     """Bytes / flops each C-ABI call of one step must move / do at minimum.
 
     indexer: each visible key once (Di bytes fp8 + 4-byte scale, or 2*Di bf16), the
              indexer queries and weights, the selected indices.
-    attend:  each attended row once per query token (1 KB bf16 or 512 B + 32 B scales
-             fp8), q in (bf16) and out (bf16); flops 4 * H * rows * 512 per token.
+    attend:  each attended row once per query token (1 KB bf16, 512 B + 32 B scales fp8,
+             256 B + 64 B scales fp4; window rows bf16), q in (bf16) and out (bf16); flops
+             4 * H * rows * 512 per token.
     compress: raw kv + logits of the new tokens (2 KB per token) and the new rows.
     """
     rows = wl.B * wl.Tq
     E = wl.E
     key_b = (wl.Di + 4) if wl.idx_dtype == "fp8" else 2 * wl.Di
-    kv_row_b = (wl.D + 4 * wl.D // wl.kv_scale_block) if wl.kv_dtype == "fp8" else 2 * wl.D
+    kv_row_b = kv_row_bytes(wl)
     c = {}
     if wl.mode == "csa":
         c["index_bytes"] = rows * (E * key_b + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4)
         c["index_flops"] = rows * E * wl.Hi * wl.Di * 2
-        att_rows = wl.topk + wl.W
+        ent_rows = wl.topk
     else:
-        att_rows = E + wl.W
-    c["attend_bytes"] = rows * (att_rows * kv_row_b + 2 * wl.H * wl.D * 2)
+        ent_rows = E
+    att_rows = ent_rows + wl.W
+    c["attend_bytes"] = rows * (ent_rows * kv_row_b + wl.W * 2 * wl.D + 2 * wl.H * wl.D * 2)
     c["attend_flops"] = rows * 4 * wl.H * att_rows * wl.D
     new_entries = wl.E - wl.n_entries(wl.N - wl.Tq)
     raw = (new_entries - 1) * wl.stride + wl.window if new_entries else 0
@@ -71,7 +83,7 @@ def build_layers(wl, n_layers, device, torch, out_dtype):
 
 
 def layer_bytes(wl):
-    kv_row_b = (wl.D + 4 * wl.D // wl.kv_scale_block) if wl.kv_dtype == "fp8" else 2 * wl.D
+    kv_row_b = kv_row_bytes(wl)
     key_b = ((wl.Di + 4) if wl.idx_dtype == "fp8" else 2 * wl.Di) if wl.mode == "csa" else 0
     return wl.B * wl.E * (kv_row_b + key_b + (4 if wl.mode == "csa" else 0))
 
@@ -355,8 +367,14 @@ def cpu_baseline(wl, budget_s=12.0):
         qp = int(t["q_pos"][b, 0])
         new, _ = O.compress(t["kv_raw"][b].double().numpy(), t["z_raw"][b].double().numpy(), wl.window,
                             wl.stride, wl.pos0 + meta["E_pre"] * wl.stride, f)
-        kv = t["kv_cache"][b].double().numpy() if wl.kv_dtype == "bf16" else O.fp8_block_dequantize(
-            t["kv_cache"][b].numpy(), t["kv_cache_scale"][b].numpy(), wl.kv_scale_block)
+        if wl.kv_dtype == "fp4":
+            kv = O.mxfp4_block_dequantize(O.fp4_unpack(t["kv_cache"][b].numpy()),
+                                          t["kv_cache_scale"][b].numpy(), wl.kv_scale_block)
+        elif wl.kv_dtype == "fp8":
+            kv = O.fp8_block_dequantize(t["kv_cache"][b].numpy(), t["kv_cache_scale"][b].numpy(),
+                                        wl.kv_scale_block)
+        else:
+            kv = t["kv_cache"][b].double().numpy()
         kv[meta["E_pre"]:] = new[:meta["n_new_entries"]]
         win = t["win_cache"][b].double().numpy()
         win[meta["win_first_new"]:] = O.rope(t["kv_raw"][b, -meta["new_tok"]:].double().numpy(),
@@ -384,7 +402,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v4pro_csa_decode_65k")
     ap.add_argument("--extra", default="v4pro_hca_decode_1m,v4flash_csa_decode_1m_fp8,v4pro_csa_prefill_4k_on_131k,"
-                                       "v41flash_csa2_decode_1m_fp8,v4pro_csa_decode_65k_mtp4",
+                                       "v41flash_csa2_decode_1m_fp4,v4pro_csa_decode_65k_mtp4",
                     help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compressor-bulk", action="store_true")

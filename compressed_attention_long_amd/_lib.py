@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcsa.so")
 
 CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EWORKSPACE, CSA_EHIP = 0, -1, -2, -3, -4
-CSA_BF16, CSA_FP8_E4M3, CSA_FP32 = 0, 1, 2
+CSA_BF16, CSA_FP8_E4M3, CSA_FP32, CSA_FP4_E2M1 = 0, 1, 2, 3
 
 # Entry points declared in include/csa.h, in declaration order.
 EXPORTS = (
@@ -131,8 +131,9 @@ def _stream(stream=None):
 class Cache:
     """A per-layer row cache (see csa_cache_t): tensors plus row geometry.
 
-    data     [B, cap, C] torch.bfloat16, or torch.uint8 holding E4M3FN codes
-    scales   [B, cap, C // scale_block] float32 (fp8 only)
+    data     [B, cap, C] torch.bfloat16, or torch.uint8 holding E4M3FN codes, or with
+             fmt=CSA_FP4_E2M1 [B, cap, C // 2] torch.uint8 holding two E2M1 codes per byte
+    scales   [B, cap, C // scale_block] float32 (fp8 and fp4; fp4 blocks are 32 channels)
     n_valid  [B] int32     rows holding data
     pos0     [B] int64     position of raw token 0 of row 0
     """
@@ -144,9 +145,12 @@ class Cache:
     stride: int
     scales: Optional[torch.Tensor] = None
     scale_block: int = 0
+    fmt: Optional[int] = None      # storage code; None: bf16 or fp8 from data's dtype
 
     @property
     def dtype_code(self) -> int:
+        if self.fmt is not None:
+            return self.fmt
         return CSA_FP8_E4M3 if self.data.dtype == torch.uint8 else CSA_BF16
 
     @property
@@ -159,7 +163,7 @@ class Cache:
 
     @property
     def C(self) -> int:
-        return self.data.shape[2]
+        return self.data.shape[2] * (2 if self.dtype_code == CSA_FP4_E2M1 else 1)
 
     def struct(self) -> CCache:
         assert self.data.is_contiguous()

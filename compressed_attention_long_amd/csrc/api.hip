@@ -45,9 +45,14 @@ int check_cache(const csa_cache_t* c, const char* name, bool reads) {
   REQUIRE(c->C >= 1, CSA_EINVAL, "%s: C must be >= 1 (got %d)", name, c->C);
   REQUIRE(c->window >= 1 && c->stride >= 1, CSA_EINVAL, "%s: window and stride must be >= 1 (got %d, %d)",
           name, c->window, c->stride);
-  REQUIRE(c->dtype == CSA_BF16 || c->dtype == CSA_FP8_E4M3, CSA_ENOTSUP, "%s: dtype %d not supported", name,
-          c->dtype);
+  REQUIRE(c->dtype == CSA_BF16 || c->dtype == CSA_FP8_E4M3 || c->dtype == CSA_FP4_E2M1, CSA_ENOTSUP,
+          "%s: dtype %d not supported", name, c->dtype);
   REQUIRE(aligned(c->data, 16), CSA_EINVAL, "%s: data must be 16-byte aligned", name);
+  if (c->dtype == CSA_FP4_E2M1) {
+    REQUIRE(c->scales != nullptr, CSA_EINVAL, "%s: fp4 cache needs scales", name);
+    REQUIRE(c->scale_block == 32 && c->C % 32 == 0, CSA_EINVAL,
+            "%s: fp4 caches use 32-channel blocks (scale_block %d, C %d)", name, c->scale_block, c->C);
+  }
   if (c->dtype == CSA_FP8_E4M3) {
     REQUIRE(c->scales != nullptr, CSA_EINVAL, "%s: fp8 cache needs scales", name);
     REQUIRE(c->scale_block >= 1 && c->C % c->scale_block == 0, CSA_EINVAL,
@@ -192,6 +197,7 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int 
   REQUIRE(q_idx && w && q_pos && idx_out, CSA_EINVAL, "q_idx, w, q_pos and idx_out must be non-NULL");
   REQUIRE(Hi >= 1 && Hi <= 64, CSA_ENOTSUP, "Hi must be in [1, 64] (got %d)", Hi);
   REQUIRE(keys->C == 128, CSA_ENOTSUP, "indexer key dim must be 128 (got %d)", keys->C);
+  REQUIRE(keys->dtype != CSA_FP4_E2M1, CSA_ENOTSUP, "fp4 indexer keys are not supported");
   REQUIRE(keys->dtype == CSA_BF16 || keys->scale_block == keys->C, CSA_ENOTSUP,
           "fp8 indexer keys need one scale per key (scale_block == C)");
   REQUIRE(aligned(q_idx, 16), CSA_EINVAL, "q_idx must be 16-byte aligned");
@@ -289,7 +295,7 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   a.Tq = Tq;
   a.H = H;
   a.kv = kv->data;
-  a.kv_scales = kv->dtype == CSA_FP8_E4M3 ? kv->scales : nullptr;
+  a.kv_scales = kv->dtype != CSA_BF16 ? kv->scales : nullptr;
   a.kv_n_valid = kv->n_valid;
   a.kv_pos0 = kv->pos0;
   a.kv_dtype = kv->dtype;

@@ -83,8 +83,11 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool CSA, bool FP8>
+// KVF: the compressed cache's storage (CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1).
+template <bool CSA, int KVF>
 __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
+  constexpr bool QKV = KVF != CSA_BF16;   // quantized entry rows take the register path
+  constexpr int kRowB = KVF == CSA_FP8_E4M3 ? kD : (KVF == CSA_FP4_E2M1 ? kD / 2 : 2 * kD);
   // Four tile buffers as four objects: a pair of tiles is read from one half while the next
   // pair streams into the other, and separate objects let the compiler see that the LDS
   // reads never touch the half in flight (it then does not wait for those loads).
@@ -136,7 +139,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   // w + 8 (k & 3), a pair ahead: its number (a kv row >= 0, -2 - a window row, or -1 for no
   // row) and its byte offset from the kv base; the loads then take both from that lane.
   const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
-  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * (FP8 ? kD : 2 * kD);
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * kRowB;
   const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
   const int64_t win_off = winb - kvb;   // window rows are addressed from the kv base too
   struct PairRows {
@@ -163,7 +166,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       else if (!CSA) r = slot;
       else r = (j >= 0 && j < kv_nv) ? j : -1;
     }
-    const int64_t off = r >= 0 ? (int64_t)r * (FP8 ? kD : 2 * kD)
+    const int64_t off = r >= 0 ? (int64_t)r * kRowB
                                : (r <= -2 ? win_off + (int64_t)(-2 - r) * (2 * kD) : 0);
     return PairRows{r, off};
   };
@@ -178,7 +181,10 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   auto issue_row = [&](int pr, const PairRows& pr_rows, int k, uint16_t* n0, uint16_t* n1) {
     const int t = 2 * pr + (k >> 2);
     if (t >= ntile) return;
-    if (FP8 && __builtin_amdgcn_readlane(pr_rows.r, k) >= 0) return;   // fp8 rows: register path
+    // fp8/fp4 caches: entry rows take the register path, and empty slots (-1) are zero-filled
+    // there, since the bytes of a quantized row read as bf16 may be NaN (masked scores do not
+    // cancel a NaN in P x V)
+    if (QKV && __builtin_amdgcn_readlane(pr_rows.r, k) >= -1) return;
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(pr_rows.off >> 32), k);
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)pr_rows.off, k);
     const int64_t off = (int64_t)((hi << 32) | lo);
@@ -186,11 +192,12 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kvb + off + 16 * lane),
                                      (lds_void*)&dst[(wave + 8 * (k & 3)) * kPitch], 16, 0, 0);
   };
-  // fp8 entry rows: codes and the channel block's scale go through registers and are
-  // widened to bf16 (code * scale, rounded) on the way into LDS.
+  // fp8 / fp4 entry rows: codes and the channel block's scale go through registers and
+  // are widened to bf16 (code * scale, rounded; exact for fp4) on the way into LDS.  Lane
+  // l holds channels 8l .. 8l + 7 of the row: 8 fp8 codes, or 8 fp4 codes in one word.
   u32x2 pre8[8];
   float pres[8];
-  auto fetch_fp8 = [&](int pr, const PairRows& pr_rows) {
+  auto fetch_q = [&](int pr, const PairRows& pr_rows) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
@@ -198,25 +205,36 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       pres[k] = 0.f;
       if (2 * pr + (k >> 2) < ntile && r >= 0) {
         const int64_t rg = (int64_t)b * a.kv_cap + r;
-        pre8[k] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.kv) + rg * kD + 8 * lane);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv) + rg * kRowB;
+        if (KVF == CSA_FP4_E2M1) pre8[k][0] = *reinterpret_cast<const uint32_t*>(src + 4 * lane);
+        else pre8[k] = *reinterpret_cast<const u32x2*>(src + 8 * lane);
         pres[k] = a.kv_scales[rg * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
       }
     }
   };
-  auto store_fp8 = [&](int pr, const PairRows& pr_rows, uint16_t* n0, uint16_t* n1) {
+  auto store_q = [&](int pr, const PairRows& pr_rows, uint16_t* n0, uint16_t* n1) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int t = 2 * pr + (k >> 2);
       const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
-      if (t < ntile && r >= 0) {
+      if (t < ntile && r >= -1) {
         const float sc = pres[k];
-        const f32x2 f0 = fp8x2_lo(pre8[k][0]), f1 = fp8x2_hi(pre8[k][0]);
-        const f32x2 f2 = fp8x2_lo(pre8[k][1]), f3 = fp8x2_hi(pre8[k][1]);
-        u32x4 v;
-        v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
-        v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
-        v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
-        v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (r == -1) {
+        } else if (KVF == CSA_FP4_E2M1) {
+          const uint32_t w = pre8[k][0];
+          const float hs = 0.5f * sc;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = pack_bf16x2(fp4_e2m1_scaled(w >> (8 * i), hs), fp4_e2m1_scaled(w >> (8 * i + 4), hs));
+        } else {
+          const f32x2 f0 = fp8x2_lo(pre8[k][0]), f1 = fp8x2_hi(pre8[k][0]);
+          const f32x2 f2 = fp8x2_lo(pre8[k][1]), f3 = fp8x2_hi(pre8[k][1]);
+          v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
+          v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
+          v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
+          v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
+        }
         uint16_t* dst = (k >> 2) ? n1 : n0;
         *reinterpret_cast<u32x4*>(&dst[(wave + 8 * (k & 3)) * kPitch + 8 * lane]) = v;
       }
@@ -241,7 +259,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     mark_pair(0, rows0, 0);
 #pragma unroll
     for (int k = 0; k < 8; ++k) issue_row(0, rows0, k, tbA0, tbA1);
-    if (FP8) { fetch_fp8(0, rows0); store_fp8(0, rows0, tbA0, tbA1); }
+    if (QKV) { fetch_q(0, rows0); store_q(0, rows0, tbA0, tbA1); }
   }
   if (tid < a.rope_dim / 2) {
     float cs, sn;
@@ -305,7 +323,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       mark_pair(pr + 1, rows_cur, bcur ^ 2);
 #pragma unroll
       for (int k = 0; k < 8; ++k) issue_row(pr + 1, rows_cur, k, n0, n1);
-      if (FP8) fetch_fp8(pr + 1, rows_cur);
+      if (QKV) fetch_q(pr + 1, rows_cur);
     }
     idx_next = pair_idx(pr + 2);
     const int t = 2 * pr + grp;
@@ -390,7 +408,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
     }
     }
-    if (FP8 && more) store_fp8(pr + 1, rows_cur, n0, n1);
+    if (QKV && more) store_q(pr + 1, rows_cur, n0, n1);
   };
   for (int pr = 0; pr < npair; pr += 2) {
     pair_step(pr, tbA0, tbA1, tbB0, tbB1, 0);
@@ -599,14 +617,21 @@ hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const long long blocks = (long long)rows * HG * a.nsplit;
   const bool csa = a.csa_mode != 0;
-  const bool f8 = a.kv_dtype == CSA_FP8_E4M3;
   dim3 grid((unsigned)blocks);
-  if (csa) {
-    if (f8) hipLaunchKernelGGL((k_attend<true, true>), grid, dim3(kAttThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_attend<true, false>), grid, dim3(kAttThreads), 0, s, a);
-  } else {
-    if (f8) hipLaunchKernelGGL((k_attend<false, true>), grid, dim3(kAttThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_attend<false, false>), grid, dim3(kAttThreads), 0, s, a);
+  const dim3 blk(kAttThreads);
+  switch (a.kv_dtype) {
+    case CSA_FP8_E4M3:
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP8_E4M3>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_FP8_E4M3>), grid, blk, 0, s, a);
+      break;
+    case CSA_FP4_E2M1:
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP4_E2M1>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_FP4_E2M1>), grid, blk, 0, s, a);
+      break;
+    default:
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_BF16>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_BF16>), grid, blk, 0, s, a);
+      break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

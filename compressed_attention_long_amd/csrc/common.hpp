@@ -60,6 +60,28 @@ __device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float x) {
   return code == 0 ? 0u : (code | sign);
 }
 
+// fp32 -> OCP E2M1 code (4 bits), round to nearest even on the E2M1 grid, saturating at
+// +-6; written from the format definition: 1 sign, 2 exponent (bias 1), 1 mantissa bit,
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (the grid step is 0.5 below 2, 1 below 4, 2 above).
+// Negative zero encodes as +0.
+__device__ __forceinline__ uint32_t f32_to_fp4_e2m1(float x) {
+  const float a = fminf(fabsf(x), 6.0f);
+  uint32_t code;
+  if (a < 2.0f) code = (uint32_t)rintf(a * 2.0f);              // 0..4 (4 = 2.0, exponent 2)
+  else if (a < 4.0f) code = (uint32_t)rintf(a) + 2u;          // 2, 3, 4 -> codes 4, 5, 6
+  else code = (uint32_t)rintf(a * 0.5f) + 4u;                 // 4, 6 -> codes 6, 7
+  return code == 0 ? 0u : (code | ((__float_as_uint(x) >> 28) & 8u));
+}
+
+// E2M1 code (low 4 bits of c) times a scale; `half_scale` is half the block's scale.  Twice
+// the magnitude is an integer (0, 1, 2, 3, 4, 6, 8, 12), so the product is exact.
+__device__ __forceinline__ float fp4_e2m1_scaled(uint32_t c, float half_scale) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const uint32_t twice = e ? ((2u | m) << (e - 1)) : m;
+  const float v = (float)twice * half_scale;
+  return (c & 8u) ? -v : v;
+}
+
 // ---------------------------------------------------------------- rotary
 
 // (cos, sin) of pos * inv_freq, returned in fp32.  The angle is formed in fp64 and reduced

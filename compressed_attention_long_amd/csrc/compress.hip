@@ -1,4 +1,4 @@
-// Softmax-pooled KV compression with fused partial RoPE and bf16 / fp8 storage.
+// Softmax-pooled KV compression with fused partial RoPE and bf16 / fp8 / fp4 storage.
 //
 // Each cache row pools `window` raw tokens at step `stride` with a softmax taken
 // separately per channel over the window's pooling logits, then rotates the last
@@ -156,6 +156,25 @@ __device__ __forceinline__ void finish_row(const PoolState& p, const CompressArg
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + rowoff + c0) = w;
+  } else if (a.dtype == CSA_FP4_E2M1) {
+    // MXFP4: a 32-channel block spans 4 consecutive lanes; its scale is the power of two
+    // that puts the block's largest magnitude in [4, 8), 1 for a block of zeros.
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(e[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    int ex = 0;
+    (void)frexpf(amax, &ex);                        // amax = f * 2^ex, f in [0.5, 1)
+    const int es = amax > 0.f ? min(max(ex - 3, -127), 127) : 0;
+    const float scale = ldexpf(1.0f, es);
+    const float inv = ldexpf(1.0f, -es);            // exact: the scale is a power of two
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= f32_to_fp4_e2m1(e[i] * inv) << (4 * i);
+    // channel c0 + i in nibble i: even channels in the low nibble of their byte
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.out) + rowoff / 2 + c0 / 2) = w;
+    if ((c0 % 32) == 0) a.scales[((int64_t)b * a.cap + row) * (a.C / 32) + c0 / 32] = scale;
   } else {
     // fp8: one scale per scale_block channels = scale_block/8 consecutive lanes.
     float amax = 0.f;

@@ -44,7 +44,8 @@ class LayerStep:
         kv = tensors["kv_cache"]
         self.kv = ops.Cache(kv, tensors["kv_n_valid"], tensors["kv_pos0"], wl.window, wl.stride,
                             scales=tensors.get("kv_cache_scale"),
-                            scale_block=wl.kv_scale_block if wl.kv_dtype == "fp8" else 0)
+                            scale_block=wl.kv_scale_block if wl.kv_dtype != "bf16" else 0,
+                            fmt=ops.CSA_FP4_E2M1 if wl.kv_dtype == "fp4" else None)
         self.win = ops.Cache(tensors["win_cache"], tensors["win_n_valid"], tensors["win_pos0"], 1, 1)
         if wl.mode == "csa":
             ks = tensors.get("k_idx_scale")

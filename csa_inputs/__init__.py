@@ -24,8 +24,10 @@ checks at those sizes copy the device tensors back to the host for the oracle.
 
 fp8 tensors are synthesized directly as OCP e4m3fn codes (the library cast of
 a clamped Gaussian draw) plus positive per-block scales drawn around the value
-that makes code x scale ~ N(0, sigma^2).  They are stand-ins for caches that an
-earlier step already stored; the path only ever reads such bytes.
+that makes code x scale ~ N(0, sigma^2).  fp4 (MXFP4) caches are drawn the same
+way: uniform E2M1 codes, two per byte, with power-of-two scales per 32 channels.
+They are stand-ins for caches that an earlier step already stored; the path only
+ever reads such bytes.
 """
 from __future__ import annotations
 
@@ -56,8 +58,8 @@ class Workload:
     R: int = 64               # rotated dims (the last R of D)
     W: int = 128              # sliding window (raw tokens)
     Tq: int = 1               # query tokens per sequence (decode 1, prefill chunk > 1)
-    kv_dtype: str = "bf16"    # compressed KV cache storage: "bf16" | "fp8"
-    kv_scale_block: int = 64  # channels per fp8 scale in the KV cache
+    kv_dtype: str = "bf16"    # compressed KV cache storage: "bf16" | "fp8" | "fp4"
+    kv_scale_block: int = 64  # channels per scale in the KV cache (fp8; fp4 caches use 32)
     idx_dtype: str = "bf16"   # indexer key storage: "bf16" | "fp8" (one scale per key)
     pos0: int = 1             # position of raw token 0
     compress_each_step: bool = True
@@ -113,10 +115,11 @@ WORKLOADS = {
                                           idx_dtype="fp8", yarn_factor=16.0),
     # CSA2 (DeepSeek-V4.1-Flash vs Inkling, CSA2 encoder layers row): entries pool 2 raw tokens,
     # top-512; KV and selection computed in 3 of 18 layers and reused by the other 15 (5 per
-    # computed layer).  fp8 KV stands in for the page's FP4 cache.
-    "v41flash_csa2_decode_1m_fp8": Workload("v41flash_csa2_decode_1m_fp8", "csa", B=4, N=1048576, H=64,
-                                            topk=512, kv_dtype="fp8", idx_dtype="fp8", yarn_factor=16.0,
-                                            pool_window=2, pool_stride=2, reuse=5),
+    # computed layer).  The KV cache is FP4 (MXFP4, quantized after RoPE, the same page's
+    # partial-RoPE row); indexer keys stay fp8.
+    "v41flash_csa2_decode_1m_fp4": Workload("v41flash_csa2_decode_1m_fp4", "csa", B=4, N=1048576, H=64,
+                                            topk=512, kv_dtype="fp4", kv_scale_block=32, idx_dtype="fp8",
+                                            yarn_factor=16.0, pool_window=2, pool_stride=2, reuse=5),
 }
 
 
@@ -171,6 +174,29 @@ class Draw:
         scales = self.uniform(sshape, 0.75, 1.25) * (4.0 * std / FP8_MAX)
         return codes, scales.to(torch.float32)
 
+    def fp4_codes(self, shape, block=32):
+        """Random MXFP4 rows: E2M1 codes uniform over all 16, packed two per byte (channel 2k in
+        the low nibble of byte k), and power-of-two scales 2^e, e uniform in {-2, -1, 0}, per
+        `block` channels, so code x scale has magnitude ~ 1.
+
+        Returns (packed uint8 [..., C // 2], scales fp32 [..., C // block]).
+        """
+        c = shape[-1]
+        assert c % block == 0 and c % 2 == 0
+        codes = self.uniform(shape, 0.0, 16.0).floor_().clamp_(0, 15).to(torch.uint8)
+        packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).contiguous()
+        sshape = tuple(shape[:-1]) + (c // block,)
+        e = self.uniform(sshape, -2.0, 1.0).floor_().clamp_(-2, 0)
+        return packed, torch.exp2(e).to(torch.float32)
+
+    def kv_rows(self, wl, shape):
+        """Stored compressed-KV rows in the workload's format: (data, scales or None)."""
+        if wl.kv_dtype == "fp8":
+            return self.fp8_codes(shape, wl.kv_scale_block)
+        if wl.kv_dtype == "fp4":
+            return self.fp4_codes(shape, wl.kv_scale_block)
+        return self.normal(shape), None
+
 
 def seed_for(name: str) -> int:
     """Seed 1000 + index of the workload in WORKLOADS (insertion order)."""
@@ -208,12 +234,9 @@ def decode_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, n_raw_
     if n_raw_tail is not None:
         # Stored caches of the tokens before the tail: drawn, not computed.
         E = wl.E
-        if wl.kv_dtype == "fp8":
-            codes, sc = d.fp8_codes((wl.B, E, wl.D), wl.kv_scale_block)
-            out["kv_cache"] = codes
+        out["kv_cache"], sc = d.kv_rows(wl, (wl.B, E, wl.D))
+        if sc is not None:
             out["kv_cache_scale"] = sc
-        else:
-            out["kv_cache"] = d.normal((wl.B, E, wl.D))
         out["win_cache"] = d.normal((wl.B, wl.W, wl.D))
     return out
 
@@ -252,10 +275,9 @@ def step_tensors(wl: Workload, device="cpu", seed: Optional[int] = None):
             t["k_idx"] = d.normal((B, E, wl.Di), std=1.0 / math.sqrt(wl.Di))
         t["w"] = d.uniform((B, Tq, wl.Hi))
     t["sink"] = d.normal((wl.H,), dtype=torch.float32)
-    if wl.kv_dtype == "fp8":
-        t["kv_cache"], t["kv_cache_scale"] = d.fp8_codes((B, E, D), wl.kv_scale_block)
-    else:
-        t["kv_cache"] = d.normal((B, E, D))
+    t["kv_cache"], sc = d.kv_rows(wl, (B, E, D))
+    if sc is not None:
+        t["kv_cache_scale"] = sc
     win_cap = wl.W + new_tok
     t["win_cache"] = d.normal((B, win_cap, D))
     dev = t["q"].device

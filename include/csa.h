@@ -58,6 +58,8 @@ extern "C" {
 #define CSA_BF16      0     /* bfloat16 */
 #define CSA_FP8_E4M3  1     /* OCP FP8 E4M3FN codes (max 448, no infinities) with fp32 block scales */
 #define CSA_FP32      2     /* output only */
+#define CSA_FP4_E2M1  3     /* OCP MXFP4: E2M1 codes, two per byte, with power-of-two fp32 scales per
+                               32 channels (compressed KV caches only) */
 
 /*
  * A per-layer cache of rows, one set per sequence.  Used for the compressed
@@ -71,11 +73,16 @@ extern "C" {
  * it is rotated at that position and is visible to a query at position p only
  * if that position is <= p (an entry becomes visible when all its tokens are).
  *
- *   data       device [B, cap, C]: bf16 values, or fp8 codes (one byte each).
- *              Stored rows are already rotated (the cache is written after RoPE).
- *   scales     device [B, cap, C / scale_block] fp32, fp8 caches only (else NULL).
- *              Value of element c of row j = code * scales[.., j, c / scale_block].
- *              Scales must be >= 0.
+ *   data       device [B, cap, C]: bf16 values, or fp8 codes (one byte each), or for
+ *              fp4 [B, cap, C/2] bytes holding E2M1 codes, channel 2k in the low
+ *              nibble of byte k and 2k+1 in the high nibble.
+ *              Stored rows are already rotated (the cache is written after RoPE;
+ *              "DeepSeek-V4.1-Flash vs Inkling", partial-RoPE row: the FP4 KV cache
+ *              is quantized after RoPE).
+ *   scales     device [B, cap, C / scale_block] fp32, fp8 and fp4 caches only (else
+ *              NULL).  Value of element c of row j = code * scales[.., j, c / scale_block].
+ *              Scales must be >= 0; fp4 caches use scale_block 32 and powers of two
+ *              (the MX block scale: 2^(floor(log2 amax) - 2), scale 1 for a zero block).
  *   n_valid    device [B] int32: rows 0 .. n_valid[b]-1 hold data (read side).
  *              Values above cap are treated as cap, negative values as 0.
  *   pos0       device [B] int64.
@@ -85,10 +92,10 @@ typedef struct csa_cache {
     float*         scales;
     const int32_t* n_valid;
     const int64_t* pos0;
-    int32_t        dtype;        /* CSA_BF16 or CSA_FP8_E4M3 */
+    int32_t        dtype;        /* CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1 */
     int32_t        cap;          /* rows per sequence */
     int32_t        C;            /* channels per row */
-    int32_t        scale_block;  /* channels per fp8 scale (fp8 only) */
+    int32_t        scale_block;  /* channels per scale (fp8: any divisor of C; fp4: 32) */
     int32_t        window;       /* raw tokens per row */
     int32_t        stride;       /* raw tokens between consecutive rows */
 } csa_cache_t;

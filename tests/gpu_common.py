@@ -9,7 +9,10 @@ Parity bars (stated for the GPU path against the fp64 oracle):
                      the oracle's selection run on the GPU's own scores
   compressor         bf16 within one bf16 spacing of the fp64 value plus the fp32
                      error bound of the pooled sum (see pool_error_bound); fp8
-                     codes within one code step, scales within 1e-6 relative
+                     codes within one code step, scales within 1e-6 relative;
+                     fp4 (MXFP4) scales equal in >= 99% of blocks (else a factor
+                     of 2 with the block maximum at a power of two), values within
+                     one E2M1 grid step, codes equal in >= 99% of elements
   log-sum-exp        within 1e-4 absolute
 """
 from __future__ import annotations
@@ -29,11 +32,42 @@ def np64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def stored_rows(data: torch.Tensor, scales, block: int) -> np.ndarray:
-    """fp64 values of stored cache rows (bf16, or fp8 codes times scales)."""
+def stored_rows(data: torch.Tensor, scales, block: int, kv_dtype: str = "") -> np.ndarray:
+    """fp64 values of stored cache rows (bf16, fp8 codes times scales, or with kv_dtype "fp4"
+    packed E2M1 codes times the 32-channel scales)."""
+    if kv_dtype == "fp4":
+        return O.mxfp4_block_dequantize(O.fp4_unpack(data.cpu().numpy()), scales.cpu().numpy(), block)
     if data.dtype == torch.uint8:
         return O.fp8_block_dequantize(data.cpu().numpy(), scales.cpu().numpy(), block)
     return np64(data)
+
+
+def _e2m1_step(mag: np.ndarray) -> np.ndarray:
+    """Spacing of the E2M1 grid at code magnitude `mag` (0.5 below 2, 1 below 4, else 2)."""
+    return np.where(mag < 2.0, 0.5, np.where(mag < 4.0, 1.0, 2.0))
+
+
+def check_fp4_rows(packed: np.ndarray, scales: np.ndarray, ref: np.ndarray, what: str = ""):
+    """GPU MXFP4 rows (packed codes [n, C/2], scales [n, C/32]) against the oracle's
+    quantization of the fp64 rows `ref` [n, C]."""
+    codes_o, sc_o = O.mxfp4_block_quantize(ref)
+    codes_g = O.fp4_unpack(packed)
+    same_scale = scales == sc_o
+    assert same_scale.mean() >= 0.99, f"{what}: only {same_scale.mean():.4f} of the block scales agree"
+    if not same_scale.all():
+        # a differing scale may only come from a block maximum at a power of two
+        r = scales[~same_scale] / sc_o[~same_scale]
+        assert np.all((r == 2.0) | (r == 0.5)), f"{what}: scales differ by more than a factor 2"
+        amax = np.abs(ref.reshape(ref.shape[0], -1, 32)).max(-1)[~same_scale]
+        near = np.abs(amax / np.exp2(np.round(np.log2(amax))) - 1.0)
+        assert np.all(near < 1e-5), f"{what}: scales differ away from a power-of-two maximum"
+    vg = O.fp4_e2m1_decode(codes_g) * np.repeat(scales, 32, axis=-1)
+    vo = O.fp4_e2m1_decode(codes_o) * np.repeat(sc_o, 32, axis=-1)
+    step = np.maximum(_e2m1_step(np.abs(O.fp4_e2m1_decode(codes_g))) * np.repeat(scales, 32, axis=-1),
+                      _e2m1_step(np.abs(O.fp4_e2m1_decode(codes_o))) * np.repeat(sc_o, 32, axis=-1))
+    assert np.all(np.abs(vg - vo) <= step), f"{what}: fp4 values more than one grid step apart"
+    assert np.mean((codes_g == codes_o) | ((codes_g & 7) == 0) & ((codes_o & 7) == 0)) > 0.99, \
+        f"{what}: fewer than 99% of the fp4 codes agree"
 
 
 def check_attention(o_gpu: np.ndarray, o_ora: np.ndarray, what: str = ""):

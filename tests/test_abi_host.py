@@ -30,8 +30,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def cache(dtype=L.CSA_BF16, cap=64, C=512, window=8, stride=4, scales=True, sb=64):
-    return L.CCache(FAKE, FAKE if (dtype == L.CSA_FP8_E4M3 and scales) else None, FAKE, FAKE, dtype, cap, C,
-                    sb, window, stride)
+    quant = dtype in (L.CSA_FP8_E4M3, L.CSA_FP4_E2M1)
+    return L.CCache(FAKE, FAKE if (quant and scales) else None, FAKE, FAKE, dtype, cap, C, sb, window, stride)
 
 
 def rc_msg(rc):
@@ -59,6 +59,11 @@ def test_compress_validation():
     assert compress(cache(dtype=L.CSA_FP8_E4M3, scales=False))[0] == L.CSA_EINVAL
     assert compress(cache(dtype=L.CSA_FP8_E4M3, sb=24))[0] == L.CSA_EINVAL   # does not divide C
     assert compress(cache(dtype=L.CSA_FP8_E4M3, sb=1024, C=1024), ld_tok=1024, ld_seq=1024 * 64)[0] == L.CSA_ENOTSUP
+    # fp4 (MXFP4) caches: scales required, 32-channel blocks only
+    assert compress(cache(dtype=L.CSA_FP4_E2M1, scales=False, sb=32))[0] == L.CSA_EINVAL
+    rc, msg = compress(cache(dtype=L.CSA_FP4_E2M1, sb=64))
+    assert rc == L.CSA_EINVAL and "32" in msg
+    assert compress(cache(dtype=L.CSA_FP4_E2M1, sb=32), n_new=0) == (L.CSA_OK, "")
     # nothing to do is a success with no launch
     rc, msg = compress(c, n_new=0)
     assert rc == L.CSA_OK and msg == ""
@@ -90,6 +95,8 @@ def test_index_topk_validation():
     assert index(k, Hi=65)[0] == L.CSA_ENOTSUP
     assert index(cache(C=256))[0] == L.CSA_ENOTSUP
     assert index(cache(C=128, dtype=L.CSA_FP8_E4M3, sb=64))[0] == L.CSA_ENOTSUP
+    rc, msg = index(cache(C=128, dtype=L.CSA_FP4_E2M1, sb=32))
+    assert rc == L.CSA_ENOTSUP and "fp4" in msg
     need = L.index_topk_workspace_bytes(1, 1, 64, 64, 16)
     assert need >= 64 * 4
     rc, msg = index(k, ws=FAKE, wsb=need - 1)
@@ -130,6 +137,10 @@ def test_attend_validation():
     hneed = L.hca_attend_workspace_bytes(32, 1, 128, 2048, 128)
     assert attend(kv, win, hca=True, ws=FAKE, wsb=hneed - 256)[0] == L.CSA_EWORKSPACE
     assert attend(kv, win, B=0)[0] == L.CSA_OK
+    fp4 = cache(cap=2048, dtype=L.CSA_FP4_E2M1, sb=32)
+    assert attend(fp4, win, B=0)[0] == L.CSA_OK                   # fp4 entries are accepted
+    assert attend(cache(cap=2048, dtype=L.CSA_FP4_E2M1, sb=32, scales=False), win)[0] == L.CSA_EINVAL
+    assert attend(kv, cache(cap=160, window=1, stride=1, dtype=L.CSA_FP4_E2M1, sb=32))[0] == L.CSA_ENOTSUP
 
 
 def test_workspace_sizes_scale_with_work():

@@ -13,7 +13,7 @@ from compressed_attention_long_amd.step import LayerStep
 from oracle import csa_oracle as O
 
 from gpu_common import (check_attention, check_bf16_rows, check_scores, check_topk, np64, oracle_rows_csa,
-                        oracle_rows_hca, pool_error_bound, stored_rows)
+                        oracle_rows_hca, pool_error_bound, stored_rows, check_fp4_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -61,10 +61,11 @@ def check_rows(wl, t, meta, step, samples):
             ig = step.idx[b, tq].cpu().numpy()
             check_topk(ig, sg, so, vis, wl.topk, f"{wl.name} b={b} t={tq}")
             sel = torch.from_numpy(ig[ig >= 0].astype(np.int64)).to(DEV)
-            kv_sel = stored_rows(step.kv.data[b][sel], sc_b[sel] if sc_b is not None else None, kv_block)
+            kv_sel = stored_rows(step.kv.data[b][sel], sc_b[sel] if sc_b is not None else None, kv_block,
+                                 wl.kv_dtype)
             X = oracle_rows_csa(kv_sel, np.arange(len(sel)), win_rows, win_pos, qp, wl.W, len(sel))
         else:
-            kv_rows = stored_rows(step.kv.data[b], sc_b, kv_block)
+            kv_rows = stored_rows(step.kv.data[b], sc_b, kv_block, wl.kv_dtype)
             X = oracle_rows_hca(kv_rows, ent_pos_all, win_rows, win_pos, qp, wl.W)
         o, l = O.attend(np64(t["q"][b, tq]), qp, X, sink, oracle_scale(wl), fo)
         check_attention(np64(step.out[b, tq]), o, f"{wl.name} b={b} t={tq}")
@@ -78,6 +79,10 @@ def check_new_entry(wl, t, meta, step, b):
     n = meta["n_new_entries"]
     ent, _ = O.compress(np64(t["kv_raw"][b]), np64(t["z_raw"][b]), wl.window, wl.stride,
                         wl.pos0 + first * wl.stride, fo)
+    if wl.kv_dtype == "fp4":
+        check_fp4_rows(step.kv.data[b, first:first + n].cpu().numpy(),
+                       step.kv.scales[b, first:first + n].cpu().numpy(), ent[:n], f"{wl.name} new entries b={b}")
+        return
     got = stored_rows(step.kv.data[b, first:first + n],
                       step.kv.scales[b, first:first + n] if step.kv.scales is not None else None, wl.kv_scale_block)
     if wl.kv_dtype == "fp8":
@@ -122,11 +127,11 @@ def test_v4pro_csa_decode_65k_mtp4():
     check_rows(wl, t, meta, step, [(0, 0), (0, 3), (21, 1), (31, 2)])
 
 
-def test_v41flash_csa2_decode_1m_fp8_with_reuse():
-    """CSA2 at 1M: entries pool 2 tokens, top-512 of 524,288, fp8 KV; then a reuse layer (its own
+def test_v41flash_csa2_decode_1m_fp4_with_reuse():
+    """CSA2 at 1M: entries pool 2 tokens, top-512 of 524,288, MXFP4 KV; then a reuse layer (its own
     queries and sink over the computed layer's KV and selection)."""
     from compressed_attention_long_amd.step import ReuseStep
-    wl, t, meta, step = run_step("v41flash_csa2_decode_1m_fp8")
+    wl, t, meta, step = run_step("v41flash_csa2_decode_1m_fp4")
     check_rows(wl, t, meta, step, [(0, 0), (3, 0)])
     check_new_entry(wl, t, meta, step, 1)
     r = ci.reuse_tensors(wl, DEV)
@@ -139,7 +144,7 @@ def test_v41flash_csa2_decode_1m_fp8_with_reuse():
         qp = int(t["q_pos"][b, 0])
         ig = step.idx[b, 0].cpu().numpy()
         sel = torch.from_numpy(ig[ig >= 0].astype(np.int64)).to(DEV)
-        kv_sel = stored_rows(step.kv.data[b][sel], step.kv.scales[b][sel], wl.kv_scale_block)
+        kv_sel = stored_rows(step.kv.data[b][sel], step.kv.scales[b][sel], wl.kv_scale_block, wl.kv_dtype)
         X = oracle_rows_csa(kv_sel, np.arange(len(sel)), np64(step.win.data[b]), win_pos, qp, wl.W, len(sel))
         o, l = O.attend(np64(r["q"][b, 0]), qp, X, np64(r["sink"]), oracle_scale(wl), fo)
         check_attention(np64(rs.out[b, 0]), o, f"reuse layer b={b}")

@@ -16,8 +16,8 @@ from compressed_attention_long_amd import _lib as ops
 from compressed_attention_long_amd.rope import rope_inv_freq, yarn_inv_freq
 from oracle import csa_oracle as O
 
-from gpu_common import (LSE_TOL, check_attention, check_bf16_rows, check_scores, check_topk, np64,
-                        oracle_rows_csa, oracle_rows_hca, pool_error_bound, stored_rows)
+from gpu_common import (LSE_TOL, check_attention, check_bf16_rows, check_fp4_rows, check_scores, check_topk,
+                        np64, oracle_rows_csa, oracle_rows_hca, pool_error_bound, stored_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -53,6 +53,10 @@ def inv_freq_pair(R=64, yarn=False):
     (1, 1, "bf16", 2, 60, 1, "yarn"),
     (2, 2, "bf16", 3, 700, 2, "yarn"),   # CSA2 geometry: 2 tokens per entry, no overlap
     (2, 2, "fp8", 2, 1, 5, "yarn"),      # CSA2 decode-step entry, fp8
+    (8, 4, "fp4", 2, 333, 0, 64),        # MXFP4 cache (32-channel power-of-two scales), run mode
+    (2, 2, "fp4", 3, 700, 2, "yarn"),    # CSA2 geometry, fp4 (the V4.1-Flash cache)
+    (2, 2, "fp4", 2, 1, 5, "yarn"),      # CSA2 decode-step entry, fp4 (split layout)
+    (128, 128, "fp4", 2, 5, 0, "yarn"),  # HCA geometry, fp4
 ])
 def test_compress_parity(window, stride, dtype, B, n_new, first, R):
     yarn = R == "yarn"
@@ -66,17 +70,18 @@ def test_compress_parity(window, stride, dtype, B, n_new, first, R):
     pos0_list = [1 + 977 * b for b in range(B)]
     pos0_list[-1] = 1048576 - (first + n_new) * stride - window      # large angles
     pos0 = torch.tensor(pos0_list, dtype=torch.int64)
-    sb = 64
+    sb = 32 if dtype == "fp4" else 64
     if dtype == "bf16":
         data = torch.full((B, cap, 512), 12345, dtype=torch.int16).view(torch.bfloat16)
         scales = None
     else:
-        data = torch.full((B, cap, 512), 0xAA, dtype=torch.uint8)
+        data = torch.full((B, cap, 256 if dtype == "fp4" else 512), 0xAA, dtype=torch.uint8)
         scales = torch.full((B, cap, 512 // sb), -1.0, dtype=torch.float32)
     dg = data.to(DEV)
     sg = scales.to(DEV) if scales is not None else None
     cache = ops.Cache(dg, torch.full((B,), cap, dtype=torch.int32, device=DEV), pos0.to(DEV), window, stride,
-                      scales=sg, scale_block=sb if dtype == "fp8" else 0)
+                      scales=sg, scale_block=sb if dtype != "bf16" else 0,
+                      fmt=ops.CSA_FP4_E2M1 if dtype == "fp4" else None)
     fg, fo = inv_freq_pair(R, yarn) if R else (None, np.zeros(0))
     ops.compress(kv.to(DEV), z.to(DEV) if window > 1 else None, cache, first, n_new, fg, R)
     torch.cuda.synchronize()
@@ -90,6 +95,11 @@ def test_compress_parity(window, stride, dtype, B, n_new, first, R):
             check_bf16_rows(got, ref, bound, f"b={b}")
             untouched = torch.cat([out[b, :first], out[b, first + n_new:]]).view(torch.int16)
             assert torch.all(untouched == 12345)
+        elif dtype == "fp4":
+            check_fp4_rows(out[b, first:first + n_new].numpy(), sg.cpu()[b, first:first + n_new].numpy(), ref,
+                           f"b={b}")
+            assert torch.all(out[b, :first] == 0xAA) and torch.all(out[b, first + n_new:] == 0xAA)
+            assert torch.all(sg.cpu()[b, :first] == -1.0) and torch.all(sg.cpu()[b, first + n_new:] == -1.0)
         else:
             codes_o, sc_o = O.fp8_block_quantize(ref, sb)
             sc_g = sg.cpu()[b, first:first + n_new].numpy()
@@ -257,7 +267,13 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     d = ci.Draw(seed, "cpu")
     q = d.normal((B, Tq, H, 512), std=qmul / math.sqrt(512))
     sink = d.normal((H,), dtype=torch.float32)
-    if kv_fp8:
+    if kv_fp8 == "fp4":
+        # MXFP4 entries: code x power-of-two scale is exact in bf16, so staging adds no rounding
+        packed, sc = d.fp4_codes((B, cap, 512), 32)
+        kv = ops.Cache(packed.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV), None, 8, 4,
+                       scales=sc.to(DEV), scale_block=32, fmt=ops.CSA_FP4_E2M1)
+        kv_ref = O.mxfp4_block_dequantize(O.fp4_unpack(packed.numpy()), sc.numpy(), 32)
+    elif kv_fp8:
         codes, sc = d.fp8_codes((B, cap, 512), 64)
         kv = ops.Cache(codes.to(DEV), torch.tensor(n_valid, dtype=torch.int32, device=DEV), None, 8, 4,
                        scales=sc.to(DEV), scale_block=64)
@@ -332,6 +348,9 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     # exceeds the bar (CPU emulation of that rounding: 1.1% at scale 1, 5.8% at scale 1 with q x 4)
     ("hca", 1, 2, 128, 64, [64], True, 0, 128, 129, 1 / math.sqrt(512), 4.0),        # fp8, sharper q
     ("hca", 3, 1, 24, 300, [300, 299, 1], False, 0, 0, 1, 1 / math.sqrt(512), 1.0),   # no window, H < 32
+    ("csa", 4, 1, 64, 6000, [6000, 5000, 512, 100], "fp4", 512, 128, 129, 1 / math.sqrt(512), 4.0),  # CSA2, fp4
+    ("csa", 2, 3, 64, 900, [900, 40], "fp4", 300, 128, 140, 1 / math.sqrt(512), 1.0),  # fp4, < k visible
+    ("hca", 2, 1, 128, 700, [700, 300], "fp4", 0, 128, 129, 1 / math.sqrt(512), 1.0),  # fp4, dense, splits
 ])
 def test_attend_parity(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul):
     _attend_case(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul, seed=400 + cap + H)
