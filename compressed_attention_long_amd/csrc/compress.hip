@@ -129,24 +129,38 @@ __device__ __forceinline__ void pool_block(PoolState& p, const uint16_t* kv, con
   }
 }
 
+// (cos, sin) of the row's position times the frequencies of the lane's rotated pairs (1, 0
+// for pairs that are not rotated).  The row's position is that of its last token.
+struct RopeTrig {
+  float cs[4], sn[4];
+};
+__device__ __forceinline__ RopeTrig rope_trig(const CompressArgs& a, const RopeIn& ri, int row, int c0) {
+  RopeTrig t;
+  const int rot0 = a.C - a.rope_dim;
+  const int64_t pos = ri.pos0 + (int64_t)row * a.stride + (a.window - 1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t.cs[k] = 1.f;
+    t.sn[k] = 0.f;
+    if (a.rope_dim > 0 && c0 + 2 * k >= rot0) rope_cs(pos, ri.fr[k], t.cs[k], t.sn[k]);
+  }
+  return t;
+}
+
 // Finish one row: normalise, rotate, store.
-__device__ __forceinline__ void finish_row(const PoolState& p, const CompressArgs& a, const RopeIn& ri, int b,
+__device__ __forceinline__ void finish_row(const PoolState& p, const CompressArgs& a, const RopeTrig& tr, int b,
                                            int row, int c0) {
   float e[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) e[i] = p.sv[i] / p.s[i];
   const int rot0 = a.C - a.rope_dim;
   if (c0 + 8 > rot0 && a.rope_dim > 0) {
-    int64_t pos = ri.pos0 + (int64_t)row * a.stride + (a.window - 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      int c = c0 + 2 * k;
-      if (c >= rot0) {
-        float cs, sn;
-        rope_cs(pos, ri.fr[k], cs, sn);
-        float x0 = e[2 * k], x1 = e[2 * k + 1];
-        e[2 * k] = x0 * cs - x1 * sn;
-        e[2 * k + 1] = x0 * sn + x1 * cs;
+      if (c0 + 2 * k >= rot0) {
+        const float x0 = e[2 * k], x1 = e[2 * k + 1];
+        e[2 * k] = x0 * tr.cs[k] - x1 * tr.sn[k];
+        e[2 * k + 1] = x0 * tr.sn[k] + x1 * tr.cs[k];
       }
     }
   }
@@ -231,7 +245,7 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
       pool_reset(cur);
       pool_regs(cur, r1, st);
       pool_merge(both, prev, cur);
-      finish_row(both, a, ri, b, a.first_row + i, c0);
+      finish_row(both, a, rope_trig(a, ri, a.first_row + i, c0), b, a.first_row + i, c0);
       prev = cur;
       r1 = r0;
     }
@@ -243,7 +257,7 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
       pool_reset(cur);
       pool_block(cur, kv, lg, a.ld_tok, (i + 1) * a.stride, a.stride, c0);
       pool_merge(both, prev, cur);
-      finish_row(both, a, ri, b, a.first_row + i, c0);
+      finish_row(both, a, rope_trig(a, ri, a.first_row + i, c0), b, a.first_row + i, c0);
       prev = cur;
     }
   } else {
@@ -251,7 +265,7 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
       PoolState p;
       pool_reset(p);
       pool_block(p, kv, lg, a.ld_tok, i * a.stride, a.window, c0);
-      finish_row(p, a, ri, b, a.first_row + i, c0);
+      finish_row(p, a, rope_trig(a, ri, a.first_row + i, c0), b, a.first_row + i, c0);
     }
   }
 }
@@ -277,13 +291,21 @@ __device__ __forceinline__ void compress_split_block(const CompressArgs& a, int 
   PoolState p;
   pool_reset(p);
   const int t0 = i * a.stride;
-  // group g takes tokens g, g + 16, g + 32, ... of the window, kB of them per load round
+  // group g takes tokens g, g + 16, g + 32, ... of the window, kB of them per load round,
+  // the next round's loads in flight while the current one is pooled
   const int mine = g < a.window ? (a.window - 1 - g) / kSplitGroups + 1 : 0;
+  RawBlock r0, r1;
+  load_block(r0, kv, lg, a.ld_tok, (int64_t)t0 + g, min(kB, mine), c0, kSplitGroups);
+  // the merging group's rotation, taken while the window's tokens are in flight
+  RopeTrig tr{};
+  if (g == 0) tr = rope_trig(a, ri, a.first_row + i, c0);
   for (int u0 = 0; u0 < mine; u0 += kB) {
-    RawBlock r;
     const int m = min(kB, mine - u0);
-    load_block(r, kv, lg, a.ld_tok, (int64_t)t0 + g + (int64_t)u0 * kSplitGroups, m, c0, kSplitGroups);
-    pool_regs(p, r, m);
+    if (u0 + kB < mine)
+      load_block(r1, kv, lg, a.ld_tok, (int64_t)t0 + g + (int64_t)(u0 + kB) * kSplitGroups, min(kB, mine - u0 - kB),
+                 c0, kSplitGroups);
+    pool_regs(p, r0, m);
+    r0 = r1;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -292,38 +314,75 @@ __device__ __forceinline__ void compress_split_block(const CompressArgs& a, int 
     sm_v[g][cs + k] = p.sv[k];
   }
   __syncthreads();
+  // one thread per channel merges the states of the groups that hold tokens, into group 0's slot
+  if (threadIdx.x < kSliceC) {
+    const int ch = threadIdx.x;
+    const int nh = min(a.window, kSplitGroups);
+    float m = kNegBig;
+    for (int h = 0; h < nh; ++h) m = fmaxf(m, sm_m[h][ch]);
+    float ss = 0.f, sv = 0.f;
+    for (int h = 0; h < nh; ++h) {
+      const float f = fexp2(sm_m[h][ch] - m);
+      ss += sm_s[h][ch] * f;
+      sv += sm_v[h][ch] * f;
+    }
+    sm_m[0][ch] = m;
+    sm_s[0][ch] = ss;
+    sm_v[0][ch] = sv;
+  }
+  __syncthreads();
   if (g != 0) return;
-  // group 0 merges the 16 states of its 8 channels (groups without tokens hold s = 0)
   PoolState q;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    float m = kNegBig;
-    for (int h = 0; h < kSplitGroups; ++h) m = fmaxf(m, sm_m[h][cs + k]);
-    float ss = 0.f, sv = 0.f;
-    for (int h = 0; h < kSplitGroups; ++h) {
-      const float f = fexp2(sm_m[h][cs + k] - m);
-      ss += sm_s[h][cs + k] * f;
-      sv += sm_v[h][cs + k] * f;
-    }
-    q.m[k] = m;
-    q.s[k] = ss;
-    q.sv[k] = sv;
+    q.m[k] = sm_m[0][cs + k];
+    q.s[k] = sm_s[0][cs + k];
+    q.sv[k] = sm_v[0][cs + k];
   }
-  finish_row(q, a, ri, b, a.first_row + i, c0);
+  finish_row(q, a, tr, b, a.first_row + i, c0);
 }
 
-__global__ void __launch_bounds__(256) k_compress_split(CompressArgs a) {
-  compress_split_block(a, blockIdx.x, blockIdx.y, blockIdx.z);
+// Short windows (CSA: 8 tokens; the raw-window write: 1) and decode-sized calls: one group of
+// C/8 lanes per (row, sequence), each lane loading its 8 channels of every token of the row
+// (all loads in flight together), with no cross-group merge.  Block-unit u covers the
+// 256 / (C/8) consecutive (row, sequence) pairs from u * groups on, sequence fastest.
+__device__ __forceinline__ void compress_rows_block(const CompressArgs& a, int u) {
+  const int lanes = a.C / 8;
+  const int groups = 256 / lanes;
+  const int g = threadIdx.x / lanes, li = threadIdx.x % lanes;
+  const long long unit = (long long)u * groups + g;
+  if (unit >= (long long)a.n_new * a.B) return;
+  const int i = (int)(unit / a.B), b = (int)(unit % a.B);
+  const int c0 = li * 8;
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (int64_t)b * a.ld_seq;
+  const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
+                                : nullptr;
+  const RopeIn ri = rope_in(a, b, c0);
+  // every token of the row in flight (window <= 2 kB), then the rotation while they arrive
+  RawBlock r0, r1;
+  const int64_t t0 = (int64_t)i * a.stride;
+  const int n0 = min(kB, a.window), n1 = a.window - n0;
+  load_block(r0, kv, lg, a.ld_tok, t0, n0, c0);
+  if (n1 > 0) load_block(r1, kv, lg, a.ld_tok, t0 + kB, n1, c0);
+  const RopeTrig tr = rope_trig(a, ri, a.first_row + i, c0);
+  PoolState p;
+  pool_reset(p);
+  pool_regs(p, r0, n0);
+  if (n1 > 0) pool_regs(p, r1, n1);
+  finish_row(p, a, tr, b, a.first_row + i, c0);
 }
 
 // Several calls in one launch (a step's new entries and its raw-window write): block L
-// belongs to call c when start[c] <= L < start[c + 1], and within it to (row, sequence,
-// slice) in that order of significance.  The call is selected by a uniform branch so that
-// its arguments stay in scalar registers.
+// belongs to call c when start[c] <= L < start[c + 1].  In the split layout its blocks are
+// (row, sequence, slice) in that order of significance; in the rows layout they are the
+// block-units of compress_rows_block.  The call is selected by a uniform branch so that its
+// arguments stay in scalar registers.
 constexpr int kBatchMax = 4;
+constexpr int kLaySplit = 0, kLayRows = 1;
 struct CompressBatch {
   CompressArgs a[kBatchMax];
   int start[kBatchMax + 1];
+  int lay[kBatchMax];
   int n;
 };
 __global__ void __launch_bounds__(256) k_compress_split_batch(CompressBatch bt) {
@@ -332,6 +391,10 @@ __global__ void __launch_bounds__(256) k_compress_split_batch(CompressBatch bt) 
   while (c + 1 < bt.n && L >= bt.start[c + 1]) ++c;
   auto run = [&](const CompressArgs& a) {
     const int r = L - bt.start[c];
+    if (bt.lay[c] == kLayRows) {
+      compress_rows_block(a, r);
+      return;
+    }
     const int nz = a.C / kSliceC;
     const int z = r % nz, rb = r / nz;
     compress_split_block(a, rb / a.B, rb % a.B, z);
@@ -344,17 +407,32 @@ __global__ void __launch_bounds__(256) k_compress_split_batch(CompressBatch bt) 
   }
 }
 
-// Calls that the split layout serves: 128-channel slices, and either long windows or few
-// rows (every token of a row then loads in parallel).
-static bool split_layout(const CompressArgs& a, bool any_window) {
+// Layout of a call in the one-launch kernel, or -1 for the run-mode kernel.  Long windows
+// take the split layout (128-channel slices, the window's tokens spread over 16 lane groups);
+// few rows (a decode step) take the rows layout when the window is short (every token of a
+// row loads at once in one lane group) and the split layout otherwise.  Many rows of a short
+// window (prefill) take the run-mode kernel, which reads shared tokens once.
+static int batch_layout(const CompressArgs& a) {
   const long long rows = (long long)a.n_new * a.B;
   const bool split_ok = a.C % kSliceC == 0 && (a.dtype == CSA_BF16 || a.scale_block <= kSliceC);
-  return split_ok && (a.window >= 2 * kSplitGroups || ((any_window || a.window >= 4) && rows <= 512));
+  if (split_ok && a.window >= 2 * kSplitGroups) return kLaySplit;
+  if (rows > 512) return -1;
+  if (a.window <= 2 * kB) return kLayRows;
+  return split_ok ? kLaySplit : -1;
+}
+
+static long long batch_blocks(const CompressArgs& a, int lay) {
+  const long long rows = (long long)a.n_new * a.B;
+  if (lay == kLayRows) {
+    const int groups = 256 / (a.C / 8);
+    return (rows + groups - 1) / groups;
+  }
+  return rows * (a.C / kSliceC);
 }
 
 hipError_t launch_compress_batch(const CompressArgs* a, int n, hipStream_t s) {
-  bool fuse = n >= 2 && n <= kBatchMax;
-  for (int i = 0; fuse && i < n; ++i) fuse = split_layout(a[i], true) && a[i].n_new > 0 && a[i].B > 0;
+  bool fuse = n >= 1 && n <= kBatchMax;
+  for (int i = 0; fuse && i < n; ++i) fuse = batch_layout(a[i]) >= 0;
   if (!fuse) {
     for (int i = 0; i < n; ++i) {
       const hipError_t e = launch_compress(a[i], s);
@@ -363,27 +441,26 @@ hipError_t launch_compress_batch(const CompressArgs* a, int n, hipStream_t s) {
     return hipSuccess;
   }
   CompressBatch bt{};
-  bt.n = n;
   long long total = 0;
   for (int i = 0; i < n; ++i) {
-    bt.a[i] = a[i];
-    bt.start[i] = (int)total;
-    total += (long long)a[i].n_new * a[i].B * (a[i].C / kSliceC);
+    if (a[i].n_new <= 0 || a[i].B <= 0) continue;   // nothing to write
+    const int m = bt.n++;
+    bt.a[m] = a[i];
+    bt.lay[m] = batch_layout(a[i]);
+    bt.start[m] = (int)total;
+    total += batch_blocks(a[i], bt.lay[m]);
   }
-  bt.start[n] = (int)total;
+  if (bt.n == 0) return hipSuccess;
+  bt.start[bt.n] = (int)total;
   hipLaunchKernelGGL(k_compress_split_batch, dim3((unsigned)total), dim3(256), 0, s, bt);
   return hipGetLastError();
 }
 
 hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   CompressArgs a = a0;
-  // long windows, or few rows (a decode step): every token of a row loads in parallel
-  if (split_layout(a, false)) {
-    if (a.n_new == 0 || a.B == 0) return hipSuccess;
-    dim3 grid(a.n_new, a.B, a.C / kSliceC);
-    hipLaunchKernelGGL(k_compress_split, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
+  if (a.n_new == 0 || a.B == 0) return hipSuccess;
+  // long windows, or few rows (a decode step): the one-launch kernel with a single call
+  if (batch_layout(a) >= 0) return launch_compress_batch(&a, 1, s);
   const int lanes = a.C / 8;
   const int groups = 256 / lanes;
   // Long runs amortise the extra leading block of overlapping windows; short runs keep
