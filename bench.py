@@ -395,6 +395,47 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"{wl.B}; fp64 NumPy oracle; {dt:.1f} s of host time)"}
 
 
+def achievable_peaks(torch):
+    """Measured ceilings on this GPU, beside the datasheet peaks: HBM bandwidth of a plain
+    device copy of 2 GiB (torch's copy kernel; bytes read + written) and dense bf16 GEMM
+    throughput at 8192^3 (torch.matmul, the vendor BLAS).  Context for the roofline fractions,
+    which stay against the datasheet peaks."""
+    out = {}
+    src = torch.empty(1 << 29, dtype=torch.float32, device="cuda").fill_(1.0)   # 2 GiB
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = 1e9
+    for _ in range(5):
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    out["hbm_copy_GB_per_s"] = 2 * src.numel() * 4 / (best * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        a @ b
+    torch.cuda.synchronize()
+    best = 1e9
+    for _ in range(5):
+        e0.record()
+        a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    out["bf16_gemm_TFLOP_per_s"] = 2 * n ** 3 / (best * 1e-3) / 1e12
+    out["how"] = "best of 5: torch copy of a 2 GiB buffer (read + write bytes); torch.matmul bf16 8192^3"
+    del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -406,6 +447,7 @@ def main():
                     help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compressor-bulk", action="store_true")
+    ap.add_argument("--no-achievable", action="store_true", help="skip the measured HBM / GEMM ceilings")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the hardware-counter workload (calibration copy + eager steps) and exit")
@@ -446,13 +488,22 @@ def main():
             d["TFLOP_per_s"] = costs[f"{name}_flops"] / (t_ms * 1e-3) / 1e12
             d["mfma_frac"] = d["TFLOP_per_s"] / BF16_PEAK_TFLOPS
         calls[name] = d
-    # dominant call of the step
+    # dominant call of the step; its roofline is the one its arithmetic intensity falls under
+    # (algorithmic flops per algorithmic byte against the ridge of the two datasheet peaks)
     dom = max(calls, key=lambda k: calls[k]["ms"])
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if dom == "attend":
-        roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom),
-                "kernel": "csa_attend (k_attend + k_attend_combine)",
-                "hbm_GB_per_s": calls[dom]["GB_per_s"], "hbm_frac": calls[dom]["hbm_frac"]}
+        intensity = costs["attend_flops"] / costs["attend_bytes"]
+        both = {"kernel": "csa_attend (k_attend + k_attend_combine)", "intensity_flop_per_byte": intensity,
+                "ridge_flop_per_byte": ridge, "hbm_GB_per_s": calls[dom]["GB_per_s"], "hbm_frac": calls[dom]["hbm_frac"],
+                "mfma_TFLOP_per_s": calls[dom]["TFLOP_per_s"], "mfma_frac": calls[dom]["mfma_frac"]}
+        if intensity < ridge:
+            roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": calls[dom]["hbm_frac"], "traffic": measured_traffic(wl.name, dom), **both}
+        else:
+            roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom),
+                    **both}
     else:
         roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": calls[dom]["hbm_frac"], "traffic": measured_traffic(wl.name, dom),
@@ -486,6 +537,9 @@ def main():
     if not args.no_compressor_bulk:
         print("[bench] compressor over whole raw streams", file=sys.stderr, flush=True)
         extra["compressor_bulk"] = compressor_bulk(torch)
+    if not args.no_achievable:
+        print("[bench] measured ceilings", file=sys.stderr, flush=True)
+        extra["achievable_peaks"] = achievable_peaks(torch)
     base = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

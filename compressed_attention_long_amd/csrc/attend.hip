@@ -508,7 +508,9 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
 constexpr int kCombineHeads = 4;
 __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
   const int rows = a.B * a.Tq;
-  const int rh = blockIdx.x * kCombineHeads + (threadIdx.x >> 6);   // row * H + head
+  // blocks in the order of the attention grid's XCD ranges: a row's merge runs on the XCD that
+  // wrote its partials
+  const int rh = (int)xcd_remap(blockIdx.x, gridDim.x) * kCombineHeads + (threadIdx.x >> 6);   // row * H + head
   if (rh >= rows * a.H) return;
   const int row = rh / a.H, head = rh % a.H;
   const int d0 = (threadIdx.x & 63) * 8;
