@@ -319,7 +319,7 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   a.lse = lse_out;
   a.slot_cap = slot_cap;
   if (need > 0) {
-    const int ns = csa::attend_nsplit(rows, H, slot_cap, csa_mode);
+    const int ns = csa::attend_plan(rows, H, slot_cap).nsplit;
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = a.part_o + (size_t)rows * ns * H * 512;
   }

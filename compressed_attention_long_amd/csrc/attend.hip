@@ -9,11 +9,12 @@
 // sink and partial-RoPE rows; atlas Raw config fields head_dim 512, one KV head).
 //
 // Kernel design (gfx950, wave64, bf16 MFMA 16x16x32, fp32 accumulation):
-//  * a block = 8 waves = two groups of 4 waves; each group holds 64 heads (16 per wave)
-//    of one query row and one split of its row set.  Tiles of 32 rows are staged in LDS
-//    and used by all 4 waves of a group for both contractions (K = V); the groups take
-//    alternate tiles and merge their softmax states through LDS at the end, so each SIMD
-//    runs two waves whose load, softmax and MFMA phases overlap;
+//  * a block = 8 waves in tile groups: two groups of 4 waves holding 64 heads (32-row tiles),
+//    or four groups of 2 waves holding 32 heads (16-row tiles), 16 heads per wave, for one
+//    query row and one split of its row set.  Tiles are staged in LDS and used by all waves
+//    of a group for both contractions (K = V); the groups take alternate tiles and merge
+//    their softmax states through LDS at the end, so each SIMD runs two waves whose load,
+//    softmax and MFMA phases overlap;
 //  * scores are computed transposed, S^T = K Q^T (M = rows, N = heads, K = channels),
 //    and the output as O^T = V^T P^T (M = channels, N = heads, K = rows): every
 //    accumulator lane then belongs to one head, so the online-softmax statistics,
@@ -32,16 +33,26 @@
 
 namespace csa {
 
-constexpr int kAttWaves = 8;        // two groups of kGroupWaves
-constexpr int kGroupWaves = 4;
+constexpr int kAttWaves = 8;
 constexpr int kAttThreads = kAttWaves * 64;
-constexpr int kHeadsPerBlock = 64;
-constexpr int kTile = 32;           // rows per LDS tile
 constexpr int kD = 512;             // channels (head dim)
 constexpr int kPitch = 520;         // bf16 per LDS row: 1040 B, rows land 4 banks apart
+constexpr int kStepRows = 64;       // rows staged per step (one tile per group); two steps in LDS
 constexpr int kTargetBlocks = 256;  // split until the grid has about this many blocks
-constexpr int kBufs = 4;            // LDS tile buffers: one tile pair consumed while the next is in flight
 constexpr float kRescale = 8.f;     // lazy-rescale threshold (log2 units)
+
+// Block shapes.  HPB = heads per block: 64 (two groups of 4 waves, 32-row tiles) or 32 (four
+// groups of 2 waves, 16-row tiles).  Both stage 64 rows per step; each row read from LDS
+// serves 16 heads per wave either way.  The 32-head shape gives twice the blocks for the same
+// splits, for calls too small to fill the GPU with the 64-head shape; its 16-row tiles take
+// the 16x16x16 MFMA for P V (half the work per instruction), so it is slower per row.
+template <int HPB>
+struct AttCfg {
+  static constexpr int GW = HPB / 16;            // waves per tile group
+  static constexpr int NG = kAttWaves / GW;      // tile groups
+  static constexpr int T = kStepRows / NG;       // rows per tile
+  static constexpr int RPT = T / 8;              // rows of each tile a wave moves per step
+};
 
 __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int window, int stride,
                                                 int n_valid, int cap) {
@@ -83,23 +94,24 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// KVF: the compressed cache's storage (CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1).
-template <bool CSA, int KVF>
+// KVF: the compressed cache's storage (CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1); HPB: the
+// block shape (AttCfg).
+template <bool CSA, int KVF, int HPB>
 __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   constexpr bool QKV = KVF != CSA_BF16;   // quantized entry rows take the register path
   constexpr int kRowB = KVF == CSA_FP8_E4M3 ? kD : (KVF == CSA_FP4_E2M1 ? kD / 2 : 2 * kD);
-  // Four tile buffers as four objects: a pair of tiles is read from one half while the next
-  // pair streams into the other, and separate objects let the compiler see that the LDS
-  // reads never touch the half in flight (it then does not wait for those loads).
-  __shared__ __attribute__((aligned(16))) uint16_t tbA0[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t tbA1[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t tbB0[kTile * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t tbB1[kTile * kPitch];
-  __shared__ __attribute__((aligned(4))) uint8_t tvalid[kBufs][kTile];
+  constexpr int GW = AttCfg<HPB>::GW, NG = AttCfg<HPB>::NG, T = AttCfg<HPB>::T, RPT = AttCfg<HPB>::RPT;
+  // Two halves of tile buffers as two objects: one step's tiles are read from one half while
+  // the next step's stream into the other, and separate objects let the compiler see that the
+  // LDS reads never touch the half in flight (it then does not wait for those loads).  Group
+  // g's tile of a step is rows [g T, (g + 1) T) of the half.
+  __shared__ __attribute__((aligned(16))) uint16_t tbA[kStepRows * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tbB[kStepRows * kPitch];
+  __shared__ __attribute__((aligned(4))) uint8_t tvalid[2 * NG][T];
   __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
-  __shared__ f32x4 mrg_ml[kGroupWaves][kWave];  // group 1's (max, sum, normaliser) per lane, for the merge
+  __shared__ f32x4 mrg_ml[kAttWaves / 2][kWave];  // merging waves' (max, sum, normaliser) per lane
 
-  const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const int HG = (a.H + HPB - 1) / HPB;
   const uint32_t total = gridDim.x;
   const uint32_t logical = xcd_remap(blockIdx.x, total);
   const int hg = logical % HG;
@@ -110,9 +122,9 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
-  const int grp = wave >> 2, hw = wave & 3;                     // tile group, head block
+  const int grp = wave / GW, hw = wave % GW;                    // tile group, head block
   const int n = lane & 15, g = lane >> 4;
-  const int head = hg * kHeadsPerBlock + hw * 16 + n;
+  const int head = hg * HPB + hw * 16 + n;
   const bool head_ok = head < a.H;
 
   const int64_t p = a.q_pos[row];
@@ -132,12 +144,13 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   const int n_slots = n_ent + n_win;
   const int s0 = split * a.slots_per_split;
   const int s1 = min(n_slots, s0 + a.slots_per_split);
-  const int ntile = s1 > s0 ? (s1 - s0 + kTile - 1) / kTile : 0;
+  const int ntile = s1 > s0 ? (s1 - s0 + T - 1) / T : 0;
 
-  // ---- rows.  Wave w moves rows w, w+8, w+16, w+24 of both tiles of a tile pair (tiles 2pr
-  // and 2pr + 1).  Lane k < 8 of the wave prepares the row of tile 2pr + (k >> 2), tile row
-  // w + 8 (k & 3), a pair ahead: its number (a kv row >= 0, -2 - a window row, or -1 for no
-  // row) and its byte offset from the kv base; the loads then take both from that lane.
+  // ---- rows.  A step stages tiles NG pr .. NG pr + NG - 1 (64 rows); wave w moves rows
+  // w + 8 i (i < RPT) of each.  Lane k < 8 of the wave prepares the row of tile
+  // NG pr + k / RPT, tile row w + 8 (k % RPT), a step ahead: its number (a kv row >= 0,
+  // -2 - a window row, or -1 for no row) and its byte offset from the kv base; the loads then
+  // take both from that lane.
   const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * kRowB;
   const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
@@ -150,16 +163,16 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   // it into a row waits until the pair is issued, so the load's latency stays hidden
   auto pair_idx = [&](int pr) -> int {
     const int k = lane & 7;
-    const int t = 2 * pr + (k >> 2);
-    const int slot = s0 + t * kTile + wave + 8 * (k & 3);
+    const int t = NG * pr + k / RPT;
+    const int slot = s0 + t * T + wave + 8 * (k % RPT);
     int j = -1;
     if (CSA && lane < 8 && t < ntile && slot < s1 && slot < n_ent) j = idxrow[slot];
     return j;
   };
   auto pair_rows = [&](int pr, int j) -> PairRows {
     const int k = lane & 7;
-    const int t = 2 * pr + (k >> 2);
-    const int slot = s0 + t * kTile + wave + 8 * (k & 3);
+    const int t = NG * pr + k / RPT;
+    const int slot = s0 + t * T + wave + 8 * (k % RPT);
     int r = -1;
     if (lane < 8 && t < ntile && slot < s1) {
       if (slot >= n_ent) r = -2 - (int)(r_lo + (slot - n_ent));
@@ -171,15 +184,19 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     return PairRows{r, off};
   };
   // bf16 rows go straight into LDS (1 KB per instruction, 16 B per lane).  The valid flags
-  // of a pair are written first; the 8 loads may then be spread over the compute.
+  // of a step are written first; the 8 loads may then be spread over the compute.
   auto mark_pair = [&](int pr, const PairRows& pr_rows, int bnxt) {
     if (lane < 8) {
-      const int t = 2 * pr + (lane >> 2);
-      if (t < ntile) tvalid[bnxt + (lane >> 2)][wave + 8 * (lane & 3)] = pr_rows.r != -1;
+      const int t = NG * pr + lane / RPT;
+      if (t < ntile) tvalid[bnxt + lane / RPT][wave + 8 * (lane % RPT)] = pr_rows.r != -1;
     }
   };
-  auto issue_row = [&](int pr, const PairRows& pr_rows, int k, uint16_t* n0, uint16_t* n1) {
-    const int t = 2 * pr + (k >> 2);
+  // LDS address of lane-k row of a step in a half
+  auto row_dst = [&](uint16_t* half, int k) -> uint16_t* {
+    return half + ((k / RPT) * T + wave + 8 * (k % RPT)) * kPitch;
+  };
+  auto issue_row = [&](int pr, const PairRows& pr_rows, int k, uint16_t* half) {
+    const int t = NG * pr + k / RPT;
     if (t >= ntile) return;
     // fp8/fp4 caches: entry rows take the register path, and empty slots (-1) are zero-filled
     // there, since the bytes of a quantized row read as bf16 may be NaN (masked scores do not
@@ -188,9 +205,8 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(pr_rows.off >> 32), k);
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)pr_rows.off, k);
     const int64_t off = (int64_t)((hi << 32) | lo);
-    uint16_t* dst = (k >> 2) ? n1 : n0;
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kvb + off + 16 * lane),
-                                     (lds_void*)&dst[(wave + 8 * (k & 3)) * kPitch], 16, 0, 0);
+                                     (lds_void*)row_dst(half, k), 16, 0, 0);
   };
   // fp8 / fp4 entry rows: codes and the channel block's scale go through registers and
   // are widened to bf16 (code * scale, rounded; exact for fp4) on the way into LDS.  Lane
@@ -203,7 +219,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
       pre8[k] = u32x2{0u, 0u};
       pres[k] = 0.f;
-      if (2 * pr + (k >> 2) < ntile && r >= 0) {
+      if (NG * pr + k / RPT < ntile && r >= 0) {
         const int64_t rg = (int64_t)b * a.kv_cap + r;
         const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv) + rg * kRowB;
         if (KVF == CSA_FP4_E2M1) pre8[k][0] = *reinterpret_cast<const uint32_t*>(src + 4 * lane);
@@ -212,10 +228,10 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       }
     }
   };
-  auto store_q = [&](int pr, const PairRows& pr_rows, uint16_t* n0, uint16_t* n1) {
+  auto store_q = [&](int pr, const PairRows& pr_rows, uint16_t* half) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int t = 2 * pr + (k >> 2);
+      const int t = NG * pr + k / RPT;
       const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
       if (t < ntile && r >= -1) {
         const float sc = pres[k];
@@ -235,16 +251,15 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
           v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
           v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
         }
-        uint16_t* dst = (k >> 2) ? n1 : n0;
-        *reinterpret_cast<u32x4*>(&dst[(wave + 8 * (k & 3)) * kPitch + 8 * lane]) = v;
+        *reinterpret_cast<u32x4*>(row_dst(half, k) + 8 * lane) = v;
       }
     }
   };
 
-  // ---- prologue: the first two pairs' row numbers are loaded first (they gate the first
-  // tile loads), then the query fragments; the first pair's rows go out as soon as the
+  // ---- prologue: the first two steps' row numbers are loaded first (they gate the first
+  // tile loads), then the query fragments; the first step's rows go out as soon as the
   // numbers arrive, and the rotation table is built while everything is in flight.
-  const int npair = (ntile + 1) / 2;
+  const int npair = (ntile + NG - 1) / NG;
   const int idx0 = pair_idx(0);
   int idx_next = pair_idx(1);
   // the query loads go out before the first tile loads, which wait for the indices: in-order
@@ -258,8 +273,8 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   if (ntile > 0) {
     mark_pair(0, rows0, 0);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) issue_row(0, rows0, k, tbA0, tbA1);
-    if (QKV) { fetch_q(0, rows0); store_q(0, rows0, tbA0, tbA1); }
+    for (int k = 0; k < 8; ++k) issue_row(0, rows0, k, tbA);
+    if (QKV) { fetch_q(0, rows0); store_q(0, rows0, tbA); }
   }
   if (tid < a.rope_dim / 2) {
     float cs, sn;
@@ -310,31 +325,33 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One tile pair: c0/c1 hold pair pr (buffer ids bcur, bcur + 1), n0/n1 receive pair pr + 1.
-  auto pair_step = [&](int pr, const uint16_t* c0, const uint16_t* c1, uint16_t* n0, uint16_t* n1, int bcur) {
-    // this wave's loads of pair pr are the only tile loads outstanding; after the barrier the
-    // pair is visible to all and every wave is done with pair pr - 1, whose buffers take pair
-    // pr + 1; the row numbers of pair pr + 2 are fetched meanwhile
+  // One step: half `cur` holds step pr (buffer ids bcur .. bcur + NG - 1), `nxt` receives
+  // step pr + 1.
+  auto pair_step = [&](int pr, const uint16_t* cur, uint16_t* nxt, int bcur) {
+    // this wave's loads of step pr are the only tile loads outstanding; after the barrier the
+    // step is visible to all and every wave is done with step pr - 1, whose buffers take step
+    // pr + 1; the row numbers of step pr + 2 are fetched meanwhile
     wait_vmcnt<0>();
     __syncthreads();
     const PairRows rows_cur = pair_rows(pr + 1, idx_next);
-    const bool more = pr + 1 < npair;   // false whenever this group has no tile in pair pr
+    const bool more = pr + 1 < npair;   // false whenever this group has no tile in step pr
     if (more) {
-      mark_pair(pr + 1, rows_cur, bcur ^ 2);
+      mark_pair(pr + 1, rows_cur, bcur ^ NG);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) issue_row(pr + 1, rows_cur, k, n0, n1);
+      for (int k = 0; k < 8; ++k) issue_row(pr + 1, rows_cur, k, nxt);
       if (QKV) fetch_q(pr + 1, rows_cur);
     }
     idx_next = pair_idx(pr + 2);
-    const int t = 2 * pr + grp;
+    const int t = NG * pr + grp;
     if (t < ntile) {
     const int buf = bcur + grp;
-    const uint16_t* tl = grp ? c1 : c0;
+    const uint16_t* tl = cur + grp * T * kPitch;
 
     // S^T = K Q^T for rows 16kb + [0,16) of the tile
-    f32x4 sacc[2];
+    constexpr int KB = T / 16;
+    f32x4 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       const uint16_t* rp = &tl[(16 * kb + n) * kPitch + 8 * g];
 #pragma unroll
@@ -346,21 +363,21 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       }
     }
     // online softmax over this tile's rows 16kb + 4g + i (lane's head n)
-    float sv[8];
+    float sv[4 * KB];
     int vmask = 0;
     float tmax = kNegBig;
-    // valid flags of rows 16kb + 4g + [0, 4): one 32-bit LDS read per kb
-    const uint32_t vf0 = *reinterpret_cast<const uint32_t*>(&tvalid[buf][4 * g]);
-    const uint32_t vf1 = *reinterpret_cast<const uint32_t*>(&tvalid[buf][16 + 4 * g]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      // valid flags of rows 16kb + 4g + [0, 4): one 32-bit LDS read
+      const uint32_t vf = *reinterpret_cast<const uint32_t*>(&tvalid[buf][16 * kb + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * kb + i;
-        const bool ok = ((kb ? vf1 : vf0) >> (8 * i)) & 0xffu;
+        const bool ok = (vf >> (8 * i)) & 0xffu;
         sv[e] = sacc[kb][i] * a.scale_log2;
         if (ok) { vmask |= 1 << e; tmax = fmaxf(tmax, sv[e]); }
       }
+    }
     tmax = max_lane_groups(tmax);
     // Lazy rescaling: the reference maximum m_run only moves when a tile's maximum exceeds it
     // by more than kRescale (log2 units), so the 128 output accumulators are rescaled rarely;
@@ -380,68 +397,88 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
       }
       m_run = m_new;
     }
-    float pv[8];
+    float pv[4 * KB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4 * KB; ++e) {
       pv[e] = (vmask >> e & 1) ? fast_exp2(sv[e] - m_run) : 0.f;
       l_run += pv[e];
     }
-    u32x4 pw;
-    pw[0] = pack_bf16x2(pv[0], pv[1]);
-    pw[1] = pack_bf16x2(pv[2], pv[3]);
-    pw[2] = pack_bf16x2(pv[4], pv[5]);
-    pw[3] = pack_bf16x2(pv[6], pv[7]);
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+    uint32_t pw[2 * KB];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) n_run += bf16lo_to_f32(pw[k]) + bf16hi_to_f32(pw[k]);
+    for (int k = 0; k < 2 * KB; ++k) {
+      pw[k] = pack_bf16x2(pv[2 * k], pv[2 * k + 1]);
+      n_run += bf16lo_to_f32(pw[k]) + bf16hi_to_f32(pw[k]);
+    }
 
     // O^T += V^T P^T: A operand (channel 16db + n, rows 16r + 4g + j) via transposing loads
     const int L = lane & 15;
+    if constexpr (KB == 2) {
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&tl[(4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
-      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_i16x4*)&tl[(16 + 4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
-      typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-      const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
+      for (int db = 0; db < 32; ++db) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)&tl[(4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)&tl[(16 + 4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+        typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
+        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
+      }
+    } else {
+      // 16-row tiles: K = 16 rows, the 16x16x16 shape (4 rows per lane, as in S^T's output)
+      const i16x4 pf = __builtin_bit_cast(i16x4, u32x2{pw[0], pw[1]});
+#pragma unroll
+      for (int db = 0; db < 32; ++db) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)&tl[(4 * g + (L >> 2)) * kPitch + 16 * db + 4 * (L & 3)]);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, pf, acc[db], 0, 0, 0);
+      }
     }
     }
-    if (QKV && more) store_q(pr + 1, rows_cur, n0, n1);
+    if (QKV && more) store_q(pr + 1, rows_cur, nxt);
   };
   for (int pr = 0; pr < npair; pr += 2) {
-    pair_step(pr, tbA0, tbA1, tbB0, tbB1, 0);
-    if (pr + 1 < npair) pair_step(pr + 1, tbB0, tbB1, tbA0, tbA1, 2);
+    pair_step(pr, tbA, tbB, 0);
+    if (pr + 1 < npair) pair_step(pr + 1, tbB, tbA, NG);
   }
 
-  // ---- merge group 1's state into group 0 through LDS (the tile buffers are free now)
+  // ---- merge the groups' states into group 0 through LDS (the tile buffers are free now):
+  // rounds halve the number of groups, groups [span, 2 span) handing theirs to group - span
   wait_vmcnt<0>();
   __syncthreads();
-  {
-    // head block hw's 32 KB go to tile buffer hw
-    uint16_t* mb16 = hw == 0 ? tbA0 : (hw == 1 ? tbA1 : (hw == 2 ? tbB0 : tbB1));
-    f32x4* mbuf = reinterpret_cast<f32x4*>(mb16);   // [db][lane]
-    if (grp == 1) {
+#pragma unroll
+  for (int span = NG / 2; span >= 1; span >>= 1) {
+    // writer slot: 32 KB per wave, slots 0-1 in half A, 2-3 in half B
+    auto slot_buf = [&](int sl) -> f32x4* {
+      return reinterpret_cast<f32x4*>((sl < 2 ? tbA : tbB) + (sl & 1) * (32 * kWave * 8));
+    };
+    if (grp >= span && grp < 2 * span) {
+      const int sl = (grp - span) * GW + hw;
+      f32x4* mbuf = slot_buf(sl);   // [db][lane]
 #pragma unroll
       for (int db = 0; db < 32; ++db) mbuf[db * kWave + lane] = acc[db];
-      mrg_ml[hw][lane] = f32x4{m_run, l_run, n_run, 0.f};
+      mrg_ml[sl][lane] = f32x4{m_run, l_run, n_run, 0.f};
     }
     __syncthreads();
-    if (grp == 1) return;
-    const f32x4 ml = mrg_ml[hw][lane];
-    const float M = fmaxf(m_run, ml[0]);
-    const float sa = fast_exp2(m_run - M), sb = fast_exp2(ml[0] - M);
+    if (grp < span) {
+      const int sl = grp * GW + hw;
+      const f32x4* mbuf = slot_buf(sl);
+      const f32x4 ml = mrg_ml[sl][lane];
+      const float M = fmaxf(m_run, ml[0]);
+      const float sa = fast_exp2(m_run - M), sb = fast_exp2(ml[0] - M);
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const f32x4 o = mbuf[db * kWave + lane];
+      for (int db = 0; db < 32; ++db) {
+        const f32x4 o = mbuf[db * kWave + lane];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * sa + o[i] * sb;
+        for (int i = 0; i < 4; ++i) acc[db][i] = acc[db][i] * sa + o[i] * sb;
+      }
+      l_run = l_run * sa + ml[1] * sb;
+      n_run = n_run * sa + ml[2] * sb;
+      m_run = M;
     }
-    l_run = l_run * sa + ml[1] * sb;
-    n_run = n_run * sa + ml[2] * sb;
-    m_run = M;
+    if (span > 1) __syncthreads();
   }
+  if (grp != 0) return;
 
   // ---- epilogue
   float l_tot = sum_lane_groups(l_run);
@@ -585,56 +622,84 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
   if (a.lse && d0 == 0) a.lse[rh] = (M + log2f(Z)) * kLn2;
 }
 
-int attend_nsplit(int rows, int H, int slot_cap, bool csa) {
-  const int HG = (H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+// Splits of the row set for a block shape: enough that the grid has about kTargetBlocks
+// blocks, at most one per two tiles, with the per-split count rounded up to whole tiles.
+static int nsplit_for(int hpb, int rows, int H, int slot_cap) {
+  const int tile = hpb == 64 ? AttCfg<64>::T : AttCfg<32>::T;
+  const int HG = (H + hpb - 1) / hpb;
   const long long base = (long long)rows * HG;
   int ns = (int)((kTargetBlocks + base - 1) / base);
-  const int max_ns = (slot_cap + 2 * kTile - 1) / (2 * kTile);   // at least two tiles per split
+  const int max_ns = (slot_cap + 2 * tile - 1) / (2 * tile);   // at least two tiles per split
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
-  // round the per-split count up to whole tiles, then recount
   int sps = (slot_cap + ns - 1) / ns;
-  sps = (sps + kTile - 1) / kTile * kTile;
-  if (sps < kTile) sps = kTile;
+  sps = (sps + tile - 1) / tile * tile;
+  if (sps < tile) sps = tile;
   return (slot_cap + sps - 1) / sps;
 }
 
-static int attend_sps(int nsplit, int slot_cap) {
-  int sps = (slot_cap + nsplit - 1) / nsplit;
-  sps = (sps + kTile - 1) / kTile * kTile;
-  return sps < kTile ? kTile : sps;
+#ifndef CSA_ATT_HPB
+#define CSA_ATT_HPB 0   // 0: chosen per call; 32 or 64: that shape always
+#endif
+
+// Block shape and splits of a call: 64 heads per block whenever that grid reaches about
+// kTargetBlocks blocks (it does the fewest MFMAs per row: 32-row tiles); 32 heads per block
+// when it cannot (few query rows over short row sets, as in 1M-token decode with top-k),
+// where twice the blocks beat the cost of 16-row tiles.
+AttendPlan attend_plan(int rows, int H, int slot_cap) {
+  AttendPlan pl;
+  int hpb = CSA_ATT_HPB;
+  if (hpb == 0) {
+    const long long blocks64 = (long long)rows * ((H + 63) / 64) * nsplit_for(64, rows, H, slot_cap);
+    hpb = blocks64 < kTargetBlocks ? 32 : 64;
+  }
+  pl.hpb = hpb;
+  pl.nsplit = nsplit_for(hpb, rows, H, slot_cap);
+  const int tile = hpb == 64 ? AttCfg<64>::T : AttCfg<32>::T;
+  int sps = (slot_cap + pl.nsplit - 1) / pl.nsplit;
+  sps = (sps + tile - 1) / tile * tile;
+  pl.sps = sps < tile ? tile : sps;
+  return pl;
 }
 
 size_t attend_workspace(int rows, int H, int slot_cap, bool csa) {
-  const int ns = attend_nsplit(rows, H, slot_cap, csa);
+  (void)csa;
+  const int ns = attend_plan(rows, H, slot_cap).nsplit;
   if (ns <= 1) return 0;
   return (size_t)rows * ns * H * (kD + 4) * sizeof(float) + 256;
+}
+
+template <int HPB>
+static void launch_attend_shape(const AttendArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 blk(kAttThreads);
+  const bool csa = a.csa_mode != 0;
+  switch (a.kv_dtype) {
+    case CSA_FP8_E4M3:
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP8_E4M3, HPB>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_FP8_E4M3, HPB>), grid, blk, 0, s, a);
+      break;
+    case CSA_FP4_E2M1:
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP4_E2M1, HPB>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_FP4_E2M1, HPB>), grid, blk, 0, s, a);
+      break;
+    default:
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_BF16, HPB>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_BF16, HPB>), grid, blk, 0, s, a);
+      break;
+  }
 }
 
 hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   AttendArgs a = a0;
   const int rows = a.B * a.Tq;
-  a.nsplit = attend_nsplit(rows, a.H, a.slot_cap, a.csa_mode != 0);
-  a.slots_per_split = attend_sps(a.nsplit, a.slot_cap);
-  const int HG = (a.H + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const AttendPlan pl = attend_plan(rows, a.H, a.slot_cap);
+  a.nsplit = pl.nsplit;
+  a.slots_per_split = pl.sps;
+  const int HG = (a.H + pl.hpb - 1) / pl.hpb;
   const long long blocks = (long long)rows * HG * a.nsplit;
-  const bool csa = a.csa_mode != 0;
-  dim3 grid((unsigned)blocks);
-  const dim3 blk(kAttThreads);
-  switch (a.kv_dtype) {
-    case CSA_FP8_E4M3:
-      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP8_E4M3>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_attend<false, CSA_FP8_E4M3>), grid, blk, 0, s, a);
-      break;
-    case CSA_FP4_E2M1:
-      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP4_E2M1>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_attend<false, CSA_FP4_E2M1>), grid, blk, 0, s, a);
-      break;
-    default:
-      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_BF16>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_attend<false, CSA_BF16>), grid, blk, 0, s, a);
-      break;
-  }
+  const dim3 grid((unsigned)blocks);
+  if (pl.hpb == 64) launch_attend_shape<64>(a, grid, s);
+  else launch_attend_shape<32>(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nsplit > 1) {

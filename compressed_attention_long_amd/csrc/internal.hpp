@@ -83,7 +83,12 @@ struct AttendArgs {
   float* part_o;          // [rows, nsplit, H, 512]
   float* part_ml;         // [rows, nsplit, H, 4]: reference max, normaliser, exact sum, pad
 };
-int attend_nsplit(int rows, int H, int slot_cap, bool csa);
+struct AttendPlan {
+  int hpb;      // heads per block (64 or 32)
+  int nsplit;   // splits of each query row's row set
+  int sps;      // rows per split (whole tiles)
+};
+AttendPlan attend_plan(int rows, int H, int slot_cap);
 size_t attend_workspace(int rows, int H, int slot_cap, bool csa);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 

@@ -351,6 +351,12 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     ("csa", 4, 1, 64, 6000, [6000, 5000, 512, 100], "fp4", 512, 128, 129, 1 / math.sqrt(512), 4.0),  # CSA2, fp4
     ("csa", 2, 3, 64, 900, [900, 40], "fp4", 300, 128, 140, 1 / math.sqrt(512), 1.0),  # fp4, < k visible
     ("hca", 2, 1, 128, 700, [700, 300], "fp4", 0, 128, 129, 1 / math.sqrt(512), 1.0),  # fp4, dense, splits
+    # enough rows for the 64-head block shape with 16 splits (the small cases above take the
+    # 32-head shape, whose grid is the larger one for them)
+    ("csa", 8, 1, 128, 3000, [3000, 2999, 2500, 2000, 1500, 1200, 1100, 1000], False, 1024, 128, 129,
+     1 / math.sqrt(512), 2.0),
+    ("hca", 8, 1, 128, 2000, [2000, 1999, 1500, 1000, 800, 700, 600, 500], False, 0, 128, 129,
+     1 / math.sqrt(512), 2.0),
 ])
 def test_attend_parity(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul):
     _attend_case(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul, seed=400 + cap + H)
