@@ -543,7 +543,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
 // (row, head) pairs, 8 channels per lane; splits are merged online, four per round, so that a
 // round's (max, sum) and output loads are all in flight together.
 constexpr int kCombineHeads = 4;
-__global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
+__global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArgs a) {
   const int rows = a.B * a.Tq;
   // blocks in the order of the attention grid's XCD ranges: a row's merge runs on the XCD that
   // wrote its partials
@@ -567,8 +567,9 @@ __global__ void __launch_bounds__(256) k_attend_combine(AttendArgs a) {
       ms[u] = s0 + u < a.nsplit ? ml[0] : kNegBig;
       ns[u] = ml[1];
       ls[u] = ml[2];
-      v[u][0] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0);
-      v[u][1] = *reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4);
+      // read once: nontemporal loads keep them from displacing other lines
+      v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0));
+      v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4));
     }
     float Mn = M;
 #pragma unroll
@@ -703,7 +704,8 @@ hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nsplit > 1) {
-    hipLaunchKernelGGL(k_attend_combine, dim3((rows * a.H + kCombineHeads - 1) / kCombineHeads), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attend_combine, dim3((rows * a.H + kCombineHeads - 1) / kCombineHeads),
+                       dim3(64 * kCombineHeads), 0, s, a);
     e = hipGetLastError();
   }
   return e;
