@@ -565,6 +565,7 @@ struct SelShared {
   uint32_t hist[kTopkBins + kTopkBins / 32];
   alignas(16) uint32_t ckey[kCandMax + 4];   // + 4: padding for 16-byte reads of the tail
   alignas(16) int cidx[kCandMax + 4];
+  alignas(16) uint8_t flag[T * NPT];         // selection flags by entry, for the ordered numbering
   int cnt[NPT * W];
   uint32_t red[2 * W];
   int ccount, bstar, above, bcnt, total;
@@ -618,12 +619,59 @@ __device__ __forceinline__ int sel_ranks(SelShared<T, NPT>& sh, uint64_t bits, E
   return sh.total;
 }
 
+// The same numbering through LDS, thread-contiguous: the flags are stored by entry, thread t
+// reads back entries [t NPT, (t + 1) NPT) (one 16-byte read per 16 entries), the per-thread
+// counts are scanned across the block (a wave scan plus the wave totals), and each thread
+// numbers its own entries in order: emit(j, number) with j the entry.  Two barriers and no
+// per-index ballot rounds.  Returns the total.
+template <int T, int NPT, class Emit>
+__device__ __forceinline__ int sel_ranks_contig(SelShared<T, NPT>& sh, uint64_t bits, Emit&& emit) {
+  constexpr int W = T / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) sh.flag[i * T + tid] = (uint8_t)((bits >> i) & 1u);
+  __syncthreads();
+  uint64_t m = 0;
+  auto take4 = [](uint32_t w) -> uint32_t {   // four 0/1 bytes -> four bits
+    return (w & 1u) | ((w >> 7) & 2u) | ((w >> 14) & 4u) | ((w >> 21) & 8u);
+  };
+  if constexpr (NPT % 16 == 0) {
+#pragma unroll
+    for (int q = 0; q < NPT / 16; ++q) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&sh.flag[tid * NPT + 16 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m |= (uint64_t)take4(w[e]) << (16 * q + 4 * e);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < NPT / 4; ++q)
+      m |= (uint64_t)take4(*reinterpret_cast<const uint32_t*>(&sh.flag[tid * NPT + 4 * q])) << (4 * q);
+  }
+  const int c = __popcll(m);
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) sh.red[wave] = (uint32_t)incl;
+  __syncthreads();
+  int pos = incl - c, total = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < W; ++w2) {
+    const int v = (int)sh.red[w2];
+    pos += w2 < wave ? v : 0;
+    total += v;
+  }
+  while (m) {
+    emit(tid * NPT + __builtin_ctzll(m), pos++);
+    m &= m - 1;
+  }
+  return total;
+}
+
 // The selection shared by all top-k kernels.  Lane t of the block holds entries
 // j = i * T + t (i < NPT) of a key array in key[i]; key 0 marks "no entry" (keys of finite
 // scores are never 0).  Selects the min(k, nvalid) entries with the largest keys, the
 // smaller j winning a tie, numbers them in ascending j and calls emit(i, number) for each.
 // Returns the number selected.
 //
+// emit(j, number) receives the entry j itself (not the register index).
 // Keys are counted in 2048 equal-width bins over the current key range [klo, khi]; the bin
 // holding the k-th largest key becomes the next range.  Widths shrink from < 2^32 to
 // < 2^21, < 2^10 and 1, so after at most three rounds the range is a single key; the
@@ -756,7 +804,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
 #pragma unroll
   for (int i = 0; i < NPT; ++i)
     f |= (uint64_t)(ok(i) && (take_all || key[i] > TK || (key[i] == TK && jof(i) <= I))) << i;
-  return sel_ranks<T, NPT>(sh, f, emit);
+  return sel_ranks_contig<T, NPT>(sh, f, emit);
 }
 
 // Scores of entries j < n starting at s, read once with coalesced loads (index clamped into
@@ -782,8 +830,8 @@ __global__ void __launch_bounds__(T) k_topk_reg(IndexArgs a) {
   int32_t* out = a.idx_out + (int64_t)row * k;
   uint32_t key[NPT];
   load_score_keys<T, NPT>(a.scores + (int64_t)row * a.cap, nvis, key);
-  const int tot = select_keys<T, NPT>(sh, key, nvis, k, [&](int i, int pos) {
-    if (pos < k) out[pos] = i * T + (int)threadIdx.x;
+  const int tot = select_keys<T, NPT>(sh, key, nvis, k, [&](int j, int pos) {
+    if (pos < k) out[pos] = j;
   });
   for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += T) out[p2] = -1;
 }
@@ -805,10 +853,11 @@ __global__ void __launch_bounds__(T) k_topk_chunk(IndexArgs a) {
   uint32_t key[NPT];
   load_score_keys<T, NPT>(a.scores + (int64_t)row * a.cap + base, n, key);
   const int64_t slot0 = ((int64_t)row * P + pch) * k;
-  const int tot = select_keys<T, NPT>(sh, key, n, k, [&](int i, int pos) {
+  const float* srow = a.scores + (int64_t)row * a.cap + base;
+  const int tot = select_keys<T, NPT>(sh, key, n, k, [&](int j, int pos) {
     if (pos < k) {
-      a.cand_key[slot0 + pos] = key[i];
-      a.cand_idx[slot0 + pos] = base + i * T + (int)threadIdx.x;
+      a.cand_key[slot0 + pos] = okey(srow[j]);   // the selected entry's key, read again
+      a.cand_idx[slot0 + pos] = base + j;
     }
   });
   for (int p2 = min(tot, k) + threadIdx.x; p2 < k; p2 += T) {
@@ -847,13 +896,13 @@ __global__ void __launch_bounds__(T) k_topk_merge(IndexArgs a, const uint32_t* i
   }
   int32_t* out = a.idx_out + (int64_t)row * k;
   const int64_t ob = ((int64_t)row * out_chunks + q) * k;
-  const int tot = select_keys<T, NPT>(sh, key, nvalid, k, [&](int i, int pos) {
+  const int tot = select_keys<T, NPT>(sh, key, nvalid, k, [&](int j, int pos) {
     if (pos >= k) return;
-    const int32_t gi = in_idx[base + i * T + (int)threadIdx.x];
+    const int32_t gi = in_idx[base + j];
     if (FINAL) {
       out[pos] = gi;
     } else {
-      out_key[ob + pos] = key[i];
+      out_key[ob + pos] = in_key[base + j];
       out_idx[ob + pos] = gi;
     }
   });
