@@ -546,13 +546,19 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
   return op(b[0], b[1]);
 }
 // inclusive prefix sum across the 64 lanes
+// DPP only: shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes without a source add 0),
+// then lane 15 of rows 0 and 2 into rows 1 and 3, then lane 31 into rows 2 and 3.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add_src(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xf, true);
+}
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  x += dpp_add_src<0x111, 0xf>(x);   // row_shr:1
+  x += dpp_add_src<0x112, 0xf>(x);   // row_shr:2
+  x += dpp_add_src<0x114, 0xf>(x);   // row_shr:4
+  x += dpp_add_src<0x118, 0xf>(x);   // row_shr:8
+  x += dpp_add_src<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_add_src<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
   return x;
 }
 
@@ -771,7 +777,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
         if (m == 0) continue;
         int base = 0;
         if (lane == 0) base = atomicAdd(&sh.ccount, __popcll(m));
-        base = __shfl(base, 0, kWave);
+        base = __builtin_amdgcn_readlane(base, 0);   // every lane is active here
         const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         if (c && slot < kCandMax) { sh.ckey[slot] = key[i]; sh.cidx[slot] = jof(i); }
