@@ -290,7 +290,8 @@ def compressor_bulk(torch, reps=3):
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_bytes_csa_decode_65k.md")
 
 
-CALL_SOURCES = {"attend": "attend.hip", "index": "indexer.hip", "compress": "compress.hip"}
+CALL_SOURCES = {"attend": ("attend.hip",), "index": ("indexer.hip", "compress_dev.hpp"),
+                "compress": ("compress.hip", "compress_dev.hpp")}
 
 
 def source_digest(call):
@@ -298,7 +299,7 @@ def source_digest(call):
     for the code it was measured on."""
     import hashlib
     h = hashlib.sha256()
-    for f in (CALL_SOURCES[call], "api.hip", "common.hpp", "internal.hpp"):
+    for f in (*CALL_SOURCES[call], "api.hip", "common.hpp", "internal.hpp"):
         with open(os.path.join(ROOT, "compressed_attention_long_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -322,7 +323,8 @@ def measured_traffic(workload, call):
 def pmc_probe(wl, torch, layers_n=4, reps=2):
     """Workload for hardware-counter passes: a plain 256 MiB device copy three times (calibrates
     FETCH_SIZE / WRITE_SIZE against a known byte count), then `reps` eager steps over `layers_n`
-    distinct layers, every C-ABI call launched on its own."""
+    distinct layers, every C-ABI call launched on its own (compress, index, attend as three
+    calls, so that the counters split by call)."""
     src = torch.empty(64 << 20, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -332,7 +334,7 @@ def pmc_probe(wl, torch, layers_n=4, reps=2):
     layers = build_layers(wl, layers_n, "cuda", torch, torch.bfloat16)
     for _ in range(reps):
         for L in layers:
-            L.run()
+            L.run(combined=False)
     torch.cuda.synchronize()
     print(json.dumps({"pmc_probe": wl.name, "copy_bytes_each_way": 256 << 20, "layers": layers_n, "reps": reps,
                       "sources": {c: source_digest(c) for c in CALL_SOURCES}}), flush=True)

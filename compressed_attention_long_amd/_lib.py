@@ -25,6 +25,7 @@ EXPORTS = (
     "csa_compress_batch",
     "csa_index_topk",
     "csa_index_topk_workspace_bytes",
+    "csa_index_topk_compress",
     "csa_attend",
     "csa_attend_workspace_bytes",
     "hca_attend",
@@ -81,6 +82,8 @@ _SIGS = {
     "csa_compress_batch": (_i32, [ctypes.POINTER(CCompressCall), _i32, _vp]),
     "csa_index_topk": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _PC, _i32, _vp, _vp, _vp, _sz, _vp]),
     "csa_index_topk_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "csa_index_topk_compress": (_i32, [ctypes.POINTER(CCompressCall), _i32, _vp, _vp, _vp, _i32, _i32, _i32, _PC,
+                                       _i32, _vp, _vp, _vp, _sz, _vp]),
     "csa_attend": (_i32, [_vp, _vp, _i32, _i32, _i32, _PC, _vp, _i32, _PC, _i32, _vp, _vp, _i32, _f32,
                           _vp, _i32, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -188,9 +191,9 @@ def compress(kv: torch.Tensor, logits: Optional[torch.Tensor], out: Cache, first
     _check("csa_compress", rc)
 
 
-def compress_batch(calls, stream=None):
-    """csa_compress_batch: calls = [(kv, logits, out, first_row, n_new, inv_freq, rope_dim), ...],
-    each as for compress(); one launch when every call is small."""
+def _compress_calls(calls):
+    """csa_compress_call_t array (and the cache structs it points to, kept alive) for calls =
+    [(kv, logits, out, first_row, n_new, inv_freq, rope_dim), ...]."""
     n = len(calls)
     arr = (CCompressCall * max(n, 1))()
     keep = []
@@ -203,7 +206,14 @@ def compress_batch(calls, stream=None):
         B, T, _ = kv.shape
         arr[i] = CCompressCall(kv.data_ptr(), _ptr(logits), kv.stride(1), kv.stride(0), B, T, first_row, n_new,
                                ctypes.pointer(c), _ptr(inv_freq), rope_dim)
-    rc = load().csa_compress_batch(arr, n, _stream(stream))
+    return arr, keep
+
+
+def compress_batch(calls, stream=None):
+    """csa_compress_batch: calls = [(kv, logits, out, first_row, n_new, inv_freq, rope_dim), ...],
+    each as for compress(); one launch when every call is small."""
+    arr, keep = _compress_calls(calls)
+    rc = load().csa_compress_batch(arr, len(calls), _stream(stream))
     _check("csa_compress_batch", rc)
 
 
@@ -225,6 +235,23 @@ def index_topk(q_idx: torch.Tensor, w: torch.Tensor, q_pos: torch.Tensor, keys: 
                                topk, idx_out.data_ptr(), _ptr(scores_out), _ptr(workspace), ws_bytes,
                                _stream(stream))
     _check("csa_index_topk", rc)
+
+
+def index_topk_compress(calls, q_idx: torch.Tensor, w: torch.Tensor, q_pos: torch.Tensor, keys: Cache, topk: int,
+                        idx_out: torch.Tensor, scores_out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """csa_index_topk_compress: compress_batch(calls) and index_topk(...) with fewer launches."""
+    assert q_idx.dtype == torch.bfloat16 and q_idx.is_contiguous()
+    assert w.dtype == torch.float32 and w.is_contiguous() and q_pos.dtype == torch.int64
+    assert idx_out.dtype == torch.int32 and idx_out.is_contiguous()
+    arr, keep = _compress_calls(calls)
+    B, Tq, Hi, _ = q_idx.shape
+    c = keys.struct()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().csa_index_topk_compress(arr, len(calls), q_idx.data_ptr(), w.data_ptr(), q_pos.data_ptr(), B, Tq,
+                                        Hi, ctypes.byref(c), topk, idx_out.data_ptr(), _ptr(scores_out),
+                                        _ptr(workspace), ws_bytes, _stream(stream))
+    _check("csa_index_topk_compress", rc)
 
 
 def csa_attend_workspace_bytes(B, Tq, H, topk, W) -> int:

@@ -186,14 +186,19 @@ size_t csa_index_topk_workspace_bytes(int B, int Tq, int Hi, int cap, int topk) 
   return index_scores_bytes(B, Tq, cap) + csa::topk_workspace(B * Tq, cap, topk);
 }
 
-int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int B, int Tq, int Hi,
-                   const csa_cache_t* keys, int topk, int32_t* idx_out, float* scores_out, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+// Validation and argument block of an index/top-k call; `empty` when there is nothing to do.
+static int index_args(const void* q_idx, const float* w, const int64_t* q_pos, int B, int Tq, int Hi,
+                      const csa_cache_t* keys, int topk, int32_t* idx_out, float* scores_out, void* workspace,
+                      size_t workspace_bytes, csa::IndexArgs& a, bool& empty) {
+  empty = false;
   int rc = check_cache(keys, "keys", true);
   if (rc) return rc;
   REQUIRE(B >= 0 && Tq >= 0, CSA_EINVAL, "B and Tq must be >= 0");
   REQUIRE(topk >= 1 && topk <= keys->cap, CSA_EINVAL, "topk must be in [1, cap=%d] (got %d)", keys->cap, topk);
-  if (B == 0 || Tq == 0) return ok();
+  if (B == 0 || Tq == 0) {
+    empty = true;
+    return CSA_OK;
+  }
   REQUIRE(q_idx && w && q_pos && idx_out, CSA_EINVAL, "q_idx, w, q_pos and idx_out must be non-NULL");
   REQUIRE(Hi >= 1 && Hi <= 64, CSA_ENOTSUP, "Hi must be in [1, 64] (got %d)", Hi);
   REQUIRE(keys->C == 128, CSA_ENOTSUP, "indexer key dim must be 128 (got %d)", keys->C);
@@ -216,7 +221,7 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int 
   if (scores_out) REQUIRE(aligned(scores_out, 16), CSA_EINVAL, "scores_out must be 16-byte aligned");
   float* scores = scores_out ? scores_out : static_cast<float*>(workspace);
   uint8_t* cand = static_cast<uint8_t*>(workspace) + sc_bytes;
-  csa::IndexArgs a{};
+  a = csa::IndexArgs{};
   a.q_idx = q_idx;
   a.w = w;
   a.q_pos = q_pos;
@@ -236,8 +241,90 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int 
   a.scores = scores;
   a.idx_out = idx_out;
   if (plan.mode == 1) a.cand_key = reinterpret_cast<uint32_t*>(cand);   // carved by the launcher
+  return CSA_OK;
+}
+
+int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos, int B, int Tq, int Hi,
+                   const csa_cache_t* keys, int topk, int32_t* idx_out, float* scores_out, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  csa::IndexArgs a;
+  bool empty;
+  const int rc = index_args(q_idx, w, q_pos, B, Tq, Hi, keys, topk, idx_out, scores_out, workspace,
+                            workspace_bytes, a, empty);
+  if (rc) return rc;
+  if (empty) return ok();
   hipError_t e = csa::launch_index_scores(a, stream);
   REQUIRE(e == hipSuccess, CSA_EHIP, "index score launch failed: %s", hipGetErrorString(e));
+  e = csa::launch_topk(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "top-k launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// Byte range [lo, hi) of a device buffer, for the overlap checks of the combined call.
+struct Span {
+  uintptr_t lo, hi;
+};
+static Span span(const void* p, size_t bytes) {
+  const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+  return Span{u, u + (p ? bytes : 0)};
+}
+static bool overlap(Span x, Span y) { return x.lo < y.hi && y.lo < x.hi; }
+
+int csa_index_topk_compress(const csa_compress_call_t* calls, int n_calls, const void* q_idx, const float* w,
+                            const int64_t* q_pos, int B, int Tq, int Hi, const csa_cache_t* keys, int topk,
+                            int32_t* idx_out, float* scores_out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  REQUIRE(n_calls >= 0, CSA_EINVAL, "n_calls must be >= 0 (got %d)", n_calls);
+  REQUIRE(n_calls == 0 || calls != nullptr, CSA_EINVAL, "calls is NULL");
+  std::vector<csa::CompressArgs> todo;
+  for (int i = 0; i < n_calls; ++i) {
+    const csa_compress_call_t& c = calls[i];
+    csa::CompressArgs ca;
+    bool cempty;
+    const int rc = compress_args(c.kv, c.logits, c.ld_tok, c.ld_seq, c.B, c.T_raw, c.first_row, c.n_new, c.out,
+                                 c.inv_freq, c.rope_dim, ca, cempty);
+    if (rc) {
+      g_err = "call " + std::to_string(i) + ": " + g_err;
+      return rc;
+    }
+    if (!cempty) todo.push_back(ca);
+  }
+  csa::IndexArgs a;
+  bool empty;
+  const int rc = index_args(q_idx, w, q_pos, B, Tq, Hi, keys, topk, idx_out, scores_out, workspace,
+                            workspace_bytes, a, empty);
+  if (rc) return rc;
+  if (!empty) {
+    // the compressor's outputs must not be anything the indexer reads or writes
+    const int64_t rows = (int64_t)B * Tq;
+    const size_t key_elt = keys->dtype == CSA_BF16 ? 2 : 1;
+    const Span ins[] = {
+        span(keys->data, (size_t)keys->cap * keys->C * key_elt * B),
+        span(keys->scales, (size_t)keys->cap * 4 * B),
+        span(q_idx, (size_t)rows * Hi * keys->C * 2),
+        span(w, (size_t)rows * Hi * 4),
+        span(a.scores, (size_t)rows * keys->cap * 4),
+        span(idx_out, (size_t)rows * topk * 4),
+        span(workspace, workspace ? workspace_bytes : 0),
+    };
+    for (size_t i = 0; i < todo.size(); ++i) {
+      const csa::CompressArgs& ca = todo[i];
+      const size_t row_b = ca.dtype == CSA_BF16 ? 2 * (size_t)ca.C : (ca.dtype == CSA_FP8_E4M3 ? ca.C : ca.C / 2);
+      const Span outs[] = {span(ca.out, row_b * ca.cap * ca.B),
+                           span(ca.scales, ca.scales ? (size_t)ca.cap * (ca.C / ca.scale_block) * 4 * ca.B : 0)};
+      for (const Span& o : outs)
+        for (const Span& x : ins)
+          REQUIRE(!overlap(o, x), CSA_EINVAL, "compress output of call %d overlaps an indexer buffer", (int)i);
+    }
+  }
+  hipError_t e = hipSuccess;
+  if (empty) {
+    if (!todo.empty()) e = csa::launch_compress_batch(todo.data(), (int)todo.size(), stream);
+    REQUIRE(e == hipSuccess, CSA_EHIP, "compress launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+  e = csa::launch_index_scores_compress(a, todo.data(), (int)todo.size(), stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "index score / compress launch failed: %s", hipGetErrorString(e));
   e = csa::launch_topk(a, stream);
   REQUIRE(e == hipSuccess, CSA_EHIP, "top-k launch failed: %s", hipGetErrorString(e));
   return ok();

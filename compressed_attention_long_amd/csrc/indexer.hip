@@ -25,8 +25,7 @@
 // or key == T and j <= I, in ascending index order.  Bins that are linear in the key
 // (uniform in value within a binade) keep LDS atomics spread out even when all scores
 // crowd into one binade.
-#include "common.hpp"
-#include "internal.hpp"
+#include "compress_dev.hpp"
 
 namespace csa {
 
@@ -61,10 +60,11 @@ constexpr int kIdxWaves = 4;
 constexpr int kDepth = 4;                // score-tile loads in flight per wave
 constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
 
+// One block of the decode scores grid: query row `row` (b * Tq + t), entries from
+// chunk * kIdxEntPerBlock.
 template <int HB, bool FP8>
-__global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
+__device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, int chunk) {
   __shared__ float sbuf[kIdxWaves][kIdxTilesPerWave * 16];
-  const int row = blockIdx.x;                 // query row (b * Tq + t)
   const int b = row / a.Tq;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
   const int64_t qp = a.q_pos[row];
   const int nvis = visible_rows(qp, a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   float* srow = a.scores + (int64_t)row * a.cap;
-  const int base = blockIdx.y * kIdxEntPerBlock + wave * (kIdxTilesPerWave * 16);
+  const int base = chunk * kIdxEntPerBlock + wave * (kIdxTilesPerWave * 16);
 
   // query fragments: A operand, row = head (hb*16 + n), k = 8g + i <-> channel 32g + 8s + i
   bf16x8 qf[HB][4];
@@ -173,6 +173,23 @@ __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
     const int j = base + i;
     if (j < a.cap) srow[j] = j < nvis ? sbuf[wave][i] : -INFINITY;
   }
+}
+
+template <int HB, bool FP8>
+__global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
+  index_scores_block<HB, FP8>(a, blockIdx.x, blockIdx.y);
+}
+
+// The same grid with a decode step's compress blocks after it (csa_index_topk_compress): the
+// compressor writes only the KV and window caches, which the scores do not read, so its
+// short, latency-bound blocks run beside the scores blocks instead of in a launch of their
+// own.  Blocks [0, n_idx) are the scores grid in launch order (row fastest).
+template <int HB, bool FP8>
+__global__ void __launch_bounds__(256) k_index_scores_compress(IndexArgs a, CompressBatch cb, int n_idx) {
+  const int L = blockIdx.x;
+  const int rows = a.B * a.Tq;
+  if (L < n_idx) index_scores_block<HB, FP8>(a, L % rows, L / rows);
+  else compress_batch_block(cb, L - n_idx);
 }
 
 // ---------------------------------------------------------------- scores, many query rows
@@ -324,6 +341,32 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   }
   CSA_IDX_LAUNCH(1) CSA_IDX_LAUNCH(2) CSA_IDX_LAUNCH(3) CSA_IDX_LAUNCH(4)
 #undef CSA_IDX_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs* calls, int n, hipStream_t s) {
+  const int rows = a.B * a.Tq;
+  const int HB = (a.Hi + 15) / 16;
+  const bool f8 = a.key_dtype == CSA_FP8_E4M3;
+  const bool mq = !f8 && a.Tq >= kMqRows && a.Di == 128;
+  CompressBatch cb;
+  long long total = 0;
+  if (mq || !make_compress_batch(calls, n, cb, total) || cb.n == 0) {
+    if (n > 0) {
+      const hipError_t e = launch_compress_batch(calls, n, s);
+      if (e != hipSuccess) return e;
+    }
+    return launch_index_scores(a, s);
+  }
+  const long long n_idx = (long long)rows * ((a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
+  const dim3 grid((unsigned)(n_idx + total));
+#define CSA_IDX_FUSED(hb)                                                                                        \
+  if (HB == hb) {                                                                                                \
+    if (f8) hipLaunchKernelGGL((k_index_scores_compress<hb, true>), grid, dim3(256), 0, s, a, cb, (int)n_idx);  \
+    else hipLaunchKernelGGL((k_index_scores_compress<hb, false>), grid, dim3(256), 0, s, a, cb, (int)n_idx);    \
+  }
+  CSA_IDX_FUSED(1) CSA_IDX_FUSED(2) CSA_IDX_FUSED(3) CSA_IDX_FUSED(4)
+#undef CSA_IDX_FUSED
   return hipGetLastError();
 }
 

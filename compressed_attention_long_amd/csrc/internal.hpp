@@ -50,6 +50,10 @@ struct TopkPlan {
 TopkPlan topk_plan(int rows, int cap, int k);
 size_t topk_workspace(int rows, int cap, int k);   // candidate area of the two-stage plan
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
+// the scores launch carrying compress calls (the batch layouts of launch_compress_batch); falls
+// back to separate launches when the calls need the run-mode kernel or the scores take the
+// many-row kernel
+hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs* calls, int n, hipStream_t s);
 hipError_t launch_topk(const IndexArgs& a, hipStream_t s);
 
 struct AttendArgs {

@@ -66,14 +66,24 @@ class LayerStep:
         self.z_raw = tensors["z_raw"]
         self.new_raw = self.kv_raw[:, self.kv_raw.shape[1] - meta["new_tok"]:]
 
-    def compress(self, stream=None):
-        """The completed entries and the raw-window write, in one batched call."""
+    def compress_calls(self):
+        """The completed entries and the raw-window write of this step."""
         m = self.meta
         calls = []
         if m["n_new_entries"] > 0:
             calls.append((self.kv_raw, self.z_raw, self.kv, m["E_pre"], m["n_new_entries"], self.inv_freq, self.wl.R))
         calls.append((self.new_raw, None, self.win, m["win_first_new"], m["new_tok"], self.inv_freq, self.wl.R))
-        ops.compress_batch(calls, stream)
+        return calls
+
+    def compress(self, stream=None):
+        """The step's compress calls, in one batched call."""
+        ops.compress_batch(self.compress_calls(), stream)
+
+    def index_compress(self, stream=None):
+        """The compress calls and the indexer / top-k in one combined call (fewer launches)."""
+        wl = self.wl
+        ops.index_topk_compress(self.compress_calls(), self.t["q_idx"], self.t["w"], self.t["q_pos"], self.keys,
+                                wl.topk, self.idx, scores_out=self.scores, workspace=self.idx_ws, stream=stream)
 
     def index(self, stream=None):
         wl = self.wl
@@ -89,10 +99,15 @@ class LayerStep:
             ops.hca_attend(self.t["q"], self.t["q_pos"], self.kv, self.win, wl.W, self.t["sink"], self.inv_freq,
                            wl.R, self.scale, self.out, self.lse, self.att_ws, stream)
 
-    def run(self, stream=None):
-        self.compress(stream)
-        if self.wl.mode == "csa":
-            self.index(stream)
+    def run(self, stream=None, combined: bool = True):
+        """The whole step.  A CSA step issues its compress calls with the indexer through the
+        combined call unless `combined` is False (then as two calls)."""
+        if self.wl.mode == "csa" and combined:
+            self.index_compress(stream)
+        else:
+            self.compress(stream)
+            if self.wl.mode == "csa":
+                self.index(stream)
         self.attend(stream)
 
 

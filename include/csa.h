@@ -196,6 +196,28 @@ int csa_index_topk(const void* q_idx, const float* w, const int64_t* q_pos,
 size_t csa_index_topk_workspace_bytes(int B, int Tq, int Hi, int cap, int topk);
 
 /*
+ * csa_index_topk_compress — a decode step's compress calls and its indexer / top-k with
+ * fewer launches.
+ *
+ * Same effect as csa_compress_batch(calls, n_calls, stream) followed by csa_index_topk(...)
+ * with the remaining arguments (the steps of one CSA layer, "DeepSeek-V4-Pro vs Inkling",
+ * Component-by-component table, CSA row).  The compressor writes only the caches named in
+ * `calls`, which the indexer does not read, so small calls (a decode step's new entry and
+ * raw-window write) run as extra blocks of the indexer's scores launch.  Calls that need
+ * the compressor's many-row kernel, or scores taken by the many-query-row kernel (bf16 keys
+ * with Tq >= 16), fall back to separate launches with the same result.  The workspace is
+ * csa_index_topk's.
+ * Errors: as for the two calls (a bad compress call's message starts "call i: "), and
+ * CSA_EINVAL when a compress output (cache data or scales) overlaps the indexer's keys,
+ * key scales, q_idx, w, scores_out, idx_out or workspace.
+ */
+int csa_index_topk_compress(const csa_compress_call_t* calls, int n_calls,
+                            const void* q_idx, const float* w, const int64_t* q_pos,
+                            int B, int Tq, int Hi, const csa_cache_t* keys, int topk,
+                            int32_t* idx_out, float* scores_out,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * csa_attend — shared-KV multi-query attention over the selected entries and
  * the sliding window, with a per-head sink and the output's inverse rotation.
  *

@@ -113,6 +113,33 @@ def test_index_topk_validation():
                                                                               L.CSA_ENOTSUP)
 
 
+def test_index_topk_compress_validation():
+    lib = L.load()
+    keys = cache(C=128)
+    out = cache()
+    ok_call = L.CCompressCall(FAKE, FAKE, 512, 512 * 64, 1, 64, 0, 4, ctypes.pointer(out), FAKE, 64)
+    bad_call = L.CCompressCall(None, FAKE, 512, 512 * 64, 1, 64, 0, 4, ctypes.pointer(out), FAKE, 64)
+
+    def run(calls, n, B=1, keys_=keys):
+        arr = (L.CCompressCall * max(len(calls), 1))(*calls)
+        return rc_msg(lib.csa_index_topk_compress(arr, n, FAKE, FAKE, FAKE, B, 1, 64, ctypes.byref(keys_), 16,
+                                                  FAKE, FAKE, None, 0, None))
+
+    rc, msg = run([ok_call, bad_call], 2)
+    assert rc == L.CSA_EINVAL and msg.startswith("call 1:")
+    assert run([ok_call], 1, keys_=cache(C=256))[0] == L.CSA_ENOTSUP          # the indexer's own checks
+    # a compress output that is the key cache itself (same device address) is refused
+    alias = cache()
+    alias.data = keys.data
+    alias_call = L.CCompressCall(FAKE, FAKE, 512, 512 * 64, 1, 64, 0, 4, ctypes.pointer(alias), FAKE, 64)
+    rc, msg = run([alias_call], 1)
+    assert rc == L.CSA_EINVAL and "overlaps" in msg
+    assert lib.csa_index_topk_compress(None, 0, FAKE, FAKE, FAKE, 0, 1, 64, ctypes.byref(keys), 16, FAKE, FAKE,
+                                       None, 0, None) == L.CSA_OK              # nothing to do: no launch
+    assert lib.csa_index_topk_compress(None, 1, FAKE, FAKE, FAKE, 0, 1, 64, ctypes.byref(keys), 16, FAKE, FAKE,
+                                       None, 0, None) == L.CSA_EINVAL
+
+
 def attend(kv, win, topk=16, H=128, W=128, ws=None, wsb=0, out_dtype=L.CSA_FP32, rope=64, hca=False, B=32):
     lib = L.load()
     if hca:

@@ -149,3 +149,46 @@ def test_v41flash_csa2_decode_1m_fp4_with_reuse():
         o, l = O.attend(np64(r["q"][b, 0]), qp, X, np64(r["sink"]), oracle_scale(wl), fo)
         check_attention(np64(rs.out[b, 0]), o, f"reuse layer b={b}")
         np.testing.assert_allclose(rs.lse[b, 0].cpu().numpy(), l, atol=1e-4)
+
+
+@pytest.mark.parametrize("name", ["v4pro_csa_decode_65k", "v41flash_csa2_decode_1m_fp4", "v4pro_csa_decode_65k_mtp4",
+                                  "v4pro_csa_prefill_4k_on_131k"])
+def test_combined_compress_index_call_equals_separate_calls(name):
+    """csa_index_topk_compress writes bit for bit what csa_compress_batch + csa_index_topk write:
+    the compress blocks riding in the scores launch (decode), or the separate launches it falls
+    back to (the prefill chunk: many-row compress and the many-query-row scores kernel)."""
+    wl = ci.WORKLOADS[name]
+    print(f"\n[gpu case] combined call {name}", flush=True)
+    t, meta = ci.step_tensors(wl, DEV)
+    step = LayerStep(wl, t, meta, out_dtype=torch.float32)
+    e0, ne = meta["E_pre"], meta["n_new_entries"]
+    w0, nw = meta["win_first_new"], meta["new_tok"]
+
+    def clear():
+        step.kv.data[:, e0:e0 + ne].zero_()
+        if step.kv.scales is not None:
+            step.kv.scales[:, e0:e0 + ne].zero_()
+        step.win.data[:, w0:w0 + nw].zero_()
+        step.idx.fill_(-7)
+        step.scores.zero_()
+        torch.cuda.synchronize()
+
+    def state():
+        s = [step.kv.data[:, e0:e0 + ne].clone(), step.win.data[:, w0:w0 + nw].clone(), step.idx.clone(),
+             step.scores.clone()]
+        if step.kv.scales is not None:
+            s.append(step.kv.scales[:, e0:e0 + ne].clone())
+        return s
+
+    clear()
+    step.compress()
+    step.index()
+    torch.cuda.synchronize()
+    ref = state()
+    clear()
+    step.index_compress()
+    torch.cuda.synchronize()
+    got = state()
+    for i, (x, y) in enumerate(zip(got, ref)):
+        assert torch.equal(x, y), f"{name}: output {i} differs between the combined and the separate calls"
+    assert torch.count_nonzero(ref[0]) > 0
