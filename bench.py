@@ -125,8 +125,10 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
 
     Headline: layer steps replayed from one HIP graph that chains all rotated layers (as a
     serving loop replays a model's layers), K steps = K // L chain replays plus K % L
-    single-layer graphs.  Also: one graph per layer step (includes a graph launch per step),
-    and an eager pass with events around each C-ABI call on the launch stream.
+    single-layer graphs.  Also: one graph per layer step (includes a graph launch per step);
+    per C-ABI call, a graph of that call over the rotated layers replayed between HIP events
+    on the launch stream (the per-call times and the roofline); and an eager pass with events
+    around each call (host launch gaps included, for reference).
     """
     n_layers = max(2, min(max_layers, math.ceil(min_cache_bytes / max(layer_bytes(wl), 1))))
     layers = build_layers(wl, n_layers, "cuda", torch, torch.bfloat16)
@@ -164,7 +166,35 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps_n
     graph_gpu = g0.elapsed_time(g1) / steps_n
-    # --- eager pass with per-call events (breakdown and roofline)
+    # --- per-call graphs: one C-ABI call per layer, replayed between events (breakdown, roofline)
+    call_fns = {"compress": lambda L: L.compress(), "attend": lambda L: L.attend()}
+    if wl.mode == "csa":
+        call_fns["index"] = lambda L: L.index()
+        call_fns["index_compress"] = lambda L: L.index_compress()
+    reps = max(2, steps_n // n_layers)
+    calls_graph = {}
+    for name, fn in call_fns.items():
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for L in layers:
+                fn(L)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            for L in layers:
+                fn(L)
+        cg.replay()
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(reps):
+            cg.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        calls_graph[name] = g0.elapsed_time(g1) / (reps * n_layers)
+        del cg
+    # --- eager pass with per-call events (reference: includes host launch gaps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps_n)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -189,6 +219,7 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
         per["step_gpu"].append(e[0].elapsed_time(e[3]))
     med = lambda xs: sorted(xs)[len(xs) // 2]
     out = {k: sum(v) / len(v) for k, v in per.items()}
+    out["calls_graph"] = calls_graph
     out["step_gpu_median"] = med(per["step_gpu"])
     out["wall_ms_per_step"] = wall
     out["graph_gpu_ms_per_step"] = graph_gpu
@@ -478,11 +509,16 @@ def main():
     tokens = wl.B * wl.Tq
     value = tokens / (ms / 1e3)
     calls = {}
-    for name in ("compress", "index", "attend"):
-        if name == "index" and wl.mode != "csa":
+    for name in ("compress", "index", "index_compress", "attend"):
+        if name not in tm["calls_graph"]:
             continue
-        t_ms = tm[name]
-        d = {"ms": t_ms}
+        t_ms = tm["calls_graph"][name]
+        d = {"ms": t_ms, "eager_event_ms": tm.get(name)}
+        if name == "index_compress":
+            d["GB_per_s"] = (costs["index_bytes"] + costs["compress_bytes"]) / (t_ms * 1e-3) / 1e9
+            d["hbm_frac"] = d["GB_per_s"] / HBM_PEAK_GBS
+            calls[name] = d
+            continue
         if f"{name}_bytes" in costs:
             d["GB_per_s"] = costs[f"{name}_bytes"] / (t_ms * 1e-3) / 1e9
             d["hbm_frac"] = d["GB_per_s"] / HBM_PEAK_GBS
@@ -492,7 +528,7 @@ def main():
         calls[name] = d
     # dominant call of the step; its roofline is the one its arithmetic intensity falls under
     # (algorithmic flops per algorithmic byte against the ridge of the two datasheet peaks)
-    dom = max(calls, key=lambda k: calls[k]["ms"])
+    dom = max((k for k in calls if k != "index_compress"), key=lambda k: calls[k]["ms"])
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if dom == "attend":
         intensity = costs["attend_flops"] / costs["attend_bytes"]
@@ -512,7 +548,10 @@ def main():
                 "kernel": "csa_index_topk (k_index_scores + k_topk)" if dom == "index" else "csa_compress"}
     extra = {"calls": calls, "timing": "value = tokens / wall time of layer steps replayed from one HIP graph "
                                        "chaining the rotated layers; per_layer_graph = one graph launch per step; "
-                                       "calls = eager pass with HIP events around each C-ABI call",
+                                       "calls[*].ms = per C-ABI call, a HIP graph of that call over the rotated "
+                                       "layers replayed between HIP events on the launch stream (average per call); "
+                                       "calls[*].eager_event_ms = events around each call in an eager pass (host "
+                                       "launch gaps included)",
              "graph_gpu_ms_per_step": tm["graph_gpu_ms_per_step"], "eager_wall_ms_per_step": tm["eager_wall_ms_per_step"],
              "per_layer_graph_ms_per_step": tm["per_layer_graph_wall_ms_per_step"],
              "step_gpu_ms": tm["step_gpu"], "step_gpu_median_ms": tm["step_gpu_median"],
@@ -524,12 +563,14 @@ def main():
         print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
         t2 = time_workload(w2, max(10, args.steps // 2), args.warmup, torch)
         c2 = algorithmic_costs(w2)
+        cg2 = t2["calls_graph"]
         e2 = {"ms_per_step": t2["wall_ms_per_step"], "tokens_per_s": w2.B * w2.Tq / (t2["wall_ms_per_step"] / 1e3),
-              "attend_ms": t2["attend"], "attend_TFLOP_per_s": c2["attend_flops"] / (t2["attend"] * 1e-3) / 1e12,
-              "attend_GB_per_s": c2["attend_bytes"] / (t2["attend"] * 1e-3) / 1e9, "compress_ms": t2["compress"]}
+              "attend_ms": cg2["attend"], "attend_TFLOP_per_s": c2["attend_flops"] / (cg2["attend"] * 1e-3) / 1e12,
+              "attend_GB_per_s": c2["attend_bytes"] / (cg2["attend"] * 1e-3) / 1e9, "compress_ms": cg2["compress"]}
         if w2.mode == "csa":
-            e2["index_ms"] = t2["index"]
-            e2["index_GB_per_s"] = c2["index_bytes"] / (t2["index"] * 1e-3) / 1e9
+            e2["index_ms"] = cg2["index"]
+            e2["index_GB_per_s"] = c2["index_bytes"] / (cg2["index"] * 1e-3) / 1e9
+            e2["index_compress_ms"] = cg2["index_compress"]
         if w2.reuse > 0:
             tr = time_reuse(w2, max(10, args.steps // 2), args.warmup, torch)
             avg = (t2["wall_ms_per_step"] + w2.reuse * tr) / (1 + w2.reuse)
