@@ -407,8 +407,8 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   a.slot_cap = slot_cap;
   if (need > 0) {
     const int ns = csa::attend_plan(rows, H, slot_cap).nsplit;
-    a.part_o = static_cast<float*>(workspace);
-    a.part_ml = a.part_o + (size_t)rows * ns * H * 512;
+    a.part_o = static_cast<uint16_t*>(workspace);
+    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)rows * ns * H * 512);
   }
   a.csa_mode = csa_mode ? 1 : 0;
   hipError_t e;

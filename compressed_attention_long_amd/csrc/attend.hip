@@ -526,20 +526,42 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     }
     if (a.lse && g == 0) a.lse[(int64_t)row * a.H + head] = (m_run + log2f(l_tot)) * kLn2;
   } else {
-    const int64_t pr = ((int64_t)row * a.nsplit + split) * a.H + head;
+    // The split's normalised output o / n in fp16 (11-bit significand: rounding within 2^-11
+    // relative, far below the error the bf16 inputs carry), scaled by 2^-e so that the head's
+    // largest magnitude sits below 2^14 whatever the range of the cache values; (m, n, l, e)
+    // stay fp32.  Half the bytes of fp32 partials, written here and read by the merge.
+    float amax = 0.f;
 #pragma unroll
     for (int db = 0; db < 32; ++db)
-      *reinterpret_cast<f32x4*>(a.part_o + pr * kD + 16 * db + 4 * g) = acc[db];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[db][i]));
+    amax = max_lane_groups(amax);
+    const float inv_n = n_tot > 0.f ? 1.f / n_tot : 0.f;
+    int e = 0;
+    if (amax * inv_n > 0.f) {
+      int ex;
+      (void)frexpf(amax * inv_n, &ex);   // amax / n = f 2^ex, f in [0.5, 1)
+      e = ex - 14;
+    }
+    const float sc = ldexpf(inv_n, -e);
+    const int64_t pr = ((int64_t)row * a.nsplit + split) * a.H + head;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      u32x2 h;
+      h[0] = pack_f16x2(acc[db][0] * sc, acc[db][1] * sc);
+      h[1] = pack_f16x2(acc[db][2] * sc, acc[db][3] * sc);
+      *reinterpret_cast<u32x2*>(a.part_o + pr * kD + 16 * db + 4 * g) = h;
+    }
     if (g == 0) {
-      *reinterpret_cast<f32x4*>(a.part_ml + 4 * pr) = f32x4{m_run, n_tot, l_tot, 0.f};
+      *reinterpret_cast<f32x4*>(a.part_ml + 4 * pr) = f32x4{m_run, n_tot, l_tot, (float)e};
     }
   }
 }
 
-// Merge split partials: M = max(sink, m_s), o = sum 2^(m_s - M) o_s / Zo with
-// Zo = 2^(sink - M) + sum n_s 2^(m_s - M) (n_s: the sum of the weights as rounded for the
-// split's PV product), lse = M + log2(2^(sink - M) + sum l_s 2^(m_s - M)) with the exact
-// sums l_s; then rotate back and store.  A block of 256 lanes merges 4
+// Merge split partials: M = max(sink, m_s), o = sum 2^(m_s - M) n_s u_s / Zo with u_s = o_s / n_s
+// (stored in fp16 times 2^-e_s) and Zo = 2^(sink - M) + sum n_s 2^(m_s - M) (n_s: the sum of the
+// weights as rounded for the split's PV product), lse = M + log2(2^(sink - M) + sum l_s
+// 2^(m_s - M)) with the exact sums l_s; then rotate back and store.  A block of 256 lanes merges 4
 // (row, head) pairs, 8 channels per lane; splits are merged online, four per round, so that a
 // round's (max, sum) and output loads are all in flight together.
 constexpr int kCombineHeads = 4;
@@ -558,8 +580,8 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
   float M = sink2, Z = 1.f, Zo = 1.f;   // relative to 2^M
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
-    f32x4 v[4][2];
-    float ms[4], ns[4], ls[4];
+    u32x4 v[4];
+    float ms[4], ns[4], ls[4], es[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t pr = base + (int64_t)min(s0 + u, a.nsplit - 1) * a.H;
@@ -567,9 +589,9 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
       ms[u] = s0 + u < a.nsplit ? ml[0] : kNegBig;
       ns[u] = ml[1];
       ls[u] = ml[2];
+      es[u] = ml[3];
       // read once: nontemporal loads keep them from displacing other lines
-      v[u][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0));
-      v[u][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.part_o + pr * kD + d0 + 4));
+      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.part_o + pr * kD + d0));
     }
     float Mn = M;
 #pragma unroll
@@ -584,10 +606,12 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
       const float w = exp2f(ms[u] - Mn);   // 0 for the padding of a partial round
       Z += ls[u] * w;
       Zo += ns[u] * w;
+      const float wo = ldexpf(ns[u] * w, (int)es[u]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] += w * v[u][0][i];
-        o[4 + i] += w * v[u][1][i];
+      for (int k = 0; k < 4; ++k) {
+        const f32x2 h = unpack_f16x2(v[u][k]);
+        o[2 * k] += wo * h[0];
+        o[2 * k + 1] += wo * h[1];
       }
     }
     M = Mn;
@@ -667,7 +691,8 @@ size_t attend_workspace(int rows, int H, int slot_cap, bool csa) {
   (void)csa;
   const int ns = attend_plan(rows, H, slot_cap).nsplit;
   if (ns <= 1) return 0;
-  return (size_t)rows * ns * H * (kD + 4) * sizeof(float) + 256;
+  // fp16 partial outputs, then fp32 (m, n, l, e): the latter start 16-byte aligned (kD even)
+  return (size_t)rows * ns * H * (kD * sizeof(uint16_t) + 4 * sizeof(float)) + 256;
 }
 
 template <int HPB>

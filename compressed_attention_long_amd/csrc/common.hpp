@@ -30,6 +30,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// ---------------------------------------------------------------- fp16
+
+// fp32 -> IEEE binary16, two values (round to nearest even: the conversion's default mode);
+// and back, exactly.
+typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t w) {
+  const f16x2_t v = __builtin_bit_cast(f16x2_t, w);
+  return f32x2{(float)v[0], (float)v[1]};
+}
+
 // ---------------------------------------------------------------- fp8 e4m3fn (OCP)
 
 // Two codes (bytes 0,1 or 2,3 of `w`) -> two fp32 values; gfx950's converter reads OCP E4M3FN.

@@ -84,8 +84,8 @@ struct AttendArgs {
   float* lse;
   // split-KV partials
   int nsplit, slot_cap, slots_per_split;
-  float* part_o;          // [rows, nsplit, H, 512]
-  float* part_ml;         // [rows, nsplit, H, 4]: reference max, normaliser, exact sum, pad
+  uint16_t* part_o;       // [rows, nsplit, H, 512] fp16: o / n times 2^-e
+  float* part_ml;         // [rows, nsplit, H, 4]: reference max, normaliser n, exact sum, e
 };
 struct AttendPlan {
   int hpb;      // heads per block (64 or 32)
