@@ -401,6 +401,45 @@ def test_attend_bf16_output_and_determinism():
     assert torch.all((o16.double() - ref).abs() <= spacing)
 
 
+def test_attend_workspace_reused_across_calls():
+    # One workspace serves split calls of 4, then 2, then 4 query rows (different splits, so
+    # different partial layouts): each output must equal that of a fresh workspace bit for bit,
+    # whatever the previous call left there.
+    B, H, cap, topk, W = 4, 128, 4000, 1024, 128
+    d = ci.Draw(5, "cpu")
+    q = d.normal((B, 1, H, 512), std=1 / math.sqrt(512)).to(DEV)
+    sink = d.normal((H,), dtype=torch.float32).to(DEV)
+    kv = ops.Cache(d.normal((B, cap, 512)).to(DEV), torch.full((B,), cap, dtype=torch.int32, device=DEV),
+                   torch.zeros(B, dtype=torch.int64, device=DEV), 8, 4)
+    qp = 4 * cap + 7
+    win = ops.Cache(d.normal((B, W, 512)).to(DEV), torch.full((B,), W, dtype=torch.int32, device=DEV),
+                    torch.full((B,), qp - W + 1, dtype=torch.int64, device=DEV), 1, 1)
+    q_pos = torch.full((B, 1), qp, dtype=torch.int64, device=DEV)
+    rng = np.random.default_rng(5)
+    idx = torch.from_numpy(np.stack([np.sort(rng.choice(cap, topk, replace=False)) for _ in range(B)])
+                           .astype(np.int32).reshape(B, 1, topk)).to(DEV)
+    fg, _ = inv_freq_pair(64)
+    scale = 1 / math.sqrt(512)
+
+    def sub(c, n):
+        return ops.Cache(c.data[:n], c.n_valid[:n], c.pos0[:n], c.window, c.stride)
+
+    def call(n, ws):
+        out = torch.empty((n, 1, H, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((n, 1, H), dtype=torch.float32, device=DEV)
+        ops.csa_attend(q[:n], q_pos[:n], sub(kv, n), idx[:n], sub(win, n), W, sink, fg, 64, scale, out, lse, ws)
+        return out, lse
+
+    need = ops.csa_attend_workspace_bytes(B, 1, H, topk, W)
+    assert need > 0 and ops.csa_attend_workspace_bytes(2, 1, H, topk, W) <= need
+    shared = ops.workspace(need, DEV)
+    for n in (B, 2, B):
+        got = call(n, shared)
+        ref = call(n, ops.workspace(ops.csa_attend_workspace_bytes(n, 1, H, topk, W), DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"{n} rows"
+
+
 # ---------------------------------------------------------------- tiny decode from raw tokens
 
 def test_tiny_csa_decode_end_to_end():
