@@ -131,6 +131,37 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   const int head = hg * HPB + hw * 16 + n;
   const bool head_ok = head < a.H;
 
+  // ---- loads that need only the block's coordinates go out first, ahead of the row set's
+  // scalars: the first two steps' top-k indices (for CSA the split and topk bound them), the
+  // block's query rows and the rotation frequencies
+  const int s0 = split * a.slots_per_split;
+  const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
+  // the raw top-k index behind lane k's row (CSA entries only), loaded a step ahead; turning
+  // it into a row waits until the step is issued, so the load's latency stays hidden
+  auto pair_idx = [&](int pr) -> int {
+    const int k = lane & 7;
+    const int t = NG * pr + k / RPT;
+    const int slot = s0 + t * T + wave + 8 * (k % RPT);
+    int j = -1;
+    if (CSA && lane < 8 && slot < s0 + a.slots_per_split && slot < a.topk) j = idxrow[slot];
+    return j;
+  };
+  const int idx0 = pair_idx(0);
+  int idx_next = pair_idx(1);
+  // the block's HPB query rows (1 KB each) go straight into the second tile half, row h at
+  // h kPitch, once for both tile groups; wave w moves rows w, w + 8, ...
+  {
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)row * a.H * (2 * kD);
+#pragma unroll
+    for (int i = 0; i < HPB / kAttWaves; ++i) {
+      const int hl = wave + kAttWaves * i;
+      const int hq = min(hg * HPB + hl, a.H - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qb + (int64_t)hq * (2 * kD) + 16 * lane),
+                                       (lds_void*)(tbB + hl * kPitch), 16, 0, 0);
+    }
+  }
+  const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
+
   const int64_t p = a.q_pos[row];
 
   // ---- the row set of this query: entries, then window rows
@@ -146,7 +177,6 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   if (r_hi > w_nv - 1) r_hi = w_nv - 1;
   const int n_win = (a.W > 0 && r_hi >= r_lo) ? (int)(r_hi - r_lo + 1) : 0;
   const int n_slots = n_ent + n_win;
-  const int s0 = split * a.slots_per_split;
   const int s1 = min(n_slots, s0 + a.slots_per_split);
   const int ntile = s1 > s0 ? (s1 - s0 + T - 1) / T : 0;
 
@@ -155,23 +185,12 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   // NG pr + k / RPT, tile row w + 8 (k % RPT), a step ahead: its number (a kv row >= 0,
   // -2 - a window row, or -1 for no row) and its byte offset from the kv base; the loads then
   // take both from that lane.
-  const int32_t* idxrow = CSA ? a.idx + (int64_t)row * a.topk : nullptr;
   const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * kRowB;
   const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
   const int64_t win_off = winb - kvb;   // window rows are addressed from the kv base too
   struct PairRows {
     int r;          // row number (lanes 0..7)
     int64_t off;    // byte offset of the row from kvb (any valid row when there is none)
-  };
-  // the raw top-k index behind lane k's row (CSA entries only), loaded a pair ahead; turning
-  // it into a row waits until the pair is issued, so the load's latency stays hidden
-  auto pair_idx = [&](int pr) -> int {
-    const int k = lane & 7;
-    const int t = NG * pr + k / RPT;
-    const int slot = s0 + t * T + wave + 8 * (k % RPT);
-    int j = -1;
-    if (CSA && lane < 8 && t < ntile && slot < s1 && slot < n_ent) j = idxrow[slot];
-    return j;
   };
   auto pair_rows = [&](int pr, int j) -> PairRows {
     const int k = lane & 7;
@@ -260,19 +279,10 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     }
   };
 
-  // ---- prologue: the first two steps' row numbers are loaded first (they gate the first
-  // tile loads), then the query fragments; the first step's rows go out as soon as the
-  // numbers arrive, and the rotation table is built while everything is in flight.
+  // ---- prologue: the first step's rows go out as soon as their indices arrive (the query
+  // loads behind them complete later, in order), and the rotation table is built while
+  // everything is in flight
   const int npair = (ntile + NG - 1) / NG;
-  const int idx0 = pair_idx(0);
-  int idx_next = pair_idx(1);
-  // the query loads go out before the first tile loads, which wait for the indices: in-order
-  // completion then lets the query rotation start while those tiles are still in flight
-  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + min(head, a.H - 1)) * kD;
-  u32x4 qraw[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
-  const double fr = tid < a.rope_dim / 2 ? a.inv_freq[tid] : 0.0;
   const PairRows rows0 = pair_rows(0, idx0);
   if (ntile > 0) {
     mark_pair(0, rows0, 0);
@@ -285,6 +295,23 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
     rope_cs(p, fr, cs, sn);
     rtab[tid] = f32x2{cs, sn};
   }
+  // the query rows have landed once only this wave's first-step tile loads, issued after them,
+  // may still be in flight (quantized rows have completed all loads in store_q already)
+  if (!QKV) {
+    switch (ntile > 0 ? min(8, ntile * RPT) : 0) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<1>(); break;
+      case 2: wait_vmcnt<2>(); break;
+      case 3: wait_vmcnt<3>(); break;
+      case 4: wait_vmcnt<4>(); break;
+      case 5: wait_vmcnt<5>(); break;
+      case 6: wait_vmcnt<6>(); break;
+      case 7: wait_vmcnt<7>(); break;
+      default: wait_vmcnt<8>(); break;
+    }
+  } else {
+    wait_vmcnt<0>();
+  }
   __syncthreads();
   // ---- query fragments (B operand of S^T = K Q^T): head = n, channels 32c + 8g + [0, 8).
   // The rotated query is not a bf16 value: its last two chunks (channels 448..511, which
@@ -294,9 +321,10 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   bf16x8 qlo[2];
   {
     const int rot0 = kD - a.rope_dim;
+    const uint16_t* qs = tbB + (hw * 16 + n) * kPitch + 8 * g;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      u32x4 v = head_ok ? qraw[c] : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qs + 32 * c) : u32x4{0u, 0u, 0u, 0u};
       u32x4 lo = {0u, 0u, 0u, 0u};
       if (32 * c + 32 > rot0 && a.rope_dim > 0) {
 #pragma unroll
