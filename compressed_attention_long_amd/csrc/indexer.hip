@@ -136,14 +136,14 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
       for (int s = 0; s < 4; ++s) {
         u32x4 kb;
         if (FP8) {
-          // 8 codes (channels 32g + 8s .. +8) -> 8 bf16, exactly
+          // 8 codes (channels 32g + 8s .. +8) -> 8 bf16, exactly: gfx950's scaled converter with
+          // scale 1 takes two E4M3FN codes straight to a bf16 pair (every E4M3 value is a bf16
+          // value; checked bit for bit against the fp32 converter over all finite code pairs)
 #pragma unroll
           for (int h2 = 0; h2 < 2; ++h2) {
-            uint32_t w = cur[2 * s + h2];
-            f32x2 lo = fp8x2_lo(w), hi = fp8x2_hi(w);
-            // upper halves of two fp32 values (exact bf16 images of E4M3 values) in one v_perm
-            kb[2 * h2] = __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u);
-            kb[2 * h2 + 1] = __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u);
+            const uint32_t w = cur[2 * s + h2];
+            kb[2 * h2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+            kb[2 * h2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
           }
         } else {
           kb[0] = cur[4 * s]; kb[1] = cur[4 * s + 1]; kb[2] = cur[4 * s + 2]; kb[3] = cur[4 * s + 3];
