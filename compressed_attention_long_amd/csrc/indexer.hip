@@ -59,6 +59,7 @@ constexpr int kIdxTilesPerWave = 32;     // 16 entries per tile
 constexpr int kIdxWaves = 4;
 constexpr int kDepth = 4;                // score-tile loads in flight per wave
 constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
+static_assert(kIdxTilesPerWave % kDepth == 0, "whole ring rounds stay inside a wave's tiles");
 
 // One block of the decode scores grid: query row `row` (b * Tq + t), entries from
 // chunk * kIdxEntPerBlock.
@@ -116,18 +117,38 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
   };
 
   // kDepth tiles in flight per wave: the loads of tile t + kDepth are issued as tile t is
-  // consumed, from a ring of register buffers indexed at compile time.
+  // consumed, from a ring of register buffers indexed at compile time.  The loop is software
+  // pipelined by one tile: tile t's products are issued before tile t - 1's ReLU-weighted head
+  // sum, which does not depend on them, so the matrix cores run while the vector ALU works.
   uint32_t ring[kDepth][KR];
   int ntile = 0;
   if (base < nvis) ntile = min(kIdxTilesPerWave, (nvis - base + 15) / 16);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d)
     load_tile(base + 16 * min(d, max(ntile - 1, 0)), ring[d]);
+  // Straight-line body: the loop runs whole ring rounds (tiles past ntile recompute the last
+  // tile's rows and land in sbuf slots whose entries are not visible), and the first round's
+  // head sum of "tile -1" lands in tile 0's slots, rewritten a step later.
+  f32x4 prev[HB];            // products of the previous tile, awaiting their head sum
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) prev[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float prev_scale = 1.f;
+  int tprev = 0;
+  auto finish = [&](const f32x4 (&acc)[HB], float kscale, int t) {
+    float sc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc += wv[hb][i] * relu(acc[hb][i]);
+    sc = sum_lane_groups(sc);
+    if (FP8) sc *= kscale;
+    // staged in LDS: global stores inside the loop would count against vmcnt and stall the ring
+    if (g == 0) sbuf[wave][16 * t + n] = sc;
+  };
   for (int t0 = 0; t0 < ntile; t0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       const int t = t0 + d;
-      if (t >= ntile) break;
       uint32_t (&cur)[KR] = ring[d];
       f32x4 acc[HB];
 #pragma unroll
@@ -156,17 +177,14 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
       const float kscale = FP8 ? __uint_as_float(cur[KW]) : 1.f;
       // next load for this ring slot (past the last tile it re-reads that tile: an L2 hit)
       load_tile(base + 16 * min(t + kDepth, ntile - 1), ring[d]);
-      float sc = 0.f;
+      finish(prev, prev_scale, tprev);
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc += wv[hb][i] * relu(acc[hb][i]);
-      sc = sum_lane_groups(sc);
-      if (FP8) sc *= kscale;
-      // staged in LDS: global stores inside the loop would count against vmcnt and stall the ring
-      if (g == 0) sbuf[wave][16 * t + n] = sc;
+      for (int hb = 0; hb < HB; ++hb) prev[hb] = acc[hb];
+      prev_scale = kscale;
+      tprev = t;
     }
   }
+  if (ntile > 0) finish(prev, prev_scale, tprev);
   // write this wave's scores, coalesced; entries past the visible count score -inf
 #pragma unroll
   for (int i = lane; i < kIdxTilesPerWave * 16; i += 64) {
