@@ -182,6 +182,8 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (2, 37, 64, 3000, [3000, 2100], False, 256, "causal"),     # multi-row kernel: ragged row groups, causal
     (1, 16, 40, 1300, [1290], False, 64, "causal"),            # multi-row kernel, heads not a multiple of 16
     (1, 1, 64, 140000, [140000], True, 512, "end"),            # CSA2 selection: top-512 of a long row (chunked)
+    (1, 128, 4, 40000, [40000], True, 256, "end"),             # 128 rows, one block each: 48 entries per lane
+    (1, 128, 4, 60000, [59000], False, 512, "end"),            # 128 rows, one block each: 64 entries per lane
 ])
 def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
     d = ci.Draw(200 + cap, "cpu")
