@@ -325,14 +325,38 @@ CALL_SOURCES = {"attend": ("attend.hip",), "index": ("indexer.hip", "compress_de
                 "compress": ("compress.hip", "compress_dev.hpp")}
 
 
+def code_only(text):
+    """C++ source without its comments and blank space: what the compiler sees, so that an edit to
+    a comment does not count as a change of the kernels."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":                       # string or character literal, escapes kept
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(" ".join(line.split()) for line in "".join(out).splitlines() if line.strip())
+
+
 def source_digest(call):
-    """sha256 over the sources of one C-ABI call's kernels: counter-derived traffic is only reported
-    for the code it was measured on."""
+    """sha256 over the code (comments and blank space dropped) of one C-ABI call's kernel sources:
+    counter-derived traffic is only reported for the code it was measured on."""
     import hashlib
     h = hashlib.sha256()
     for f in (*CALL_SOURCES[call], "api.hip", "common.hpp", "internal.hpp"):
-        with open(os.path.join(ROOT, "compressed_attention_long_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "compressed_attention_long_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -23,10 +23,13 @@
 //    contraction;
 //  * the V^T operand is read from the same row-major LDS tile with the gfx950
 //    transposing LDS load (ds_read_b64_tr_b16), so no transposed copy is stored;
+//  * the block's query rows reach LDS by DMA once (both tile groups read their fragments
+//    there), issued at entry together with the first top-k indices, ahead of the scalar
+//    loads that size the row set;
 //  * the sink joins the denominator once, in the epilogue (one split) or the split merge;
 //  * lazy rescaling: the reference maximum moves only when a tile exceeds it by 2^8;
 //  * several splits of the row set run in parallel when the query rows alone cannot
-//    fill the GPU; their (max, sum, unnormalised output) partials are merged by
+//    fill the GPU; their (max, sums, normalised fp16 output) partials are merged by
 //    k_attend_combine.  With one split the kernel normalises, rotates and stores.
 #include "common.hpp"
 #include "internal.hpp"
