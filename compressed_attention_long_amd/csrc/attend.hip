@@ -264,11 +264,15 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
         if (r == -1) {
         } else if (KVF == CSA_FP4_E2M1) {
+          // gfx950's scaled converter: byte i (channels 2i, 2i + 1 in its low and high nibbles)
+          // times the block's power-of-two scale, to a bf16 pair; exact, as code x scale fits
+          // bf16 (checked bit for bit against the E2M1 definition for every byte and every
+          // power-of-two scale 2^-127 .. 2^127)
           const uint32_t w = pre8[k][0];
-          const float hs = 0.5f * sc;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            v[i] = pack_bf16x2(fp4_e2m1_scaled(w >> (8 * i), hs), fp4_e2m1_scaled(w >> (8 * i + 4), hs));
+          v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+          v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+          v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+          v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
         } else {
           const f32x2 f0 = fp8x2_lo(pre8[k][0]), f1 = fp8x2_hi(pre8[k][0]);
           const f32x2 f2 = fp8x2_lo(pre8[k][1]), f3 = fp8x2_hi(pre8[k][1]);

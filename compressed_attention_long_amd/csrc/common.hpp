@@ -87,15 +87,6 @@ __device__ __forceinline__ uint32_t f32_to_fp4_e2m1(float x) {
   return code == 0 ? 0u : (code | ((__float_as_uint(x) >> 28) & 8u));
 }
 
-// E2M1 code (low 4 bits of c) times a scale; `half_scale` is half the block's scale.  Twice
-// the magnitude is an integer (0, 1, 2, 3, 4, 6, 8, 12), so the product is exact.
-__device__ __forceinline__ float fp4_e2m1_scaled(uint32_t c, float half_scale) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const uint32_t twice = e ? ((2u | m) << (e - 1)) : m;
-  const float v = (float)twice * half_scale;
-  return (c & 8u) ? -v : v;
-}
-
 // ---------------------------------------------------------------- rotary
 
 // (cos, sin) of pos * inv_freq, returned in fp32.  The angle is formed in fp64 and reduced
