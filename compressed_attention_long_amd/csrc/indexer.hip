@@ -788,6 +788,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
 #pragma unroll
         for (int e = 0; e < BPT; ++e) sh.hist[hslot(kTopkBins - 1 - (BPT * tid + e))] = 0;   // next round
         __syncthreads();
+        if (tid == 0) sh.ccount = 0;   // for the candidate collection below; unused within rounds
         int pre = incl - sum;
 #pragma unroll
         for (int w2 = 0; w2 < W; ++w2) pre += w2 < wave ? (int)sh.red[w2] : 0;
@@ -828,9 +829,8 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
       I = sh.I;
     } else {
       // at most kCandMax keys in [klo, khi]: collect them (one slot reservation per wave and
-      // index i), then rank each among all by (key desc, index asc)
-      if (tid == 0) sh.ccount = 0;
-      __syncthreads();
+      // index i), then rank each among all by (key desc, index asc).  The count was zeroed in
+      // the last histogram round, between its barriers.
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
         const bool c = ok(i) && key[i] >= klo && key[i] <= khi;
@@ -845,9 +845,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
       }
       __syncthreads();
       const int c = min(sh.ccount, kCandMax);
-      if (tid < 4) { sh.ckey[c + tid] = 0u; sh.cidx[c + tid] = 0x7fffffff; }
-      __syncthreads();
-      const int c4 = (c + 3) >> 2;
+      const int c4 = (c + 3) >> 2;   // the last group of four reads past c: masked below
       for (int ci = tid; ci < c; ci += T) {
         const uint32_t v = sh.ckey[ci];
         const int ji = sh.cidx[ci];
@@ -857,7 +855,8 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
           const u32x4 vo = *reinterpret_cast<const u32x4*>(&sh.ckey[4 * o4]);
           const u32x4 jo = *reinterpret_cast<const u32x4*>(&sh.cidx[4 * o4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) rank += (vo[e] > v || (vo[e] == v && (int)jo[e] < ji)) ? 1 : 0;
+          for (int e = 0; e < 4; ++e)
+            rank += (4 * o4 + e < c && (vo[e] > v || (vo[e] == v && (int)jo[e] < ji))) ? 1 : 0;
         }
         if (rank == need - 1) { sh.TK = v; sh.I = ji; }
       }
