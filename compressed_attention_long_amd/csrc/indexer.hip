@@ -991,8 +991,10 @@ __global__ void __launch_bounds__(T) k_topk_merge(IndexArgs a, const uint32_t* i
 #ifndef CSA_TOPK_SINGLE_MAX
 #define CSA_TOPK_SINGLE_MAX 16384   // rows up to this length always take one block
 #endif
-constexpr int kChunk = 8192;        // stage-1 entries per block
-constexpr int kMergeCands = 8192;   // candidates per merge block
+// 16,384 entries per stage-1 block and candidates per merge block: a 262,143-entry row takes
+// one chunk stage and one merge (23.5 us for 4 rows, against 25.6 in three stages with 8,192)
+constexpr int kChunk = 16384;       // stage-1 entries per block
+constexpr int kMergeCands = 16384;  // candidates per merge block
 TopkPlan topk_plan(int rows, int cap, int k) {
   TopkPlan pl{};
   if (cap <= CSA_TOPK_SINGLE_MAX || (cap <= 65536 && rows >= 128)) {
@@ -1031,10 +1033,12 @@ static void launch_merge(int n, bool final_stage, dim3 grid, hipStream_t s, cons
                      group, out_key, out_idx, out_count)
   if (final_stage) {
     if (n <= 4096) CSA_TOPK_MERGE(4, true);
-    else CSA_TOPK_MERGE(8, true);
+    else if (n <= 8192) CSA_TOPK_MERGE(8, true);
+    else CSA_TOPK_MERGE(16, true);
   } else {
     if (n <= 4096) CSA_TOPK_MERGE(4, false);
-    else CSA_TOPK_MERGE(8, false);
+    else if (n <= 8192) CSA_TOPK_MERGE(8, false);
+    else CSA_TOPK_MERGE(16, false);
   }
 #undef CSA_TOPK_MERGE
 }

@@ -176,7 +176,8 @@ def test_workspace_sizes_scale_with_work():
     b = L.hca_attend_workspace_bytes(16, 1, 128, 4096, 128)
     assert a > 0 and b > 0
     assert L.index_topk_workspace_bytes(32, 1, 64, 16383, 1024) >= 32 * 16383 * 4
-    assert L.index_topk_workspace_bytes(4, 1, 64, 262143, 1024) >= 4 * 262143 * 4 + 4 * 32 * 1024 * 8
+    # scores plus the stage-1 candidates of 16 chunks of 16,384 entries (key + index each)
+    assert L.index_topk_workspace_bytes(4, 1, 64, 262143, 1024) >= 4 * 262143 * 4 + 4 * 16 * 1024 * 8
 
 
 def test_rotary_tables_agree_with_the_oracle():

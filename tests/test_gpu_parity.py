@@ -178,7 +178,9 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (2, 5, 16, 700, [700, 650], False, 100, "causal"),         # prefill rows: causal visibility
     (1, 2, 48, 1500, [1500], True, 1, "end"),                  # k = 1, Hi not a multiple of 64
     (2, 1, 64, 20000, [20000, 19999], True, 1024, "end"),      # spans many blocks; two-stage top-k
-    (2, 1, 64, 70000, [70000, 500], True, 1024, "end"),        # two-stage, 9 chunks; one row with < k visible
+    (2, 1, 64, 70000, [70000, 500], True, 1024, "end"),        # two-stage, 5 chunks; one row with < k visible
+    (1, 1, 4, 300000, [300000], True, 1024, "end"),            # 19 chunks: an intermediate merge stage, then the final one
+    (1, 1, 4, 100000, [99000], False, 4096, "end"),            # k = 4,096: merge groups of 4 chunks, two stages
     (2, 37, 64, 3000, [3000, 2100], False, 256, "causal"),     # multi-row kernel: ragged row groups, causal
     (1, 16, 40, 1300, [1290], False, 64, "causal"),            # multi-row kernel, heads not a multiple of 16
     (1, 1, 64, 140000, [140000], True, 512, "end"),            # CSA2 selection: top-512 of a long row (chunked)
