@@ -57,14 +57,17 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 
 constexpr int kIdxTilesPerWave = 32;     // 16 entries per tile
 constexpr int kIdxWaves = 4;
-constexpr int kDepth = 4;                // score-tile loads in flight per wave
+// Score-tile loads in flight per wave (the register ring's depth): 8 when the scores grid has
+// at most kDeepRingBlocks blocks (about one per CU, so each wave must keep more loads in flight:
+// 65K decode fused call 32.8 -> 32.1 us), else 4 (grids of 512 and more, as at 1M, lose with 8).
+constexpr int kDeepRingBlocks = 256;
 constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
-static_assert(kIdxTilesPerWave % kDepth == 0, "whole ring rounds stay inside a wave's tiles");
 
 // One block of the decode scores grid: query row `row` (b * Tq + t), entries from
 // chunk * kIdxEntPerBlock.
-template <int HB, bool FP8>
+template <int HB, bool FP8, int DEPTH>
 __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, int chunk) {
+  static_assert(kIdxTilesPerWave % DEPTH == 0, "whole ring rounds stay inside a wave's tiles");
   __shared__ float sbuf[kIdxWaves][kIdxTilesPerWave * 16];
   const int b = row / a.Tq;
   const int lane = threadIdx.x & 63;
@@ -103,7 +106,7 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
   constexpr int KR = FP8 ? KW + 1 : KW;
   const float* sbase = FP8 ? a.key_scales + (int64_t)b * a.cap : nullptr;
   // Branch-free loads (row index clamped into the visible range; results past nvis are
-  // masked when the score is written) so the compiler can keep kDepth tiles in flight.
+  // masked when the score is written) so the compiler can keep DEPTH tiles in flight.
   const int jlast = max(nvis - 1, 0);
   auto load_tile = [&](int t0, uint32_t (&r)[KR]) {
     const int j = min(t0 + n, jlast);
@@ -116,15 +119,15 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
     if constexpr (FP8) r[KW] = __float_as_uint(sbase[j]);
   };
 
-  // kDepth tiles in flight per wave: the loads of tile t + kDepth are issued as tile t is
+  // DEPTH tiles in flight per wave: the loads of tile t + DEPTH are issued as tile t is
   // consumed, from a ring of register buffers indexed at compile time.  The loop is software
   // pipelined by one tile: tile t's products are issued before tile t - 1's ReLU-weighted head
   // sum, which does not depend on them, so the matrix cores run while the vector ALU works.
-  uint32_t ring[kDepth][KR];
+  uint32_t ring[DEPTH][KR];
   int ntile = 0;
   if (base < nvis) ntile = min(kIdxTilesPerWave, (nvis - base + 15) / 16);
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
+  for (int d = 0; d < DEPTH; ++d)
     load_tile(base + 16 * min(d, max(ntile - 1, 0)), ring[d]);
   // Straight-line body: the loop runs whole ring rounds (tiles past ntile recompute the last
   // tile's rows and land in sbuf slots whose entries are not visible), and the first round's
@@ -145,9 +148,9 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
     // staged in LDS: global stores inside the loop would count against vmcnt and stall the ring
     if (g == 0) sbuf[wave][16 * t + n] = sc;
   };
-  for (int t0 = 0; t0 < ntile; t0 += kDepth) {
+  for (int t0 = 0; t0 < ntile; t0 += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
+    for (int d = 0; d < DEPTH; ++d) {
       const int t = t0 + d;
       uint32_t (&cur)[KR] = ring[d];
       f32x4 acc[HB];
@@ -176,7 +179,7 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
       }
       const float kscale = FP8 ? __uint_as_float(cur[KW]) : 1.f;
       // next load for this ring slot (past the last tile it re-reads that tile: an L2 hit)
-      load_tile(base + 16 * min(t + kDepth, ntile - 1), ring[d]);
+      load_tile(base + 16 * min(t + DEPTH, ntile - 1), ring[d]);
       finish(prev, prev_scale, tprev);
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) prev[hb] = acc[hb];
@@ -193,20 +196,20 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
   }
 }
 
-template <int HB, bool FP8>
+template <int HB, bool FP8, int DEPTH>
 __global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
-  index_scores_block<HB, FP8>(a, blockIdx.x, blockIdx.y);
+  index_scores_block<HB, FP8, DEPTH>(a, blockIdx.x, blockIdx.y);
 }
 
 // The same grid with a decode step's compress blocks after it (csa_index_topk_compress): the
 // compressor writes only the KV and window caches, which the scores do not read, so its
 // short, latency-bound blocks run beside the scores blocks instead of in a launch of their
 // own.  Blocks [0, n_idx) are the scores grid in launch order (row fastest).
-template <int HB, bool FP8>
+template <int HB, bool FP8, int DEPTH>
 __global__ void __launch_bounds__(256) k_index_scores_compress(IndexArgs a, CompressBatch cb, int n_idx) {
   const int L = blockIdx.x;
   const int rows = a.B * a.Tq;
-  if (L < n_idx) index_scores_block<HB, FP8>(a, L % rows, L / rows);
+  if (L < n_idx) index_scores_block<HB, FP8, DEPTH>(a, L % rows, L / rows);
   else compress_batch_block(cb, L - n_idx);
 }
 
@@ -344,10 +347,13 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   dim3 grid(rows, (a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
   const int HB = (a.Hi + 15) / 16;
   const bool f8 = a.key_dtype == CSA_FP8_E4M3;
+  const bool deep = (long long)grid.x * grid.y <= kDeepRingBlocks;
 #define CSA_IDX_LAUNCH(hb)                                                                     \
   if (HB == hb) {                                                                              \
-    if (f8) hipLaunchKernelGGL((k_index_scores<hb, true>), grid, dim3(256), 0, s, a);          \
-    else hipLaunchKernelGGL((k_index_scores<hb, false>), grid, dim3(256), 0, s, a);            \
+    if (f8 && deep) hipLaunchKernelGGL((k_index_scores<hb, true, 8>), grid, dim3(256), 0, s, a); \
+    else if (f8) hipLaunchKernelGGL((k_index_scores<hb, true, 4>), grid, dim3(256), 0, s, a);   \
+    else if (deep) hipLaunchKernelGGL((k_index_scores<hb, false, 8>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((k_index_scores<hb, false, 4>), grid, dim3(256), 0, s, a);          \
   }
   if (!f8 && a.Tq >= kMqRows && a.Di == 128) {
     const dim3 gmq(a.B * ((a.Tq + kMqRows - 1) / kMqRows));
@@ -378,10 +384,13 @@ hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs* 
   }
   const long long n_idx = (long long)rows * ((a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
   const dim3 grid((unsigned)(n_idx + total));
-#define CSA_IDX_FUSED(hb)                                                                                        \
-  if (HB == hb) {                                                                                                \
-    if (f8) hipLaunchKernelGGL((k_index_scores_compress<hb, true>), grid, dim3(256), 0, s, a, cb, (int)n_idx);  \
-    else hipLaunchKernelGGL((k_index_scores_compress<hb, false>), grid, dim3(256), 0, s, a, cb, (int)n_idx);    \
+  const bool deep = n_idx <= kDeepRingBlocks;
+#define CSA_IDX_FUSED(hb)                                                                                           \
+  if (HB == hb) {                                                                                                   \
+    if (f8 && deep) hipLaunchKernelGGL((k_index_scores_compress<hb, true, 8>), grid, dim3(256), 0, s, a, cb, (int)n_idx); \
+    else if (f8) hipLaunchKernelGGL((k_index_scores_compress<hb, true, 4>), grid, dim3(256), 0, s, a, cb, (int)n_idx);    \
+    else if (deep) hipLaunchKernelGGL((k_index_scores_compress<hb, false, 8>), grid, dim3(256), 0, s, a, cb, (int)n_idx); \
+    else hipLaunchKernelGGL((k_index_scores_compress<hb, false, 4>), grid, dim3(256), 0, s, a, cb, (int)n_idx);          \
   }
   CSA_IDX_FUSED(1) CSA_IDX_FUSED(2) CSA_IDX_FUSED(3) CSA_IDX_FUSED(4)
 #undef CSA_IDX_FUSED
