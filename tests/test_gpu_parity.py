@@ -181,6 +181,7 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (2, 1, 64, 70000, [70000, 500], True, 1024, "end"),        # two-stage, 5 chunks; one row with < k visible
     (1, 1, 4, 300000, [300000], True, 1024, "end"),            # 19 chunks: an intermediate merge stage, then the final one
     (1, 1, 4, 100000, [99000], False, 4096, "end"),            # k = 4,096: merge groups of 4 chunks, two stages
+    (2, 8, 16, 70000, [70000, 65000], False, 1024, "causal"),   # bf16 keys, 560-block scores grid (4-deep ring)
     (2, 37, 64, 3000, [3000, 2100], False, 256, "causal"),     # multi-row kernel: ragged row groups, causal
     (1, 16, 40, 1300, [1290], False, 64, "causal"),            # multi-row kernel, heads not a multiple of 16
     (1, 1, 64, 140000, [140000], True, 512, "end"),            # CSA2 selection: top-512 of a long row (chunked)
