@@ -389,6 +389,74 @@ def test_fp8_encode_matches_library_in_range_and_saturates():
     assert np.all(np.abs(O.fp8_e4m3_decode(codes)).reshape(3, 2, 64).max(-1) == 448.0)
 
 
+def test_fp8_block_dequantize_hand_values():
+    """Codes and scales written out by hand, with every block a different scale, so that a
+    block index taken modulo instead of divided (np.tile for np.repeat), a wrong block size or
+    a transposed block layout moves a value."""
+    one, neg_one, tiny, top = 0x38, 0xB8, 0x01, 0x7E        # 1.0, -1.0, 2^-9, 448 in E4M3FN
+    pattern = np.array([one, neg_one, tiny, top], dtype=np.uint8)
+    vals = np.array([1.0, -1.0, 2.0 ** -9, 448.0])
+    codes = np.stack([np.full(256, one, dtype=np.uint8), np.tile(pattern, 64)])        # [2, 256]
+    # block 64: four scales per row
+    sc64 = np.array([[0.5, 2.0, 3.0, 0.25], [1.0, 4.0, 0.125, 10.0]], dtype=np.float32)
+    want = np.empty((2, 256))
+    want[0, 0:64], want[0, 64:128], want[0, 128:192], want[0, 192:256] = 0.5, 2.0, 3.0, 0.25
+    for c in range(256):
+        want[1, c] = vals[c % 4] * [1.0, 4.0, 0.125, 10.0][c // 64]
+    got = O.fp8_block_dequantize(codes, sc64, 64)
+    np.testing.assert_array_equal(got, want)
+    # block 128: two scales per row (the indexer-key layout when C = 256)
+    sc128 = np.array([[6.0, 0.75], [0.5, 8.0]], dtype=np.float32)
+    want128 = np.empty((2, 256))
+    want128[0, :128], want128[0, 128:] = 6.0, 0.75
+    want128[1, :128] = np.tile(vals, 32) * 0.5
+    want128[1, 128:] = np.tile(vals, 32) * 8.0
+    np.testing.assert_array_equal(O.fp8_block_dequantize(codes, sc128, 128), want128)
+    # leading batch dimensions broadcast row by row
+    c3 = np.stack([codes, codes[::-1]])                        # [2, 2, 256]
+    s3 = np.stack([sc64, sc64[::-1]])
+    got3 = O.fp8_block_dequantize(c3, s3, 64)
+    np.testing.assert_array_equal(got3[0], want)
+    np.testing.assert_array_equal(got3[1], want[::-1])
+
+
+def test_fp8_block_quantize_scales_and_codes():
+    """Scales are fp32 amax / 448 per block and codes are the E4M3FN rounding of fp32 x / scale,
+    checked against hand values and against torch's float8_e4m3fn conversion (a library routine),
+    block by block, on rows whose blocks differ in magnitude by decades."""
+    # hand values: block maxima that make the scale exact
+    x = np.zeros((1, 256))
+    x[0, 0:64] = np.linspace(-448.0, 100.0, 64)           # amax 448 -> scale 1, codes = E4M3(x)
+    x[0, 64:128] = 0.0                                     # zero block -> scale 0, codes 0
+    x[0, 128:192] = np.linspace(-3.0, 896.0, 64)           # amax 896 -> scale 2
+    x[0, 192:256] = 1.0                                    # amax 1 -> scale fp32(1/448), codes 448
+    codes, sc = O.fp8_block_quantize(x, 64)
+    assert sc.dtype == np.float32 and sc.shape == (1, 4)
+    assert sc[0, 0] == 1.0 and sc[0, 1] == 0.0 and sc[0, 2] == 2.0
+    assert sc[0, 3] == np.float32(1.0) / np.float32(448.0)
+    lib = lambda v: torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.fp8_e4m3_decode(codes[0, 0:64]), O.fp8_e4m3_decode(lib(x[0, 0:64])))
+    assert np.all(codes[0, 64:128] == 0)
+    np.testing.assert_array_equal(O.fp8_e4m3_decode(codes[0, 128:192]),
+                                  O.fp8_e4m3_decode(lib(x[0, 128:192] / 2.0)))
+    assert np.all(codes[0, 192:256] == 0x7E)
+    # random rows: per-block magnitudes 1e-3 .. 1e3
+    r = rng(16)
+    y = r.standard_normal((5, 512)) * np.repeat(10.0 ** r.integers(-3, 4, size=(5, 8)), 64, axis=1)
+    codes, sc = O.fp8_block_quantize(y, 64)
+    y32 = torch.from_numpy(y.astype(np.float32)).view(5, 8, 64)
+    sc_lib = (y32.abs().amax(-1) / torch.tensor(448.0, dtype=torch.float32)).numpy()
+    np.testing.assert_array_equal(sc, sc_lib)
+    code_lib = (y32 / torch.from_numpy(sc_lib)[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.fp8_e4m3_decode(codes.reshape(5, 8, 64)), O.fp8_e4m3_decode(code_lib))
+    # the round trip is within half a code step of every value (the block's scale times 2^-4 of
+    # the element's binade, or the subnormal spacing)
+    back = O.fp8_block_dequantize(codes, sc, 64)
+    step = np.repeat(sc.astype(np.float64), 64, axis=1) * np.ldexp(
+        1.0, np.maximum(np.frexp(np.abs(y) / np.repeat(sc.astype(np.float64), 64, axis=1))[1] - 4, -9))
+    assert np.all(np.abs(back - y) <= 0.5 * step * (1 + 1e-6))
+
+
 def test_bf16_round_matches_library():
     r = rng(15)
     x = np.concatenate([r.standard_normal(20000).astype(np.float32),
