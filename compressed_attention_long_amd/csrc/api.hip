@@ -194,7 +194,8 @@ static int index_args(const void* q_idx, const float* w, const int64_t* q_pos, i
   int rc = check_cache(keys, "keys", true);
   if (rc) return rc;
   REQUIRE(B >= 0 && Tq >= 0, CSA_EINVAL, "B and Tq must be >= 0");
-  REQUIRE(topk >= 1 && topk <= keys->cap, CSA_EINVAL, "topk must be in [1, cap=%d] (got %d)", keys->cap, topk);
+  REQUIRE(topk >= 1 && topk <= keys->cap && topk <= 4096, CSA_EINVAL, "topk must be in [1, min(cap=%d, 4096)] (got %d)",
+          keys->cap, topk);
   if (B == 0 || Tq == 0) {
     empty = true;
     return CSA_OK;

@@ -403,200 +403,15 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkBins = 2048;
 constexpr int kCandMax = 512;
 
-struct TopkShared {
-  int hist[kTopkBins];
-  alignas(16) uint32_t ckey[kCandMax + 4];   // + 4: padding for 16-byte reads of the tail
-  alignas(16) int cidx[kCandMax + 4];
-  int wsum[kTopkThreads / 64];
-  uint32_t wmin[kTopkThreads / 64], wmax[kTopkThreads / 64];
-  int ccount;
-  int bstar, above;
-  uint32_t TK;
-  int I;
-};
-
 // Order-preserving map of fp32 bit patterns onto uint32.
 __device__ __forceinline__ uint32_t okey(float v) {
   uint32_t u = __float_as_uint(v);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the block (1024 lanes); also returns the total.
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < kTopkThreads / 64; ++w2) {
-    int s = wsum[w2];
-    if (w2 < wave) before += s;
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return before + x - v;
-}
-
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, TopkShared& sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-  }
-  if (lane == 0) { sh.wmin[wave] = mn; sh.wmax[wave] = mx; }
-  __syncthreads();
-  mn = sh.wmin[0];
-  mx = sh.wmax[0];
-#pragma unroll
-  for (int w2 = 1; w2 < kTopkThreads / 64; ++w2) { mn = min(mn, sh.wmin[w2]); mx = max(mx, sh.wmax[w2]); }
-  __syncthreads();
-}
-
-// One block (1024 lanes) per query row.  Keys are bins of a linear scale over the
-// current key range [klo, khi]: bin = (key - klo) >> shift with 2048 bins.  Each
-// refinement keeps only the bin holding the k-th largest key, whose key range is
-// at most 2^shift - 1 wide, so after at most three passes the candidates are one
-// key value (the range shrinks from < 2^32 to < 2^21, < 2^10, then 0).
-// Visit every visible entry j < nvis of a row in global memory, 8 loads per lane in
-// flight (indices clamped into the row; out-of-range lanes are masked).
-template <typename F>
-__device__ __forceinline__ void for_each_key(const float* s, int nvis, F&& fn) {
-  constexpr int U = 8;
-  const int last = max(nvis - 1, 0);
-  for (int j0 = threadIdx.x; j0 < nvis; j0 += U * kTopkThreads) {
-    uint32_t kk[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) kk[u] = okey(s[min(j0 + u * kTopkThreads, last)]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * kTopkThreads;
-      if (j < nvis) fn(kk[u], j);
-    }
-  }
-}
-
-__global__ void __launch_bounds__(kTopkThreads) k_topk(IndexArgs a) {
-  __shared__ TopkShared sh;
-  const int row = blockIdx.x;
-  const int b = row / a.Tq;
-  const int tid = threadIdx.x;
-  const int k = a.topk;
-  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
-  const float* s = a.scores + (int64_t)row * a.cap;
-  int32_t* out = a.idx_out + (int64_t)row * k;
-
-  uint32_t TK = 0xffffffffu;   // threshold (key, index) in the order (score desc, index asc)
-  int I = -1;
-  const bool take_all = nvis <= k;
-  if (!take_all) {
-    if (tid == 0) { sh.bstar = 0; sh.above = 0; sh.TK = 0xffffffffu; sh.I = -1; }
-    uint32_t klo = 0xffffffffu, khi = 0u;
-    for_each_key(s, nvis, [&](uint32_t v, int) { klo = min(klo, v); khi = max(khi, v); });
-    block_minmax(klo, khi, sh);
-    int above = 0;                          // entries known to rank above the current range
-    for (int iter = 0; iter < 4 && klo < khi; ++iter) {
-      for (int i = tid; i < kTopkBins; i += kTopkThreads) sh.hist[i] = 0;
-      __syncthreads();
-      const uint32_t range = khi - klo;
-      const int shift = max(0, 32 - __clz((int)range) - 11);
-      for_each_key(s, nvis, [&](uint32_t v, int) {
-        if (v >= klo && v <= khi) atomicAdd(&sh.hist[(v - klo) >> shift], 1);
-      });
-      __syncthreads();
-      // thread t owns bins 2u+1 and 2u with u = 1023 - t, so the scan runs from the top bin down
-      const int u = kTopkThreads - 1 - tid;
-      const int hA = sh.hist[2 * u + 1], hB = sh.hist[2 * u];
-      int tot;
-      const int pre = block_excl_scan(hA + hB, sh.wsum, tot);   // entries in higher bins
-      const int need = k - above;
-      if (pre < need && pre + hA >= need) { sh.bstar = 2 * u + 1; sh.above = pre; }
-      else if (pre + hA < need && pre + hA + hB >= need) { sh.bstar = 2 * u; sh.above = pre + hA; }
-      __syncthreads();
-      const int bstar = min(max(sh.bstar, 0), kTopkBins - 1);
-      const int cnt = sh.hist[bstar];
-      above += sh.above;
-      uint32_t nlo = 0xffffffffu, nhi = 0u;
-      for_each_key(s, nvis, [&](uint32_t v, int) {
-        if (v >= klo && v <= khi && (int)((v - klo) >> shift) == bstar) { nlo = min(nlo, v); nhi = max(nhi, v); }
-      });
-      block_minmax(nlo, nhi, sh);
-      klo = nlo;
-      khi = nhi;
-      if (cnt <= kCandMax) break;
-    }
-    // candidates: keys in [klo, khi]; `need` of them are taken, best first
-    const int need = k - above;
-    if (klo == khi) {
-      // all candidates share one key: the need-th smallest index among them
-      TK = klo;
-      int base = 0;
-      for (int j0 = 0; j0 < nvis; j0 += kTopkThreads) {
-        const int j = j0 + tid;
-        const int f = (j < nvis && okey(s[j]) == klo) ? 1 : 0;
-        int tot;
-        const int pre = block_excl_scan(f, sh.wsum, tot);
-        if (f && base + pre == need - 1) sh.I = j;
-        base += tot;
-        if (base >= need) break;
-      }
-      __syncthreads();
-      I = sh.I;
-    } else {
-      if (tid == 0) sh.ccount = 0;
-      __syncthreads();
-      for_each_key(s, nvis, [&](uint32_t v, int j) {
-        if (v >= klo && v <= khi) {
-          int slot = atomicAdd(&sh.ccount, 1);
-          if (slot < kCandMax) { sh.ckey[slot] = v; sh.cidx[slot] = j; }
-        }
-      });
-      __syncthreads();
-      const int c = min(sh.ccount, kCandMax);
-      for (int ci = tid; ci < c; ci += kTopkThreads) {
-        const uint32_t v = sh.ckey[ci];
-        const int ji = sh.cidx[ci];
-        int rank = 0;
-        for (int o = 0; o < c; ++o) {
-          const uint32_t vo = sh.ckey[o];
-          rank += (vo > v || (vo == v && sh.cidx[o] < ji)) ? 1 : 0;
-        }
-        if (rank == need - 1) { sh.TK = v; sh.I = ji; }
-      }
-      __syncthreads();
-      TK = sh.TK;
-      I = sh.I;
-    }
-  }
-  // ascending compaction of the selected entries
-  int base = 0;
-  for (int j0 = 0; j0 < nvis; j0 += kTopkThreads) {
-    const int j = j0 + tid;
-    int f = 0;
-    if (j < nvis) {
-      if (take_all) f = 1;
-      else { const uint32_t v = okey(s[j]); f = (v > TK || (v == TK && j <= I)) ? 1 : 0; }
-    }
-    int tot;
-    const int pre = block_excl_scan(f, sh.wsum, tot);
-    if (f && base + pre < k) out[base + pre] = j;
-    base += tot;
-  }
-  for (int p = base + tid; p < k; p += kTopkThreads) out[p] = -1;
-}
-
-// Same selection with the row held in registers, read once with coalesced loads: thread t
-// owns entries j = i * 1024 + t (i < NPT).  Order-dependent steps (ascending output, the
-// smallest index among tied keys) number the selected entries in index order with wave
-// ballots plus one scan over the per-(i, wave) counts.  Used when the row has at most
-// NPT * 1024 entries.
+// The selection holds a row (or a chunk of one) in registers, read once with coalesced loads:
+// thread t owns entries j = i * T + t (i < NPT).  Order-dependent steps (ascending output, the
+// smallest index among tied keys) number the selected entries in index order.
 // ---- wave-wide reductions without LDS: DPP within rows of 16 lanes (quad swaps, half-row
 // and row mirrors), then the gfx950 lane-swap permutes across rows and wave halves.
 template <int CTRL>
@@ -992,47 +807,6 @@ __global__ void __launch_bounds__(T) k_topk_merge(IndexArgs a, const uint32_t* i
   }
 }
 
-// Plan of the top-k for rows of up to `cap` entries.  Rows that fit one register-resident
-// block take one block per row.  Longer rows go through stage 1 (chunks of 8192 entries,
-// `nchunk` per row) and merge stages that each reduce `group` chunks of k candidates (8192
-// candidates per block) to one, until one block per row finishes; that needs k <= 4096.
-// Anything else uses the streaming kernel.
-#ifndef CSA_TOPK_SINGLE_MAX
-#define CSA_TOPK_SINGLE_MAX 16384   // rows up to this length always take one block
-#endif
-// 16,384 entries per stage-1 block and candidates per merge block: a 262,143-entry row takes
-// one chunk stage and one merge (23.5 us for 4 rows, against 25.6 in three stages with 8,192)
-constexpr int kChunk = 16384;       // stage-1 entries per block
-constexpr int kMergeCands = 16384;  // candidates per merge block
-TopkPlan topk_plan(int rows, int cap, int k) {
-  TopkPlan pl{};
-  if (cap <= CSA_TOPK_SINGLE_MAX || (cap <= 65536 && rows >= 128)) {
-    pl.mode = 0;
-    return pl;
-  }
-  if (k > kMergeCands / 2) {
-    pl.mode = cap <= 65536 ? 0 : 2;
-    return pl;
-  }
-  pl.mode = 1;
-  pl.chunk = kChunk;
-  pl.nchunk = (cap + kChunk - 1) / kChunk;
-  pl.group = kMergeCands / k;
-  if ((long long)rows > 0x7fffffffLL || pl.nchunk > 65535) pl.mode = 2;
-  return pl;
-}
-
-size_t topk_workspace(int rows, int cap, int k) {
-  const TopkPlan pl = topk_plan(rows, cap, k);
-  if (pl.mode != 1) return 0;
-  // two candidate areas (stage outputs alternate between them): the first holds the stage-1
-  // chunks, the second the first merge stage's
-  const size_t per_chunk = (size_t)k * (sizeof(uint32_t) + sizeof(int32_t)) + sizeof(int);
-  const size_t c2 = (pl.nchunk + pl.group - 1) / pl.group;
-  const size_t bytes = (size_t)rows * (pl.nchunk + c2) * per_chunk + 4 * 256;
-  return (bytes + 255) / 256 * 256;
-}
-
 static void launch_merge(int n, bool final_stage, dim3 grid, hipStream_t s, const IndexArgs& a,
                          const uint32_t* in_key, const int32_t* in_idx, const int* in_count, int chunks,
                          int group, uint32_t* out_key, int32_t* out_idx, int* out_count) {
@@ -1067,31 +841,22 @@ hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
     else hipLaunchKernelGGL((k_topk_reg<1024, 64>), grid, dim3(1024), 0, s, a);
     return hipGetLastError();
   }
-  if (pl.mode == 2) {
-    hipLaunchKernelGGL(k_topk, dim3(rows), dim3(kTopkThreads), 0, s, a);
-    return hipGetLastError();
-  }
-  // candidate areas A (stage-1 chunks) and B (first merge stage), each [keys | indices | counts]
-  const size_t nA = (size_t)rows * pl.nchunk * k;
-  const int c2 = (pl.nchunk + pl.group - 1) / pl.group;
-  const size_t nB = (size_t)rows * c2 * k;
-  auto align = [](uint8_t* p) {
-    return reinterpret_cast<uint8_t*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255));
-  };
-  uint8_t* w = align(reinterpret_cast<uint8_t*>(a.cand_key));
-  uint32_t* keyA = reinterpret_cast<uint32_t*>(w);
-  int32_t* idxA = reinterpret_cast<int32_t*>(keyA + nA);
-  int* cntA = reinterpret_cast<int*>(idxA + nA);
-  w = align(reinterpret_cast<uint8_t*>(cntA + (size_t)rows * pl.nchunk));
-  uint32_t* keyB = reinterpret_cast<uint32_t*>(w);
-  int32_t* idxB = reinterpret_cast<int32_t*>(keyB + nB);
-  int* cntB = reinterpret_cast<int*>(idxB + nB);
+  // candidate areas A (stage-1 chunks) and B (first merge stage): offsets from the candidate
+  // area's start (the workspace part the C ABI points cand_key at, 256-byte aligned)
+  const TopkCarve cv = topk_carve(rows, pl, k);
+  uint8_t* w = reinterpret_cast<uint8_t*>(a.cand_key);
+  uint32_t* keyA = reinterpret_cast<uint32_t*>(w + cv.keyA);
+  int32_t* idxA = reinterpret_cast<int32_t*>(w + cv.idxA);
+  int* cntA = reinterpret_cast<int*>(w + cv.cntA);
+  uint32_t* keyB = reinterpret_cast<uint32_t*>(w + cv.keyB);
+  int32_t* idxB = reinterpret_cast<int32_t*>(w + cv.idxB);
+  int* cntB = reinterpret_cast<int*>(w + cv.cntB);
   a.cand_key = keyA;
   a.cand_idx = idxA;
   a.cand_count = cntA;
   a.chunk = pl.chunk;
   a.nchunk = pl.nchunk;
-  hipLaunchKernelGGL((k_topk_chunk<1024, kChunk / 1024>), dim3(rows, pl.nchunk), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL((k_topk_chunk<1024, kTopkChunk / 1024>), dim3(rows, pl.nchunk), dim3(1024), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t* in_key = keyA;

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "csa.h"
+#include "workspace.hpp"
 
 namespace csa {
 
@@ -43,12 +44,6 @@ struct IndexArgs {
   int* cand_count;
   int chunk, nchunk;      // set by the launcher
 };
-struct TopkPlan {
-  int mode;               // 0: one block per row; 1: chunked stages; 2: streaming
-  int chunk, npt1, nchunk, group;
-};
-TopkPlan topk_plan(int rows, int cap, int k);
-size_t topk_workspace(int rows, int cap, int k);   // candidate area of the two-stage plan
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s);
 // the scores launch carrying compress calls (the batch layouts of launch_compress_batch); falls
 // back to separate launches when the calls need the run-mode kernel or the scores take the

@@ -245,7 +245,7 @@ int csa_index_topk_compress(const csa_compress_call_t* calls, int n_calls,
  *   out        device [B, Tq, H, 512], out_dtype CSA_FP32 or CSA_BF16
  *   lse_out    device fp32 [B, Tq, H] or NULL
  *   workspace  at least csa_attend_workspace_bytes(...) bytes, 256-byte aligned
- * Requires H % 16 == 0 or H < 16, H <= 128, topk <= 4096, 16-byte aligned q/out/kv rows.
+ * Requires H % 16 == 0 or H < 16, H <= 128, 0 <= topk <= kv->cap, 16-byte aligned q/out/kv rows.
  */
 int csa_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H,
                const csa_cache_t* kv, const int32_t* idx, int topk,

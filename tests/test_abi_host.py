@@ -92,6 +92,7 @@ def test_index_topk_validation():
     k = cache(C=128)
     assert index(k, topk=65)[0] == L.CSA_EINVAL                    # topk > cap
     assert index(k, topk=0)[0] == L.CSA_EINVAL
+    assert index(cache(C=128, cap=10000), topk=4097)[0] == L.CSA_EINVAL     # topk above 4,096
     assert index(k, Hi=65)[0] == L.CSA_ENOTSUP
     assert index(cache(C=256))[0] == L.CSA_ENOTSUP
     assert index(cache(C=128, dtype=L.CSA_FP8_E4M3, sb=64))[0] == L.CSA_ENOTSUP
