@@ -71,6 +71,14 @@ def algorithmic_costs(wl):
     return c
 
 
+def stats(samples):
+    """Median, 10th and 90th percentiles (nearest rank) and count of timing samples (ms)."""
+    xs = sorted(samples)
+    n = len(xs)
+    pick = lambda q: xs[min(n - 1, max(0, int(math.ceil(q * n)) - 1))]
+    return {"median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9), "n": n}
+
+
 def build_layers(wl, n_layers, device, torch, out_dtype):
     import csa_inputs as ci
     from compressed_attention_long_amd.step import LayerStep
@@ -142,15 +150,18 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
         graphs[i % n_layers].replay()
     torch.cuda.synchronize()
     g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_samp = max(steps_n, 50)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_samp + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    g0.record()
-    for i in range(steps_n):
+    for i in range(n_samp):
+        step_ev[i].record(stream)
         graphs[i % n_layers].replay()
-    g1.record()
+    step_ev[n_samp].record(stream)
     torch.cuda.synchronize()
-    wall_per_layer_graph = (time.perf_counter() - t0) * 1e3 / steps_n
-    graph_gpu_per_layer_graph = g0.elapsed_time(g1) / steps_n
+    wall_per_layer_graph = (time.perf_counter() - t0) * 1e3 / n_samp
+    step_samples = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(n_samp)]
+    graph_gpu_per_layer_graph = sum(step_samples) / n_samp
     # --- chained graph (headline)
     chain = capture_chain(layers, torch)
     for i in range(max(1, warmup // n_layers)):
@@ -171,8 +182,8 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     if wl.mode == "csa":
         call_fns["index"] = lambda L: L.index()
         call_fns["index_compress"] = lambda L: L.index_compress()
-    reps = max(2, steps_n // n_layers)
-    calls_graph = {}
+    reps = max(50, steps_n // n_layers)
+    calls_graph, calls_samples = {}, {}
     for name, fn in call_fns.items():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -187,12 +198,15 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
                 fn(L)
         cg.replay()
         torch.cuda.synchronize()
-        g0.record(stream)
-        for _ in range(reps):
+        cev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for r in range(reps):
+            cev[r].record(stream)
             cg.replay()
-        g1.record(stream)
+        cev[reps].record(stream)
         torch.cuda.synchronize()
-        calls_graph[name] = g0.elapsed_time(g1) / (reps * n_layers)
+        samples = [cev[r].elapsed_time(cev[r + 1]) / n_layers for r in range(reps)]
+        calls_graph[name] = sum(samples) / reps
+        calls_samples[name] = samples
         del cg
     # --- eager pass with per-call events (reference: includes host launch gaps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps_n)]
@@ -220,6 +234,8 @@ def time_workload(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30, max_layer
     med = lambda xs: sorted(xs)[len(xs) // 2]
     out = {k: sum(v) / len(v) for k, v in per.items()}
     out["calls_graph"] = calls_graph
+    out["calls_stats"] = {k: stats(v) for k, v in calls_samples.items()}
+    out["step_stats"] = stats(step_samples)
     out["step_gpu_median"] = med(per["step_gpu"])
     out["wall_ms_per_step"] = wall
     out["graph_gpu_ms_per_step"] = graph_gpu
@@ -395,61 +411,102 @@ def pmc_probe(wl, torch, layers_n=4, reps=2):
                       "sources": {c: source_digest(c) for c in CALL_SOURCES}}), flush=True)
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The fp64 oracle on a bounded sample of the same workload: whole decode steps of
-    single sequences (compress the new entry, index, select, attend), as many as fit
-    in about `budget_s` seconds of host time.  Reported in tokens/s."""
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, budget_s=12.0, threads=None, max_rows=None):
+    """The fp64 oracle on a bounded sample of the same workload, in tokens/s.
+
+    Inputs are one sequence's share of the workload (B = 1, same shapes and distributions).
+    A decode step per query row: compress the step's new entries and window rows, then (CSA)
+    index, select and attend, or (HCA) attend to every visible entry.  A prefill chunk: its
+    new entries are compressed once (charged pro rata to the sampled rows), then sampled query
+    rows (first, last, the rest spread uniformly) each run the indexer, top-k and attention.
+    Rows are taken until about `budget_s` seconds have passed (at most `max_rows`).  `threads`
+    limits the BLAS pool (None: all the host's cores)."""
+    import contextlib
+    import dataclasses
     import numpy as np
     import csa_inputs as ci
     from oracle import csa_oracle as O
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=threads) if threads else contextlib.nullcontext()
     except Exception:
-        cores = os.cpu_count() or 1
-    t, meta = ci.step_tensors(wl, "cpu")
-    if wl.yarn_factor > 1.0:
-        f = O.yarn_inv_freq(160000.0, wl.R, wl.yarn_factor, wl.yarn_base_len)
-        scale = O.yarn_logit_scale(wl.yarn_factor) / math.sqrt(wl.D)
-    else:
-        f = O.rope_inv_freq(160000.0, wl.R)
-        scale = 1 / math.sqrt(wl.D)
-    E = wl.E
-    ent_pos = O.entry_positions(wl.pos0, E, wl.window, wl.stride)
-    win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
-    n_done = 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        b = n_done % wl.B
-        qp = int(t["q_pos"][b, 0])
-        new, _ = O.compress(t["kv_raw"][b].double().numpy(), t["z_raw"][b].double().numpy(), wl.window,
-                            wl.stride, wl.pos0 + meta["E_pre"] * wl.stride, f)
+        limit = contextlib.nullcontext()
+    one = dataclasses.replace(wl, B=1)
+    t, meta = ci.step_tensors(one, "cpu", seed=ci.seed_for(wl.name))
+    with limit:
+        cores = _blas_threads()
+        if wl.yarn_factor > 1.0:
+            f = O.yarn_inv_freq(160000.0, wl.R, wl.yarn_factor, wl.yarn_base_len)
+            scale = O.yarn_logit_scale(wl.yarn_factor) / math.sqrt(wl.D)
+        else:
+            f = O.rope_inv_freq(160000.0, wl.R)
+            scale = 1 / math.sqrt(wl.D)
+        ent_pos = O.entry_positions(wl.pos0, wl.E, wl.window, wl.stride)
+        win_pos = int(t["win_pos0"][0]) + np.arange(meta["win_cap"])
+        sink = t["sink"].double().numpy()
         if wl.kv_dtype == "fp4":
-            kv = O.mxfp4_block_dequantize(O.fp4_unpack(t["kv_cache"][b].numpy()),
-                                          t["kv_cache_scale"][b].numpy(), wl.kv_scale_block)
+            kv = O.mxfp4_block_dequantize(O.fp4_unpack(t["kv_cache"][0].numpy()), t["kv_cache_scale"][0].numpy(),
+                                          wl.kv_scale_block)
         elif wl.kv_dtype == "fp8":
-            kv = O.fp8_block_dequantize(t["kv_cache"][b].numpy(), t["kv_cache_scale"][b].numpy(),
-                                        wl.kv_scale_block)
+            kv = O.fp8_block_dequantize(t["kv_cache"][0].numpy(), t["kv_cache_scale"][0].numpy(), wl.kv_scale_block)
         else:
-            kv = t["kv_cache"][b].double().numpy()
-        kv[meta["E_pre"]:] = new[:meta["n_new_entries"]]
-        win = t["win_cache"][b].double().numpy()
-        win[meta["win_first_new"]:] = O.rope(t["kv_raw"][b, -meta["new_tok"]:].double().numpy(),
-                                             win_pos[meta["win_first_new"]:], f)
+            kv = t["kv_cache"][0].double().numpy()
+        keys = None
         if wl.mode == "csa":
-            keys = t["k_idx"][b].double().numpy() if wl.idx_dtype == "bf16" else O.fp8_block_dequantize(
-                t["k_idx"][b].numpy(), t["k_idx_scale"][b].numpy(), wl.Di)
-            O.csa_query(t["q"][b, 0].double().numpy(), qp, t["q_idx"][b, 0].double().numpy(),
-                        t["w"][b, 0].double().numpy(), kv, ent_pos, keys, win, win_pos, t["sink"].double().numpy(),
-                        wl.topk, scale, f, wl.W)
+            keys = t["k_idx"][0].double().numpy() if wl.idx_dtype == "bf16" else O.fp8_block_dequantize(
+                t["k_idx"][0].numpy(), t["k_idx_scale"][0].numpy(), wl.Di)
+        win = t["win_cache"][0].double().numpy()
+        kv_raw, z_raw = t["kv_raw"][0].double().numpy(), t["z_raw"][0].double().numpy()
+        Tq = wl.Tq
+        if Tq > 1:
+            order = [0, Tq - 1] + [int(round(x)) for x in np.linspace(0, Tq - 1, 64)[1:-1]]
         else:
-            O.hca_query(t["q"][b, 0].double().numpy(), qp, kv, ent_pos, win, win_pos, t["sink"].double().numpy(),
-                        scale, f, wl.W)
-        n_done += 1
-    dt = time.perf_counter() - t0
-    return {"value": n_done / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_done} single-sequence decode steps of {wl.name} (sequences cycled over the batch of "
-                      f"{wl.B}; fp64 NumPy oracle; {dt:.1f} s of host time)"}
+            order = [0]
+
+        def compress_step():
+            new, _ = O.compress(kv_raw, z_raw, wl.window, wl.stride, wl.pos0 + meta["E_pre"] * wl.stride, f)
+            kv[meta["E_pre"]:] = new[:meta["n_new_entries"]]
+            win[meta["win_first_new"]:] = O.rope(kv_raw[-meta["new_tok"]:], win_pos[meta["win_first_new"]:], f)
+
+        def query(tq):
+            qp = int(t["q_pos"][0, tq])
+            q = t["q"][0, tq].double().numpy()
+            if wl.mode == "csa":
+                O.csa_query(q, qp, t["q_idx"][0, tq].double().numpy(), t["w"][0, tq].double().numpy(), kv, ent_pos,
+                            keys, win, win_pos, sink, wl.topk, scale, f, wl.W)
+            else:
+                O.hca_query(q, qp, kv, ent_pos, win, win_pos, sink, scale, f, wl.W)
+
+        n_rows, t_rows, t_comp, n_comp = 0, 0.0, 0.0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s and (max_rows is None or n_rows < max_rows):
+            if Tq == 1 or n_comp == 0:
+                c0 = time.perf_counter()
+                compress_step()
+                t_comp += time.perf_counter() - c0
+                n_comp += 1
+            r0 = time.perf_counter()
+            query(order[n_rows % len(order)])
+            t_rows += time.perf_counter() - r0
+            n_rows += 1
+        if Tq == 1:
+            total = t_comp + t_rows
+            what = f"{n_rows} single-sequence decode steps"
+        else:
+            total = t_comp * n_rows / Tq + t_rows         # the chunk's compression, pro rata
+            what = (f"{n_rows} sampled query rows of the {Tq}-row chunk (first, last, uniform), the chunk's "
+                    f"compression charged pro rata")
+    return {"value": n_rows / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what} of {wl.name} (one sequence's inputs of the same shapes; fp64 NumPy oracle, "
+                      f"{cores} BLAS thread{'s' if cores > 1 else ''}; {time.perf_counter() - t0:.1f} s of host time)"}
 
 
 def achievable_peaks(torch):
@@ -550,26 +607,25 @@ def main():
             d["TFLOP_per_s"] = costs[f"{name}_flops"] / (t_ms * 1e-3) / 1e12
             d["mfma_frac"] = d["TFLOP_per_s"] / BF16_PEAK_TFLOPS
         calls[name] = d
-    # dominant call of the step; its roofline is the one its arithmetic intensity falls under
-    # (algorithmic flops per algorithmic byte against the ridge of the two datasheet peaks)
+    # dominant call of the step.  Attention (and a prefill chunk's indexer) is a dense contraction:
+    # its roofline is bf16 MFMA; the decode indexer and the compressor stream HBM.
     dom = max((k for k in calls if k != "index_compress"), key=lambda k: calls[k]["ms"])
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if dom == "attend":
-        intensity = costs["attend_flops"] / costs["attend_bytes"]
-        both = {"kernel": "csa_attend (k_attend + k_attend_combine)", "intensity_flop_per_byte": intensity,
-                "ridge_flop_per_byte": ridge, "hbm_GB_per_s": calls[dom]["GB_per_s"], "hbm_frac": calls[dom]["hbm_frac"],
-                "mfma_TFLOP_per_s": calls[dom]["TFLOP_per_s"], "mfma_frac": calls[dom]["mfma_frac"]}
-        if intensity < ridge:
-            roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": calls[dom]["hbm_frac"], "traffic": measured_traffic(wl.name, dom), **both}
-        else:
-            roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom),
-                    **both}
+    if dom == "attend" or (dom == "index" and wl.Tq >= 16):
+        kern = ("csa_attend (k_attend + k_attend_combine)" if wl.mode == "csa" else "hca_attend") if dom == "attend" \
+            else "csa_index_topk (k_index_scores_mq + top-k)"
+        intensity = costs[f"{dom}_flops"] / costs[f"{dom}_bytes"]
+        roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom), "kernel": kern,
+                "hbm_GB_per_s": calls[dom]["GB_per_s"], "hbm_frac": calls[dom]["hbm_frac"],
+                "intensity_flop_per_byte": intensity, "ridge_flop_per_byte": ridge}
     else:
         roof = {"bound": "hbm", "achieved": calls[dom]["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": calls[dom]["hbm_frac"], "traffic": measured_traffic(wl.name, dom),
                 "kernel": "csa_index_topk (k_index_scores + k_topk)" if dom == "index" else "csa_compress"}
+    for name in calls:
+        if name in tm["calls_stats"]:
+            calls[name]["stats"] = tm["calls_stats"][name]
     extra = {"calls": calls, "timing": "value = tokens / wall time of layer steps replayed from one HIP graph "
                                        "chaining the rotated layers; per_layer_graph = one graph launch per step; "
                                        "calls[*].ms = per C-ABI call, a HIP graph of that call over the rotated "
@@ -579,6 +635,7 @@ def main():
              "graph_gpu_ms_per_step": tm["graph_gpu_ms_per_step"], "eager_wall_ms_per_step": tm["eager_wall_ms_per_step"],
              "per_layer_graph_ms_per_step": tm["per_layer_graph_wall_ms_per_step"],
              "step_gpu_ms": tm["step_gpu"], "step_gpu_median_ms": tm["step_gpu_median"],
+             "step_stats": tm["step_stats"],
              "layers_rotated": tm["layers"], "pages_config_context": {
                  "layers": 61, "csa_layers": 30, "hca_layers": 31, "heads": 128, "head_dim": 512,
                  "index_topk": 1024, "sliding_window": 128}}
@@ -591,9 +648,20 @@ def main():
         e2 = {"ms_per_step": t2["wall_ms_per_step"], "tokens_per_s": w2.B * w2.Tq / (t2["wall_ms_per_step"] / 1e3),
               "attend_ms": cg2["attend"], "attend_TFLOP_per_s": c2["attend_flops"] / (cg2["attend"] * 1e-3) / 1e12,
               "attend_GB_per_s": c2["attend_bytes"] / (cg2["attend"] * 1e-3) / 1e9, "compress_ms": cg2["compress"]}
+        e2["attend_mfma_frac"] = e2["attend_TFLOP_per_s"] / BF16_PEAK_TFLOPS
+        e2["step_stats"] = t2["step_stats"]
+        e2["attend_stats"] = t2["calls_stats"]["attend"]
         if w2.mode == "csa":
             e2["index_ms"] = cg2["index"]
-            e2["index_GB_per_s"] = c2["index_bytes"] / (cg2["index"] * 1e-3) / 1e9
+            e2["index_stats"] = t2["calls_stats"]["index"]
+            if w2.Tq >= 16:
+                # a prefill chunk's scores are a contraction over keys held in LDS for 16 query rows:
+                # reported against bf16 MFMA (keys cross HBM about once per chunk, not once per row)
+                e2["index_TFLOP_per_s"] = c2["index_flops"] / (cg2["index"] * 1e-3) / 1e12
+                e2["index_mfma_frac"] = e2["index_TFLOP_per_s"] / BF16_PEAK_TFLOPS
+            else:
+                e2["index_GB_per_s"] = c2["index_bytes"] / (cg2["index"] * 1e-3) / 1e9
+                e2["index_hbm_frac"] = e2["index_GB_per_s"] / HBM_PEAK_GBS
             e2["index_compress_ms"] = cg2["index_compress"]
         if w2.reuse > 0:
             tr = time_reuse(w2, max(10, args.steps // 2), args.warmup, torch)
@@ -611,6 +679,18 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         base = cpu_baseline(wl, args.cpu_budget)
+        # the oracle on the other workloads, each on a bounded sample (tokens/s, cores stated)
+        others = {}
+        for name, budget, threads, max_rows in [("tiny_csa_decode", 3.0, None, None), ("tiny_csa_decode", 3.0, 1, None),
+                                                ("v4pro_hca_decode_1m", 4.0, None, None),
+                                                ("v4flash_csa_decode_1m_fp8", 6.0, None, None),
+                                                ("v4pro_csa_prefill_4k_on_131k", 6.0, None, 64)]:
+            if name == wl.name and threads is None:
+                continue
+            print(f"[bench] cpu oracle {name} threads={threads or 'all'}", file=sys.stderr, flush=True)
+            key = name + ("_single_thread" if threads == 1 else "")
+            others[key] = cpu_baseline(ci.WORKLOADS[name], budget, threads=threads, max_rows=max_rows)
+        extra["cpu_oracle"] = others
     line = {
         "metric": METRIC,
         "value": value,
