@@ -357,8 +357,8 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   REQUIRE(kv->C == 512 && win->C == 512, CSA_ENOTSUP, "head dim must be 512 (kv %d, win %d)", kv->C, win->C);
   REQUIRE(win->dtype == CSA_BF16, CSA_ENOTSUP, "window cache must be bf16");
   REQUIRE(win->window == 1 && win->stride == 1, CSA_EINVAL, "window cache must have window = stride = 1");
-  REQUIRE(kv->dtype == CSA_BF16 || kv->scale_block % 8 == 0, CSA_ENOTSUP,
-          "fp8 KV scale_block must be a multiple of 8 (got %d)", kv->scale_block);
+  REQUIRE(kv->dtype != CSA_FP8_E4M3 || kv->scale_block % 64 == 0, CSA_ENOTSUP,
+          "fp8 KV scale_block must be a multiple of 64 (got %d)", kv->scale_block);
   REQUIRE(W >= 0, CSA_EINVAL, "W must be >= 0 (got %d)", W);
   REQUIRE(out_dtype == CSA_FP32 || out_dtype == CSA_BF16, CSA_ENOTSUP, "out_dtype must be FP32 or BF16");
   REQUIRE(aligned(q, 16) && aligned(out, 16), CSA_EINVAL, "q and out must be 16-byte aligned");
@@ -407,9 +407,10 @@ static int attend_common(const void* q, const int64_t* q_pos, int B, int Tq, int
   a.lse = lse_out;
   a.slot_cap = slot_cap;
   if (need > 0) {
-    const int ns = csa::attend_plan(rows, H, slot_cap).nsplit;
-    a.part_o = static_cast<uint16_t*>(workspace);
-    a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)rows * ns * H * 512);
+    const csa::AttendCarve cv =
+        csa::attend_carve(rows, H, csa::attend_plan(rows, H, slot_cap, csa_mode, csa::att_kind(kv->dtype)));
+    a.part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + cv.part_o);
+    a.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + cv.part_ml);
   }
   a.csa_mode = csa_mode ? 1 : 0;
   hipError_t e;

@@ -9,23 +9,28 @@
 // sink and partial-RoPE rows; atlas Raw config fields head_dim 512, one KV head).
 //
 // Kernel design (gfx950, wave64, bf16 MFMA 16x16x32, fp32 accumulation):
-//  * a block = 8 waves in tile groups: two groups of 4 waves holding 64 heads (32-row tiles),
-//    or four groups of 2 waves holding 32 heads (16-row tiles), 16 heads per wave, for one
-//    query row and one split of its row set.  Tiles are staged in LDS and used by all waves
-//    of a group for both contractions (K = V); the groups take alternate tiles and merge
-//    their softmax states through LDS at the end, so each SIMD runs two waves whose load,
-//    softmax and MFMA phases overlap;
-//  * scores are computed transposed, S^T = K Q^T (M = rows, N = heads, K = channels),
-//    and the output as O^T = V^T P^T (M = channels, N = heads, K = rows): every
-//    accumulator lane then belongs to one head, so the online-softmax statistics,
-//    the rescaling and the final normalisation stay in the lane, and the P tile
-//    leaves the score accumulators already in the B-operand layout of the second
-//    contraction;
-//  * the V^T operand is read from the same row-major LDS tile with the gfx950
-//    transposing LDS load (ds_read_b64_tr_b16), so no transposed copy is stored;
-//  * the block's query rows reach LDS by DMA once (both tile groups read their fragments
-//    there), issued at entry together with the first top-k indices, ahead of the scalar
-//    loads that size the row set;
+//  * a block = NP wave pairs for one query row and one split of its row set; pair p owns
+//    16 heads.  Rows are staged in LDS in 32-row tiles through a ring of four tile
+//    buffers, so three tiles are in flight while one is consumed, and every wave of the
+//    block uses every staged row (the block's 16 NP heads share it as key and value);
+//  * scores are computed transposed, S^T = K Q^T (M = rows, N = heads, K = channels):
+//    wave h of a pair scores rows 16h .. 16h + 15 of a tile for its pair's heads, so every
+//    accumulator lane belongs to one head;
+//  * the two waves of a pair exchange their tiles' maxima and their softmax weights P
+//    through LDS; then each computes O^T = V^T P^T (M = channels, N = heads, K = rows) over
+//    all 32 rows for half the channels (wave h: channels 256h .. 256h + 255), so each wave
+//    holds 64 accumulator registers instead of 128 and a block of eight waves covers 64
+//    heads with one copy of each row;
+//  * the V^T operand is read from the same row-major LDS tile with the gfx950 transposing
+//    LDS load (ds_read_b64_tr_b16), so no transposed copy is stored;
+//  * the loop is software pipelined by one tile: the scores of tile t + 1 and the P V
+//    product of tile t run back to back, then the maxima and weights of tile t + 1 are
+//    exchanged (two barriers per tile);
+//  * bf16 rows reach LDS by direct DMA; fp8 and fp4 entry rows go through registers.  fp4
+//    codes times their power-of-two scale are exact in bf16.  fp8 rows are staged as their
+//    exact codes and the per-64-channel scales are applied in fp32: to the scores per
+//    channel block, and to the weights per channel block in P V, carried as bf16 hi + lo
+//    parts so that the scaled weights keep about 16 bits;
 //  * the sink joins the denominator once, in the epilogue (one split) or the split merge;
 //  * lazy rescaling: the reference maximum moves only when a tile exceeds it by 2^8;
 //  * several splits of the row set run in parallel when the query rows alone cannot
@@ -36,29 +41,20 @@
 
 namespace csa {
 
-constexpr int kAttWaves = 8;
-constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kD = 512;             // channels (head dim)
-// bf16 per LDS row: 1056 B, so consecutive rows start 8 banks apart.  Measured with the LDS
-// bank-conflict counter at the 65K decode shape: no conflicts at this pitch (for the scores'
-// 16-byte row reads and the transposing reads of P V alike), against 2.4 M conflict cycles per
-// launch at 1040, 1072, 1088 or 1104 bytes.
+// bf16 per LDS row: 1056 B, so consecutive rows start 8 banks apart (no bank conflicts for the
+// scores' 16-byte row reads or the transposing reads of P V at this pitch).
 constexpr int kPitch = 528;
-constexpr int kStepRows = 64;       // rows staged per step (one tile per group); two steps in LDS
-constexpr int kTargetBlocks = 256;  // split until the grid has about this many blocks
+constexpr int kTR = kAttTile;       // rows per tile
 constexpr float kRescale = 8.f;     // lazy-rescale threshold (log2 units)
 
-// Block shapes.  HPB = heads per block: 64 (two groups of 4 waves, 32-row tiles) or 32 (four
-// groups of 2 waves, 16-row tiles).  Both stage 64 rows per step; each row read from LDS
-// serves 16 heads per wave either way.  The 32-head shape gives twice the blocks for the same
-// splits, for calls too small to fill the GPU with the 64-head shape; its 16-row tiles take
-// the 16x16x16 MFMA for P V (half the work per instruction), so it is slower per row.
-template <int HPB>
-struct AttCfg {
-  static constexpr int GW = HPB / 16;            // waves per tile group
-  static constexpr int NG = kAttWaves / GW;      // tile groups
-  static constexpr int T = kStepRows / NG;       // rows per tile
-  static constexpr int RPT = T / 8;              // rows of each tile a wave moves per step
+// Block shape: NP wave pairs, 16 heads each.
+template <int NP>
+struct AttShape {
+  static constexpr int HPB = 16 * NP;     // heads per block
+  static constexpr int NW = 2 * NP;       // waves
+  static constexpr int NT = 64 * NW;      // threads
+  static constexpr int RPW = kTR / NW;    // rows of a tile each wave moves
 };
 
 __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int window, int stride,
@@ -70,6 +66,8 @@ __device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int wi
 }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 
 // Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups holding one head) with
 // the gfx950 lane-swap permutes, no LDS round trip.
@@ -92,21 +90,76 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 
 // Hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which softmax weights tolerate.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Wait until at most N vector-memory loads of this wave are outstanding (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima = no wait).
+// vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima = no wait).  Loads
+// complete in issue order.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Workgroup barrier for the tile ring.  __syncthreads() is a release fence plus the barrier, and
+// the fence waits for every LDS write of the wave, the DMA loads into LDS included: no tile could
+// stay in flight across it.  Here the waits are explicit instead: this wave's own LDS stores
+// (lgkmcnt(0)) before the barrier, and (by the caller, with wait_tiles) the DMA of exactly the
+// tiles the next step reads.  The "memory" clobber keeps the compiler from moving LDS accesses
+// across the barrier; it still counts the DMA loads that are in flight for every later LDS read.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
-// KVF: the compressed cache's storage (CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1); HPB: the
-// block shape (AttCfg).
-template <bool CSA, int KVF, int HPB>
-__global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
-  constexpr bool QKV = KVF != CSA_BF16;   // quantized entry rows take the register path
-  constexpr int kRowB = KVF == CSA_FP8_E4M3 ? kD : (KVF == CSA_FP4_E2M1 ? kD / 2 : 2 * kD);
+// One 1 KB row from global memory into LDS (16 bytes per lane, lane i at lds_row + 16 i) by the
+// direct global-to-LDS load, issued through inline asm: the compiler's own tracking of these loads
+// cannot tell the four tile buffers apart, and would wait for every load in flight before any read
+// of any tile buffer.  The ring's waits are explicit instead (wait_tiles before ring_barrier), and
+// the "memory" clobber keeps LDS accesses from moving across the issue.
+__device__ __forceinline__ void dma_row(const void* src_lane, uint16_t* lds_row) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_row;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(src_lane)
+               : "memory", "m0");
+}
+
+// wait until at most k tiles of RPW loads each are outstanding, k in 0..3
+template <int RPW>
+__device__ __forceinline__ void wait_tiles(int k) {
+  switch (k) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<RPW>(); break;
+    case 2: wait_vmcnt<2 * RPW>(); break;
+    default: wait_vmcnt<3 * RPW>(); break;
+  }
+}
+
+// ---------------------------------------------------------------- grouped kernel (bf16 caches)
+//
+// A block = 8 waves in tile groups: two groups of 4 waves holding 64 heads (32-row tiles), or four
+// groups of 2 waves holding 32 heads (16-row tiles), 16 heads and all 512 channels per wave, for one
+// query row and one split of its row set.  A step stages 64 rows (one tile per group) in LDS by
+// DMA; each group uses its tile for both contractions (K = V), the groups take alternate tiles and
+// merge their softmax states through LDS at the end, so each SIMD runs two waves whose load,
+// softmax and MFMA phases overlap.  Two steps fit in LDS: the next step's rows stream in while the
+// current one is consumed.  Scores and outputs are transposed as in the pair kernel below; the
+// rotated query dims are carried as bf16 hi + lo; the sink joins once (epilogue or merge); lazy
+// rescaling; weights rounded to bf16 for P V and normalised by their own sum.
+constexpr int kAttWaves = 8;
+constexpr int kAttThreads = kAttWaves * 64;
+constexpr int kStepRows = 64;       // rows staged per step (one tile per group); two steps in LDS
+
+template <int HPB>
+struct AttCfg {
+  static constexpr int GW = HPB / 16;            // waves per tile group
+  static constexpr int NG = kAttWaves / GW;      // tile groups
+  static constexpr int T = kStepRows / NG;       // rows per tile
+  static constexpr int RPT = T / 8;              // rows of each tile a wave moves per step
+  static_assert(T == kAttGroupTile64 * HPB / 64, "tile rows must match the plan's");
+};
+
+// Grouped kernel (bf16 caches); HPB: the block shape (AttCfg).
+template <bool CSA, int HPB>
+__global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
+  constexpr bool QKV = false;
+  constexpr int kRowB = 2 * kD;
   constexpr int GW = AttCfg<HPB>::GW, NG = AttCfg<HPB>::NG, T = AttCfg<HPB>::T, RPT = AttCfg<HPB>::RPT;
   // Two halves of tile buffers as two objects: one step's tiles are read from one half while
   // the next step's stream into the other, and separate objects let the compiler see that the
@@ -224,67 +277,14 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   auto issue_row = [&](int pr, const PairRows& pr_rows, int k, uint16_t* half) {
     const int t = NG * pr + k / RPT;
     if (t >= ntile) return;
-    // fp8/fp4 caches: entry rows take the register path, and empty slots (-1) are zero-filled
-    // there, since the bytes of a quantized row read as bf16 may be NaN (masked scores do not
-    // cancel a NaN in P x V)
-    if (QKV && __builtin_amdgcn_readlane(pr_rows.r, k) >= -1) return;
     const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(pr_rows.off >> 32), k);
     const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)pr_rows.off, k);
     const int64_t off = (int64_t)((hi << 32) | lo);
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(kvb + off + 16 * lane),
                                      (lds_void*)row_dst(half, k), 16, 0, 0);
   };
-  // fp8 / fp4 entry rows: codes and the channel block's scale go through registers and
-  // are widened to bf16 (code * scale, rounded; exact for fp4) on the way into LDS.  Lane
-  // l holds channels 8l .. 8l + 7 of the row: 8 fp8 codes, or 8 fp4 codes in one word.
-  u32x2 pre8[8];
-  float pres[8];
-  auto fetch_q = [&](int pr, const PairRows& pr_rows) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
-      pre8[k] = u32x2{0u, 0u};
-      pres[k] = 0.f;
-      if (NG * pr + k / RPT < ntile && r >= 0) {
-        const int64_t rg = (int64_t)b * a.kv_cap + r;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv) + rg * kRowB;
-        if (KVF == CSA_FP4_E2M1) pre8[k][0] = *reinterpret_cast<const uint32_t*>(src + 4 * lane);
-        else pre8[k] = *reinterpret_cast<const u32x2*>(src + 8 * lane);
-        pres[k] = a.kv_scales[rg * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
-      }
-    }
-  };
-  auto store_q = [&](int pr, const PairRows& pr_rows, uint16_t* half) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int t = NG * pr + k / RPT;
-      const int r = __builtin_amdgcn_readlane(pr_rows.r, k);
-      if (t < ntile && r >= -1) {
-        const float sc = pres[k];
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (r == -1) {
-        } else if (KVF == CSA_FP4_E2M1) {
-          // gfx950's scaled converter: byte i (channels 2i, 2i + 1 in its low and high nibbles)
-          // times the block's power-of-two scale, to a bf16 pair; exact, as code x scale fits
-          // bf16 (checked bit for bit against the E2M1 definition for every byte and every
-          // power-of-two scale 2^-127 .. 2^127)
-          const uint32_t w = pre8[k][0];
-          v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
-          v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
-          v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
-          v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
-        } else {
-          const f32x2 f0 = fp8x2_lo(pre8[k][0]), f1 = fp8x2_hi(pre8[k][0]);
-          const f32x2 f2 = fp8x2_lo(pre8[k][1]), f3 = fp8x2_hi(pre8[k][1]);
-          v[0] = pack_bf16x2(f0[0] * sc, f0[1] * sc);
-          v[1] = pack_bf16x2(f1[0] * sc, f1[1] * sc);
-          v[2] = pack_bf16x2(f2[0] * sc, f2[1] * sc);
-          v[3] = pack_bf16x2(f3[0] * sc, f3[1] * sc);
-        }
-        *reinterpret_cast<u32x4*>(row_dst(half, k) + 8 * lane) = v;
-      }
-    }
-  };
+  auto fetch_q = [&](int, const PairRows&) {};
+  auto store_q = [&](int, const PairRows&, uint16_t*) {};
 
   // ---- prologue: the first step's rows go out as soon as their indices arrive (the query
   // loads behind them complete later, in order), and the rotation table is built while
@@ -597,9 +597,545 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend(AttendArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------- wave-pair kernel (quantized caches)
+
+// KVF: the compressed cache's storage (CSA_BF16, CSA_FP8_E4M3 or CSA_FP4_E2M1); NP: wave pairs.
+template <bool CSA, int KVF, int NP>
+__global__ void __launch_bounds__(AttShape<NP>::NT) k_attend(AttendArgs a) {
+  using Sh = AttShape<NP>;
+  constexpr int HPB = Sh::HPB, NW = Sh::NW, RPW = Sh::RPW;
+  constexpr bool QKV = KVF != CSA_BF16;       // quantized entry rows take the register path
+  constexpr bool F8 = KVF == CSA_FP8_E4M3;    // exact codes in LDS; block scales applied in fp32
+  constexpr int kRowB = F8 ? kD : (KVF == CSA_FP4_E2M1 ? kD / 2 : 2 * kD);
+  static_assert(HPB <= 2 * kTR, "the block's query rows are staged in two tile buffers");
+
+  // Four tile buffers as four objects: the compiler can then see that the DMA into one does not
+  // alias the reads of another (and does not wait for it before those reads).
+  __shared__ __attribute__((aligned(16))) uint16_t tb0[kTR * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tb1[kTR * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tb2[kTR * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t tb3[kTR * kPitch];
+  __shared__ __attribute__((aligned(16))) int32_t idxl[CSA ? kAttIdxMax : 4];   // the split's top-k indices
+  __shared__ __attribute__((aligned(16))) uint32_t pbuf[2][NP][2][kWave][2];   // weights P (bf16), by parity
+  __shared__ float mref[2][NP][2][16];          // the producing wave's reference of those weights
+  __shared__ __attribute__((aligned(4))) uint8_t tvalid[4][kTR];
+  __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
+  __shared__ __attribute__((aligned(16))) float qsc[F8 ? 4 : 1][kD / 64][kTR];   // fp8 row scales
+  __shared__ f32x4 xch[NP][2][16];              // end of the row set: (l, m_own, amax) per wave and head
+
+  const int HG = (a.H + HPB - 1) / HPB;
+  const uint32_t logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int hg = logical % HG;
+  const int split = (logical / HG) % a.nsplit;
+  const int row = logical / (HG * a.nsplit);
+  const int b = row / a.Tq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  const int p = wave >> 1, h = wave & 1;                        // pair (16 heads), half
+  const int n = lane & 15, g = lane >> 4;
+  const int head = hg * HPB + 16 * p + n;
+  const bool head_ok = head < a.H;
+
+  // ---- loads that need only the block's coordinates go out first: the split's top-k indices
+  // (CSA) and the block's query rows, both by DMA into LDS
+  const int s0 = split * a.slots_per_split;
+  if (CSA) {
+    const int nidx = max(0, min(a.slots_per_split, a.topk - s0));
+    const int32_t* irow = a.idx + (int64_t)row * a.topk;
+    for (int i = wave; i * kWave < nidx; i += NW) {
+      const int j = min(s0 + i * kWave + lane, a.topk - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(irow + j), (lds_void*)(idxl + i * kWave), 4,
+                                       0, 0);
+    }
+  }
+  {
+    // query row r (head hg HPB + r) at row r % 32 of tile buffer 2 + r / 32; wave w moves rows
+    // w, w + NW, ...
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)row * a.H * (2 * kD);
+#pragma unroll
+    for (int i = 0; i < HPB / NW; ++i) {
+      const int r = wave + NW * i;              // i < kTR / NW: rows 0..31 (buffer 2), else 32..63
+      const int hq = min(hg * HPB + r, a.H - 1);
+      const void* src = qb + (int64_t)hq * (2 * kD) + 16 * lane;
+      if (i < kTR / NW) __builtin_amdgcn_global_load_lds(src, (lds_void*)(tb2 + r * kPitch), 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds(src, (lds_void*)(tb3 + (r - kTR) * kPitch), 16, 0, 0);
+    }
+  }
+  const int64_t pq = a.q_pos[row];
+  if (tid < a.rope_dim / 2) {
+    float cs, sn;
+    rope_cs(pq, a.inv_freq[tid], cs, sn);
+    rtab[tid] = f32x2{cs, sn};
+  }
+
+  // ---- the row set of this query: entries, then window rows
+  const int kv_nv = min(max(a.kv_n_valid[b], 0), a.kv_cap);
+  const int n_ent = CSA ? a.topk
+                        : visible_rows_att(pq, a.kv_pos0[b], a.kv_window, a.kv_stride, a.kv_n_valid[b], a.kv_cap);
+  const int64_t wp0 = a.win_pos0[b];
+  const int w_nv = min(max(a.win_n_valid[b], 0), a.win_cap);
+  int64_t r_lo = pq - a.W + 1 - wp0;
+  int64_t r_hi = pq - wp0;
+  if (r_lo < 0) r_lo = 0;
+  if (r_hi > w_nv - 1) r_hi = w_nv - 1;
+  const int n_win = (a.W > 0 && r_hi >= r_lo) ? (int)(r_hi - r_lo + 1) : 0;
+  const int n_slots = n_ent + n_win;
+  const int s1 = min(n_slots, s0 + a.slots_per_split);
+  const int ntile = s1 > s0 ? (s1 - s0 + kTR - 1) / kTR : 0;
+
+  const uint8_t* kvb = reinterpret_cast<const uint8_t*>(a.kv) + (int64_t)b * a.kv_cap * kRowB;
+  const uint8_t* winb = reinterpret_cast<const uint8_t*>(a.win) + (int64_t)b * a.win_cap * (2 * kD);
+  const int64_t win_off = winb - kvb;   // window rows are addressed from the kv base too
+  // the row a missing slot loads before it is zeroed: the first window row of the query when
+  // there is one, else kv row 0 (bf16 caches only; quantized caches load nothing for it)
+  const int ph_row = n_win > 0 ? -2 - (int)r_lo : 0;
+
+  wait_vmcnt<0>();
+  __syncthreads();   // indices and query rows in LDS
+
+  // ---- rows.  Wave w moves rows w + NW i (i < RPW) of every tile.  Lane i < RPW holds the
+  // number of the row it names: a kv row (>= 0), -2 - a window row, or -1 for none.
+  auto tile_rows = [&](int t) -> int {
+    const int slot = s0 + t * kTR + wave + NW * lane;
+    int r = -1;
+    if (lane < RPW && slot < s1) {
+      if (slot >= n_ent) r = -2 - (int)(r_lo + (slot - n_ent));
+      else if (!CSA) r = slot;
+      else {
+        const int j = idxl[slot - s0];
+        r = (j >= 0 && j < kv_nv) ? j : -1;
+      }
+    }
+    return r;
+  };
+  auto row_off = [&](int r) -> int64_t {
+    return r >= 0 ? (int64_t)r * kRowB : (r <= -2 ? win_off + (int64_t)(-2 - r) * (2 * kD) : 0);
+  };
+  // flags and (bf16) the DMA of every row into its own slot: exactly RPW loads per wave per tile,
+  // so that the load counter tells which tile has landed.  A missing row (-1) loads a valid
+  // placeholder row and is zeroed once it has landed (zero_tile): stale or unwritten bytes could
+  // be NaN, which a zero weight does not cancel in P V.
+  auto issue_tile = [&](int rr, uint16_t* buf, int st) {
+    if (lane < RPW) tvalid[st][wave + NW * lane] = rr != -1;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = __builtin_amdgcn_readlane(rr, i);
+      if (QKV && r >= -1) continue;           // quantized entry rows go through registers
+      const int64_t off = row_off(r == -1 ? ph_row : r);
+      dma_row(kvb + off + 16 * lane, buf + (wave + NW * i) * kPitch);
+    }
+  };
+  auto zero_tile = [&](int rr, uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if (__builtin_amdgcn_readlane(rr, i) == -1)
+        *reinterpret_cast<u32x4*>(buf + (wave + NW * i) * kPitch + 8 * lane) = u32x4{0u, 0u, 0u, 0u};
+  };
+  // quantized entry rows: codes and the channel block's scale through registers.  Lane l holds
+  // channels 8l .. 8l + 7 of the row: 8 fp8 codes, or 8 fp4 codes in one word.
+  u32x2 pre8[QKV ? RPW : 1];
+  float pres[QKV ? RPW : 1];
+  auto fetch_q = [&](int rr) {
+    if constexpr (QKV) {
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int r = __builtin_amdgcn_readlane(rr, i);
+        pre8[i] = u32x2{0u, 0u};
+        pres[i] = 0.f;
+        if (r >= 0) {
+          const int64_t rg = (int64_t)b * a.kv_cap + r;
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.kv) + rg * kRowB;
+          if (KVF == CSA_FP4_E2M1) pre8[i][0] = *reinterpret_cast<const uint32_t*>(src + 4 * lane);
+          else pre8[i] = *reinterpret_cast<const u32x2*>(src + 8 * lane);
+          pres[i] = a.kv_scales[rg * (kD / a.kv_scale_block) + (8 * lane) / a.kv_scale_block];
+        }
+      }
+    }
+  };
+  auto store_q = [&](int rr, uint16_t* buf, int st) {
+    if constexpr (QKV) {
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int r = __builtin_amdgcn_readlane(rr, i);
+        const int tr = wave + NW * i;
+        if (F8 && (lane & 7) == 0) qsc[st][lane >> 3][tr] = r >= 0 ? pres[i] : (r == -1 ? 0.f : 1.f);
+        if (r < -1) continue;                  // window rows came by DMA
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};       // a missing row stays zero
+        if (r >= 0) {
+        if constexpr (KVF == CSA_FP4_E2M1) {
+          // gfx950's scaled converter: byte i (channels 2i, 2i + 1 in its low and high nibbles)
+          // times the block's power-of-two scale, to a bf16 pair; exact, as code x scale fits bf16
+          const uint32_t w = pre8[i][0];
+          const float sc = pres[i];
+          v[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+          v[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+          v[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+          v[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+        } else {
+          // E4M3FN codes to bf16, exactly (every E4M3 value is a bf16 value): the scaled
+          // converter with scale 1, two codes to a bf16 pair
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t w = pre8[i][k];
+            v[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+            v[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+          }
+        }
+        }
+        *reinterpret_cast<u32x4*>(buf + tr * kPitch + 8 * lane) = v;
+      }
+    }
+  };
+
+  // ---- prologue: tiles 0 and 1 go out while the query fragments are read; tiles 2 and 3 once
+  // the query rows (in tile buffers 2 and 3) are no longer needed
+  const int rows0 = tile_rows(0), rows1 = tile_rows(1), rows2 = tile_rows(2), rows3 = tile_rows(3);
+  int rows_next = tile_rows(4);
+  if constexpr (!QKV) {
+    if (ntile > 0) issue_tile(rows0, tb0, 0);
+    if (ntile > 1) issue_tile(rows1, tb1, 1);
+  } else {
+    if (ntile > 0) { issue_tile(rows0, tb0, 0); fetch_q(rows0); }
+  }
+  // query fragments (B operand of S^T = K Q^T): head = n, channels 32c + 8g + [0, 8).  The
+  // rotated query is not a bf16 value: its last two chunks (channels 448..511, which hold the
+  // rotated pairs for rope_dim <= 64) are carried as bf16 hi + lo so the logits keep fp32
+  // accuracy; rotated channels below 448 (rope_dim > 64) are rounded to bf16.
+  bf16x8 qf[16];
+  bf16x8 qlo[2];
+  {
+    const int rot0 = kD - a.rope_dim;
+    const int qr = 16 * p + n;
+    const uint16_t* qs = (p < 2 ? tb2 : tb3) + (qr % kTR) * kPitch + 8 * g;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qs + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 lo = {0u, 0u, 0u, 0u};
+      if (32 * c + 32 > rot0 && a.rope_dim > 0) {
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const int d = 32 * c + 8 * g + 2 * k2;
+          if (d >= rot0) {
+            const f32x2 t2 = rtab[(d - rot0) >> 1];
+            const float cs = t2[0], sn = t2[1];
+            const float x0 = bf16lo_to_f32(v[k2]), x1 = bf16hi_to_f32(v[k2]);
+            const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+            v[k2] = pack_bf16x2(y0, y1);
+            lo[k2] = pack_bf16x2(y0 - bf16lo_to_f32(v[k2]), y1 - bf16hi_to_f32(v[k2]));
+          }
+        }
+      }
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+      if (c >= 14) qlo[c - 14] = __builtin_bit_cast(bf16x8, lo);
+    }
+  }
+  const bool q_split = a.rope_dim > 0;
+  __syncthreads();   // every wave has its query fragments: tile buffers 2 and 3 are free
+  if constexpr (!QKV) {
+    if (ntile > 2) issue_tile(rows2, tb2, 2);
+    if (ntile > 3) issue_tile(rows3, tb3, 3);
+    wait_tiles<RPW>(max(0, min(ntile, 4) - 1));    // tile 0 has landed
+    if (ntile > 0) zero_tile(rows0, tb0);
+  } else {
+    // quantized rows: one tile in registers at a time; tiles 0..2 are stored here, tile 3 is
+    // left in flight for the loop
+    wait_vmcnt<0>();
+    if (ntile > 0) store_q(rows0, tb0, 0);
+    if (ntile > 1) { issue_tile(rows1, tb1, 1); fetch_q(rows1); wait_vmcnt<0>(); store_q(rows1, tb1, 1); }
+    if (ntile > 2) { issue_tile(rows2, tb2, 2); fetch_q(rows2); wait_vmcnt<0>(); store_q(rows2, tb2, 2); }
+    if (ntile > 3) { issue_tile(rows3, tb3, 3); fetch_q(rows3); }
+  }
+  ring_barrier();
+
+  // ---- online softmax state.  Lane (n, g) of a wave works for head n.  Two references per
+  // wave, both integers in log2 units, so that moving weights between them is an exact
+  // power-of-two scaling of bf16 values:
+  //  * m_own, for the weights of this wave's own rows (16h .. 16h + 15 of each tile): it starts
+  //    at the first tile's maximum (rounded up) and moves only when a tile's maximum exceeds it
+  //    by more than kRescale, so a dominant row gets weight 2^(s - m_own) <= 1 exactly rounded;
+  //    l_own sums those weights in fp32 (for lse);
+  //  * m_acc, for this wave's P V accumulators, which take the weights of both waves of the
+  //    pair, each rescaled from its producer's reference by an exact power of two; it moves
+  //    lazily the same way.  n_acc sums the weights exactly as they enter the product (bf16)
+  //    and normalises the output, so the rounding of a dominant weight cancels between
+  //    numerator and denominator.  Both waves of a pair see the same weights and references,
+  //    so they hold the same m_acc and n_acc.
+  // The sink joins once, in the epilogue or in the split merge.
+  float m_own = kNegBig, l_own = 0.f;
+  float m_acc = kNegBig, n_acc = 0.f;
+  f32x4 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Scores of this wave's rows of the tile in `buf` (stage st): S^T for rows 16h + [0, 16),
+  // then the weights of rows 16h + 4g + i against this wave's reference, published with that
+  // reference in parity slot par of pbuf / mref.
+  auto score = [&](const uint16_t* buf, int st, int par) {
+    const uint16_t* rp = buf + (16 * h + n) * kPitch + 8 * g;
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (!F8) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + 32 * c);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sacc, 0, 0, 0);
+        if (c >= 14 && q_split) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[c - 14], sacc, 0, 0, 0);
+      }
+    } else {
+      // exact codes: one partial product per 64-channel block, times the rows' block scale
+#pragma unroll
+      for (int blk = 0; blk < 8; ++blk) {
+        f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 2 * blk; c < 2 * blk + 2; ++c) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + 32 * c);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], part, 0, 0, 0);
+          if (c >= 14 && q_split) part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[c - 14], part, 0, 0, 0);
+        }
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(&qsc[st][blk][16 * h + 4 * g]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[i] = fmaf(s4[i], part[i], sacc[i]);
+      }
+    }
+    const uint32_t vf = *reinterpret_cast<const uint32_t*>(&tvalid[st][16 * h + 4 * g]);
+    float sv[4];
+    float tmax = kNegBig;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = ((vf >> (8 * i)) & 0xffu) ? sacc[i] * a.scale_log2 : kNegBig;
+      tmax = fmaxf(tmax, sv[i]);
+    }
+    tmax = max_lane_groups(tmax);
+    // lazy rescaling of the own reference (see above); weights stay below 2^kRescale
+    const bool grow = tmax > m_own + kRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? ceilf(tmax) : m_own;
+      l_own *= fast_exp2(m_own - m_new);
+      m_own = m_new;
+    }
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = sv[i] > kNegBig ? fast_exp2(sv[i] - m_own) : 0.f;
+      l_own += pv[i];
+    }
+    *reinterpret_cast<u32x2*>(&pbuf[par][p][h][lane][0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+    if (g == 0) mref[par][p][h][n] = m_own;
+  };
+  // 2^k for an integer k (exact); 0 far below the range
+  auto pow2i = [](float k) -> float { return ldexpf(1.f, (int)fmaxf(k, -200.f)); };
+  // O^T += V^T P^T over the 32 rows of the tile in `buf`, channels 256h + [0, 256), with the pair's
+  // weights from parity slot par.  The K index of the contraction is permuted: k = 8g' + j names
+  // row 4g' + j (j < 4, wave 0's rows) or 16 + 4g' + j - 4 (wave 1's rows), for P (as each wave's
+  // lanes hold it) and V^T (two transposing reads of four rows each) alike.
+  auto pv_product = [&](const uint16_t* buf, int st, int par) {
+    const float r0 = mref[par][p][0][n], r1 = mref[par][p][1][n];
+    const float rt = fmaxf(r0, r1);
+    const bool grow = rt > m_acc + kRescale;
+    if (__any(grow)) {
+      const float m_new = grow ? rt : m_acc;
+      const float alpha = pow2i(m_acc - m_new);
+      n_acc *= alpha;
+      if (__any(grow && m_acc > kNegBig)) {
+#pragma unroll
+        for (int db = 0; db < 16; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+      }
+      m_acc = m_new;
+    }
+    // the producers' weights on this wave's reference: exact power-of-two rescaling of bf16
+    const float f0 = pow2i(r0 - m_acc), f1 = pow2i(r1 - m_acc);
+    const u32x2 pa = *reinterpret_cast<const u32x2*>(&pbuf[par][p][0][lane][0]);
+    const u32x2 pb = *reinterpret_cast<const u32x2*>(&pbuf[par][p][1][lane][0]);
+    float w[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      w[2 * k] = bf16lo_to_f32(pa[k]) * f0;
+      w[2 * k + 1] = bf16hi_to_f32(pa[k]) * f0;
+      w[4 + 2 * k] = bf16lo_to_f32(pb[k]) * f1;
+      w[4 + 2 * k + 1] = bf16hi_to_f32(pb[k]) * f1;
+    }
+    n_acc += ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+    const int L = lane & 15;
+    const uint16_t* v0p = buf + (4 * g + (L >> 2)) * kPitch + 256 * h + 4 * (L & 3);
+    const uint16_t* v1p = buf + (16 + 4 * g + (L >> 2)) * kPitch + 256 * h + 4 * (L & 3);
+    if constexpr (!F8) {
+      u32x4 pw;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) pw[k] = pack_bf16x2(w[2 * k], w[2 * k + 1]);   // exact
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0p + 16 * db));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1p + 16 * db));
+        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl) {
+        // the weights times the rows' scale of channel block 4h + bl, as bf16 hi + lo
+        const int blk = 4 * h + bl;
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(&qsc[st][blk][4 * g]);
+        const f32x4 sb = *reinterpret_cast<const f32x4*>(&qsc[st][blk][16 + 4 * g]);
+        float ws[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { ws[i] = w[i] * sa[i]; ws[4 + i] = w[4 + i] * sb[i]; }
+        u32x4 hi, lo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          hi[k] = pack_bf16x2(ws[2 * k], ws[2 * k + 1]);
+          lo[k] = pack_bf16x2(ws[2 * k] - bf16lo_to_f32(hi[k]), ws[2 * k + 1] - bf16hi_to_f32(hi[k]));
+        }
+        const bf16x8 pfh = __builtin_bit_cast(bf16x8, hi), pfl = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) {
+          const int db = 4 * bl + d4;
+          const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0p + 16 * db));
+          const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1p + 16 * db));
+          const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfh, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pfl, acc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // tile 0: scores and weights
+  if (ntile > 0) {
+    score(tb0, 0, 0);
+    if constexpr (!QKV) {
+      wait_tiles<RPW>(max(0, min(ntile, 4) - 2));   // tile 1 has landed
+      if (ntile > 1) zero_tile(rows1, tb1);
+    }
+    ring_barrier();
+  }
+
+  // One step, one barrier: the scores and weights of tile t + 1 (buffer bs, stage ss) and the
+  // P V product of tile t (buffer bp, stage sp); after the barrier bp receives tile t + 4, and
+  // (quantized rows) tile t + 3's registers are stored into buffer b3 (stage s3).
+  int rows_reg = rows3;   // quantized rows: the tile whose codes are in registers
+  // bz (bf16 rows): tile t + 2's buffer, whose missing rows are zeroed once it has landed.
+  auto step = [&](int t, const uint16_t* bs, int ss, uint16_t* bp, int sp, uint16_t* b3, int s3, uint16_t* bz) {
+    if (t + 1 < ntile) score(bs, ss, (t + 1) & 1);
+    pv_product(bp, sp, t & 1);
+    if constexpr (!QKV) {
+      wait_tiles<RPW>(max(0, min(ntile, t + 4) - (t + 3)));   // tile t + 2 has landed
+      if (t + 2 < ntile) zero_tile(tile_rows(t + 2), bz);
+    }
+    ring_barrier();   // weights of tile t + 1 and tile t + 2 visible; tile t and its weights done
+    const int rr = rows_next;
+    rows_next = tile_rows(t + 5);
+    if constexpr (!QKV) {
+      if (t + 4 < ntile) issue_tile(rr, bp, sp);
+    } else {
+      if (t + 3 < ntile) { wait_vmcnt<0>(); store_q(rows_reg, b3, s3); }
+      if (t + 4 < ntile) { issue_tile(rr, bp, sp); fetch_q(rr); }
+      rows_reg = rr;
+    }
+  };
+  for (int t = 0; t < ntile; t += 4) {
+    step(t, tb1, 1, tb0, 0, tb3, 3, tb2);
+    if (t + 1 >= ntile) break;
+    step(t + 1, tb2, 2, tb1, 1, tb0, 0, tb3);
+    if (t + 2 >= ntile) break;
+    step(t + 2, tb3, 3, tb2, 2, tb1, 1, tb0);
+    if (t + 3 >= ntile) break;
+    step(t + 3, tb0, 0, tb3, 3, tb2, 2, tb1);
+  }
+
+  // ---- epilogue: the pair's sums on the accumulator reference and (for partials) the largest
+  // output magnitude per head
+  const float l_w = sum_lane_groups(l_own);
+  const float n_tot = sum_lane_groups(n_acc);
+  float amax = 0.f;
+  if (a.nsplit > 1) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc[db][i]));
+    amax = max_lane_groups(amax);
+  }
+  if (g == 0) xch[p][h][n] = f32x4{l_w, m_own, amax, 0.f};
+  ring_barrier();
+  const f32x4 x0 = xch[p][0][n], x1 = xch[p][1][n];
+  const float m_run = m_acc;
+  // the exact sums of both waves' weights, each on its own reference, moved to m_acc
+  float l_tot = x0[0] * fast_exp2(fmaxf(x0[1] - m_run, -200.f)) + x1[0] * fast_exp2(fmaxf(x1[1] - m_run, -200.f));
+  if (!head_ok) return;
+  if (a.nsplit == 1) {
+    // fold in the sink: Z = l 2^(m - M) + 2^(sink - M), M = max(m, sink)
+    const float sink2 = a.sink[head] * kLog2e;
+    const float M = fmaxf(m_run, sink2);
+    const float sc = exp2f(m_run - M);
+    const float es = exp2f(sink2 - M);
+    l_tot = l_tot * sc + es;
+    const float inv = sc / (n_tot * sc + es);
+    const int rot0 = kD - a.rope_dim;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = acc[db][i] * inv;
+      const int d0 = 256 * h + 16 * db + 4 * g;
+      if (d0 + 4 > rot0 && a.rope_dim > 0) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int d = d0 + 2 * k2;
+          if (d >= rot0) {
+            // rotation by -q_pos: same cosine, negated sine
+            const f32x2 t2 = rtab[(d - rot0) >> 1];
+            const float cs = t2[0], sn = -t2[1];
+            const float y0 = o[2 * k2], y1 = o[2 * k2 + 1];
+            o[2 * k2] = y0 * cs - y1 * sn;
+            o[2 * k2 + 1] = y0 * sn + y1 * cs;
+          }
+        }
+      }
+      const int64_t off = ((int64_t)row * a.H + head) * kD + d0;
+      if (a.out_dtype == CSA_FP32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + off) = f32x4{o[0], o[1], o[2], o[3]};
+      } else {
+        u32x2 w2;
+        w2[0] = pack_bf16x2(o[0], o[1]);
+        w2[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) = w2;
+      }
+    }
+    if (a.lse && g == 0 && h == 0) a.lse[(int64_t)row * a.H + head] = (M + log2f(l_tot)) * kLn2;
+  } else {
+    // The split's normalised output o / n in fp16 (11-bit significand: rounding within 2^-11
+    // relative, far below the error the bf16 inputs carry), scaled by 2^-e so that the head's
+    // largest magnitude sits below 2^14 whatever the range of the cache values; (m, n, l, e)
+    // stay fp32.  Half the bytes of fp32 partials, written here and read by the merge.
+    const float am = fmaxf(x0[2], x1[2]);
+    const float inv_n = n_tot > 0.f ? 1.f / n_tot : 0.f;
+    int e = 0;
+    if (am * inv_n > 0.f) {
+      int ex;
+      (void)frexpf(am * inv_n, &ex);   // amax / n = f 2^ex, f in [0.5, 1)
+      e = ex - 14;
+    }
+    const float sc = ldexpf(inv_n, -e);
+    const int64_t pr = ((int64_t)row * a.nsplit + split) * a.H + head;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) {
+      u32x2 hh;
+      hh[0] = pack_f16x2(acc[db][0] * sc, acc[db][1] * sc);
+      hh[1] = pack_f16x2(acc[db][2] * sc, acc[db][3] * sc);
+      *reinterpret_cast<u32x2*>(a.part_o + pr * kD + 256 * h + 16 * db + 4 * g) = hh;
+    }
+    if (g == 0 && h == 0) *reinterpret_cast<f32x4*>(a.part_ml + 4 * pr) = f32x4{m_run, n_tot, l_tot, (float)e};
+  }
+}
+
 // Merge split partials: M = max(sink, m_s), o = sum 2^(m_s - M) n_s u_s / Zo with u_s = o_s / n_s
 // (stored in fp16 times 2^-e_s) and Zo = 2^(sink - M) + sum n_s 2^(m_s - M) (n_s: the sum of the
-// weights as rounded for the split's PV product), lse = M + log2(2^(sink - M) + sum l_s
+// weights as they entered the split's P V product), lse = M + log2(2^(sink - M) + sum l_s
 // 2^(m_s - M)) with the exact sums l_s; then rotate back and store.  A block of 256 lanes merges 4
 // (row, head) pairs, 8 channels per lane; splits are merged online, four per round, so that a
 // round's (max, sum) and output loads are all in flight together.
@@ -648,9 +1184,9 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
       const float wo = ldexpf(ns[u] * w, (int)es[u]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x2 h = unpack_f16x2(v[u][k]);
-        o[2 * k] += wo * h[0];
-        o[2 * k + 1] += wo * h[1];
+        const f32x2 hh = unpack_f16x2(v[u][k]);
+        o[2 * k] += wo * hh[0];
+        o[2 * k + 1] += wo * hh[1];
       }
     }
     M = Mn;
@@ -686,85 +1222,46 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
   if (a.lse && d0 == 0) a.lse[rh] = (M + log2f(Z)) * kLn2;
 }
 
-// Splits of the row set for a block shape: enough that the grid has about kTargetBlocks
-// blocks, at most one per two tiles, with the per-split count rounded up to whole tiles.
-static int nsplit_for(int hpb, int rows, int H, int slot_cap) {
-  const int tile = hpb == 64 ? AttCfg<64>::T : AttCfg<32>::T;
-  const int HG = (H + hpb - 1) / hpb;
-  const long long base = (long long)rows * HG;
-  int ns = (int)((kTargetBlocks + base - 1) / base);
-  const int max_ns = (slot_cap + 2 * tile - 1) / (2 * tile);   // at least two tiles per split
-  if (ns > max_ns) ns = max_ns;
-  if (ns < 1) ns = 1;
-  int sps = (slot_cap + ns - 1) / ns;
-  sps = (sps + tile - 1) / tile * tile;
-  if (sps < tile) sps = tile;
-  return (slot_cap + sps - 1) / sps;
-}
-
-#ifndef CSA_ATT_HPB
-#define CSA_ATT_HPB 0   // 0: chosen per call; 32 or 64: that shape always
-#endif
-
-// Block shape and splits of a call: 64 heads per block whenever that grid reaches about
-// kTargetBlocks blocks (it does the fewest MFMAs per row: 32-row tiles); 32 heads per block
-// when it cannot (few query rows over short row sets, as in 1M-token decode with top-k),
-// where twice the blocks beat the cost of 16-row tiles.
-AttendPlan attend_plan(int rows, int H, int slot_cap) {
-  AttendPlan pl;
-  int hpb = CSA_ATT_HPB;
-  if (hpb == 0) {
-    const long long blocks64 = (long long)rows * ((H + 63) / 64) * nsplit_for(64, rows, H, slot_cap);
-    hpb = blocks64 < kTargetBlocks ? 32 : 64;
-  }
-  pl.hpb = hpb;
-  pl.nsplit = nsplit_for(hpb, rows, H, slot_cap);
-  const int tile = hpb == 64 ? AttCfg<64>::T : AttCfg<32>::T;
-  int sps = (slot_cap + pl.nsplit - 1) / pl.nsplit;
-  sps = (sps + tile - 1) / tile * tile;
-  pl.sps = sps < tile ? tile : sps;
-  return pl;
-}
-
-size_t attend_workspace(int rows, int H, int slot_cap, bool csa) {
-  (void)csa;
-  const int ns = attend_plan(rows, H, slot_cap).nsplit;
-  if (ns <= 1) return 0;
-  // fp16 partial outputs, then fp32 (m, n, l, e): the latter start 16-byte aligned (kD even)
-  return (size_t)rows * ns * H * (kD * sizeof(uint16_t) + 4 * sizeof(float)) + 256;
-}
-
-template <int HPB>
-static void launch_attend_shape(const AttendArgs& a, dim3 grid, hipStream_t s) {
-  const dim3 blk(kAttThreads);
+template <int NP>
+static void launch_attend_pairs(const AttendArgs& a, dim3 grid, hipStream_t s) {
+  const dim3 blk(AttShape<NP>::NT);
   const bool csa = a.csa_mode != 0;
   switch (a.kv_dtype) {
     case CSA_FP8_E4M3:
-      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP8_E4M3, HPB>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_attend<false, CSA_FP8_E4M3, HPB>), grid, blk, 0, s, a);
+      if constexpr (NP == 2) {   // fp8 caches take the 32-head shape only
+        if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP8_E4M3, 2>), grid, blk, 0, s, a);
+        else hipLaunchKernelGGL((k_attend<false, CSA_FP8_E4M3, 2>), grid, blk, 0, s, a);
+      }
       break;
-    case CSA_FP4_E2M1:
-      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP4_E2M1, HPB>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_attend<false, CSA_FP4_E2M1, HPB>), grid, blk, 0, s, a);
-      break;
-    default:
-      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_BF16, HPB>), grid, blk, 0, s, a);
-      else hipLaunchKernelGGL((k_attend<false, CSA_BF16, HPB>), grid, blk, 0, s, a);
+    default:   // fp4 (bf16 caches take the grouped kernel)
+      if (csa) hipLaunchKernelGGL((k_attend<true, CSA_FP4_E2M1, NP>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((k_attend<false, CSA_FP4_E2M1, NP>), grid, blk, 0, s, a);
       break;
   }
+}
+
+template <int HPB>
+static void launch_attend_groups(const AttendArgs& a, dim3 grid, hipStream_t s) {
+  if (a.csa_mode != 0) hipLaunchKernelGGL((k_attend_grp<true, HPB>), grid, dim3(kAttThreads), 0, s, a);
+  else hipLaunchKernelGGL((k_attend_grp<false, HPB>), grid, dim3(kAttThreads), 0, s, a);
 }
 
 hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   AttendArgs a = a0;
   const int rows = a.B * a.Tq;
-  const AttendPlan pl = attend_plan(rows, a.H, a.slot_cap);
+  const AttendPlan pl = attend_plan(rows, a.H, a.slot_cap, a.csa_mode != 0, att_kind(a.kv_dtype));
   a.nsplit = pl.nsplit;
   a.slots_per_split = pl.sps;
   const int HG = (a.H + pl.hpb - 1) / pl.hpb;
   const long long blocks = (long long)rows * HG * a.nsplit;
   const dim3 grid((unsigned)blocks);
-  if (pl.hpb == 64) launch_attend_shape<64>(a, grid, s);
-  else launch_attend_shape<32>(a, grid, s);
+  if (pl.kind == kAttGroups) {
+    if (pl.hpb == 64) launch_attend_groups<64>(a, grid, s);
+    else launch_attend_groups<32>(a, grid, s);
+  } else {
+    if (pl.hpb == 64) launch_attend_pairs<4>(a, grid, s);
+    else launch_attend_pairs<2>(a, grid, s);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nsplit > 1) {

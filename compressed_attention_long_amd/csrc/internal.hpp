@@ -82,13 +82,8 @@ struct AttendArgs {
   uint16_t* part_o;       // [rows, nsplit, H, 512] fp16: o / n times 2^-e
   float* part_ml;         // [rows, nsplit, H, 4]: reference max, normaliser n, exact sum, e
 };
-struct AttendPlan {
-  int hpb;      // heads per block (64 or 32)
-  int nsplit;   // splits of each query row's row set
-  int sps;      // rows per split (whole tiles)
-};
-AttendPlan attend_plan(int rows, int H, int slot_cap);
-size_t attend_workspace(int rows, int H, int slot_cap, bool csa);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// the plan's name for a cache storage code
+inline int att_kind(int dtype) { return dtype == CSA_FP8_E4M3 ? kAttFp8 : (dtype == CSA_FP4_E2M1 ? kAttFp4 : kAttBf16); }
 
 }  // namespace csa

@@ -1,6 +1,7 @@
-// Workspace plans of the top-k selection: which stages run and where their candidate lists sit
-// in the caller's workspace.  Plain host C++ (no HIP), shared by the C ABI (sizes and checks),
-// the launcher (pointers) and a host test that checks every carving against the size it fits in.
+// Launch plans and workspace carving of the top-k selection and of attention: which stages or
+// splits run and where their intermediate results sit in the caller's workspace.  Plain host C++
+// (no HIP), shared by the C ABI (sizes and checks), the launchers (pointers) and a host test that
+// checks every carving against the size it fits in.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -72,6 +73,99 @@ inline size_t topk_workspace(int rows, int cap, int k) {
   const TopkPlan pl = topk_plan(rows, cap, k);
   if (pl.mode != 1) return 0;
   return align256(topk_carve(rows, pl, k).end);
+}
+
+// ---------------------------------------------------------------- attention
+
+// Two kernels: the grouped kernel for bf16 caches (tile groups of 16-head waves holding all 512
+// output channels, 64 rows per step, 32- or 16-row tiles) and the wave-pair kernel for quantized
+// caches (pairs of waves sharing 16 heads, 32-row tiles through a four-buffer ring, fp8 scales
+// applied in fp32).
+constexpr int kAttGroups = 0, kAttPairs = 1;
+constexpr int kAttGroupTile64 = 32;    // grouped kernel: rows per tile with 64 heads per block
+constexpr int kAttTile = 32;           // wave-pair kernel: rows per tile
+constexpr int kAttIdxMax = 1280;       // top-k indices of one split held in LDS (a multiple of 64)
+constexpr int kAttTargetBlocks = 256;  // split until the grid has about this many blocks
+
+// Storage kinds of the compressed KV cache, as the plan sees them.
+constexpr int kAttBf16 = 0, kAttFp8 = 1, kAttFp4 = 2;
+
+struct AttendPlan {
+  int kind;     // kAttGroups or kAttPairs
+  int hpb;      // heads per block (64 or 32)
+  int nsplit;   // splits of each query row's row set
+  int sps;      // rows per split (whole tiles)
+};
+
+// Splits for a block shape with `tile`-row tiles: enough that the grid has about kAttTargetBlocks
+// blocks, at least two tiles per split, at most `idx_max` slots per split (0: no limit); the
+// per-split count is rounded up to whole tiles.  slot_cap = the longest row set (top-k or visible
+// entries, plus the window).
+inline AttendPlan attend_plan_for(int kind, int hpb, int tile, int idx_max, int rows, int H, int slot_cap) {
+  AttendPlan pl{};
+  pl.kind = kind;
+  pl.hpb = hpb;
+  const long long HG = (H + hpb - 1) / hpb;
+  const long long base = (long long)rows * HG;
+  long long ns = (kAttTargetBlocks + base - 1) / base;
+  const long long max_ns = ((long long)slot_cap + 2 * tile - 1) / (2 * tile);
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  if (idx_max > 0) {
+    const long long min_ns = ((long long)slot_cap + idx_max - 1) / idx_max;
+    if (ns < min_ns) ns = min_ns;
+  }
+  long long sps = ((long long)slot_cap + ns - 1) / ns;
+  sps = (sps + tile - 1) / tile * tile;
+  if (sps < tile) sps = tile;
+  pl.sps = (int)sps;
+  const long long n = ((long long)slot_cap + sps - 1) / sps;
+  pl.nsplit = (int)(n < 1 ? 1 : n);
+  return pl;
+}
+
+// The call's plan.  Either kernel takes 64 heads per block when that grid reaches about
+// kAttTargetBlocks blocks (each staged row then serves the most heads), else 32 (few query rows
+// over short row sets, as in 1M-token decode with top-k), where twice the blocks shorten the
+// critical path.  fp8 caches always take 32 heads per block (their per-block scaling needs the
+// registers of the larger shape's second pair).
+inline AttendPlan attend_plan(int rows, int H, int slot_cap, bool csa, int kv_kind) {
+  if (kv_kind == kAttBf16) {
+    const AttendPlan p64 = attend_plan_for(kAttGroups, 64, kAttGroupTile64, 0, rows, H, slot_cap);
+    const long long blocks64 = (long long)rows * ((H + 63) / 64) * p64.nsplit;
+    return blocks64 < kAttTargetBlocks ? attend_plan_for(kAttGroups, 32, kAttGroupTile64 / 2, 0, rows, H, slot_cap)
+                                       : p64;
+  }
+  const int idx_max = csa ? kAttIdxMax : 0;
+  const AttendPlan p64 = attend_plan_for(kAttPairs, 64, kAttTile, idx_max, rows, H, slot_cap);
+  const long long blocks64 = (long long)rows * ((H + 63) / 64) * p64.nsplit;
+  return (kv_kind == kAttFp8 || blocks64 < kAttTargetBlocks)
+             ? attend_plan_for(kAttPairs, 32, kAttTile, idx_max, rows, H, slot_cap)
+             : p64;
+}
+
+// Split partials in the workspace: fp16 outputs [rows, nsplit, H, 512] from byte 0, then fp32
+// (max, normaliser, sum, exponent) [rows, nsplit, H, 4]; nothing when there is one split.
+struct AttendCarve {
+  size_t part_o, part_ml, end;
+};
+inline AttendCarve attend_carve(int rows, int H, const AttendPlan& pl) {
+  AttendCarve c{};
+  if (pl.nsplit <= 1) return c;
+  const size_t units = (size_t)rows * pl.nsplit * H;
+  c.part_o = 0;
+  c.part_ml = units * 512 * sizeof(uint16_t);
+  c.end = c.part_ml + units * 4 * sizeof(float);
+  return c;
+}
+// Bytes for any cache format (the size query does not take the format): the largest of the plans.
+inline size_t attend_workspace(int rows, int H, int slot_cap, bool csa) {
+  size_t end = 0;
+  for (int kind = kAttBf16; kind <= kAttFp4; ++kind) {
+    const AttendCarve c = attend_carve(rows, H, attend_plan(rows, H, slot_cap, csa, kind));
+    if (c.end > end) end = c.end;
+  }
+  return end == 0 ? 0 : align256(end);
 }
 
 }  // namespace csa

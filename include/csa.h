@@ -237,7 +237,9 @@ int csa_index_topk_compress(const csa_compress_call_t* calls, int n_calls,
  *     out = rope(sum_x exp(l_x) / Z * x, -p),   lse = log Z
  *
  *   q          device bf16 [B, Tq, H, 512], un-rotated
- *   kv         compressed KV cache (C == 512): bf16, or fp8 with scale_block 64
+ *   kv         compressed KV cache (C == 512): bf16, fp8 with scale_block a multiple of 64
+ *              (the codes enter both products exactly; the block scales are applied in fp32),
+ *              or fp4 (scale_block 32)
  *   idx        device int32 [B, Tq, topk] (-1 = unused slot), e.g. from csa_index_topk
  *   win        raw-window cache (window = stride = 1, C == 512, bf16, rotated rows)
  *   W          window length in raw tokens (>= 0)
@@ -245,7 +247,7 @@ int csa_index_topk_compress(const csa_compress_call_t* calls, int n_calls,
  *   out        device [B, Tq, H, 512], out_dtype CSA_FP32 or CSA_BF16
  *   lse_out    device fp32 [B, Tq, H] or NULL
  *   workspace  at least csa_attend_workspace_bytes(...) bytes, 256-byte aligned
- * Requires H % 16 == 0 or H < 16, H <= 128, 0 <= topk <= kv->cap, 16-byte aligned q/out/kv rows.
+ * Requires 1 <= H <= 1024, 0 <= topk <= kv->cap, 16-byte aligned q/out/kv rows.
  */
 int csa_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H,
                const csa_cache_t* kv, const int32_t* idx, int topk,

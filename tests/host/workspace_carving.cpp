@@ -1,7 +1,9 @@
-// Host check of the top-k workspace carving (compressed_attention_long_amd/csrc/workspace.hpp):
-// for every plan in a sweep of (rows, cap, k), every area a kernel writes lies inside the
+// Host check of the workspace carving (compressed_attention_long_amd/csrc/workspace.hpp): for
+// every top-k plan in a sweep of (rows, cap, k), every area a kernel writes lies inside the
 // candidate bytes the C ABI asks for, the areas do not overlap, each starts 256-byte aligned,
-// and every merge stage's output fits the area it is written to.  Prints one line per failure
+// and every merge stage's output fits the area it is written to; for every attention plan in a
+// sweep of (rows, heads, row-set length), the splits cover the row set, fit the LDS index list,
+// and their partials fit the workspace.  Prints one line per failure
 // and "checked N plans" at the end; exit status 1 on any failure.
 #include <cstdio>
 #include "workspace.hpp"
@@ -76,6 +78,42 @@ int main() {
         CHECK((long long)chunks * k <= kTopkMergeCands, "rows %d cap %d k %d: final merge of %d chunks", rows, cap,
               k, chunks);
       }
+  // attention: every split's rows lie inside the row set's slots, (CSA) a split's top-k slots fit
+  // the LDS index list, and the partials fit the workspace
+  const int arows[] = {1, 2, 4, 6, 8, 16, 32, 64, 128, 256, 4096, 16384};
+  const int aheads[] = {1, 8, 16, 24, 64, 100, 128};
+  const int aslots[] = {0, 1, 31, 32, 33, 129, 300, 640, 1152, 1280, 1281, 2000, 4224, 8320, 33000, 262271};
+  for (int rows : arows)
+    for (int H : aheads)
+      for (int slots : aslots)
+        for (int csa = 0; csa < 2; ++csa)
+          for (int kind = kAttBf16; kind <= kAttFp4; ++kind) {
+          ++n;
+          const AttendPlan pl = attend_plan(rows, H, slots, csa != 0, kind);
+          CHECK(kind != kAttFp8 || pl.hpb == 32, "rows %d H %d slots %d: fp8 plan with %d heads per block", rows, H,
+                slots, pl.hpb);
+          CHECK((kind == kAttBf16) == (pl.kind == kAttGroups), "rows %d H %d slots %d: kernel kind", rows, H, slots);
+          const int tile = pl.kind == kAttGroups ? (pl.hpb == 64 ? kAttGroupTile64 : kAttGroupTile64 / 2) : kAttTile;
+          CHECK(pl.hpb == 32 || pl.hpb == 64, "rows %d H %d slots %d: %d heads per block", rows, H, slots, pl.hpb);
+          CHECK(pl.nsplit >= 1 && pl.sps >= tile && pl.sps % tile == 0,
+                "rows %d H %d slots %d: %d splits of %d", rows, H, slots, pl.nsplit, pl.sps);
+          CHECK((long long)pl.nsplit * pl.sps >= slots, "rows %d H %d slots %d: splits do not cover the rows", rows,
+                H, slots);
+          CHECK(slots == 0 || (long long)(pl.nsplit - 1) * pl.sps < slots, "rows %d H %d slots %d: an empty split",
+                rows, H, slots);
+          if (csa && pl.kind == kAttPairs)
+            CHECK(pl.sps <= kAttIdxMax, "rows %d H %d slots %d: %d slots per split", rows, H, slots, pl.sps);
+          const size_t ws = attend_workspace(rows, H, slots, csa != 0);
+          const AttendCarve c = attend_carve(rows, H, pl);
+          const size_t units = (size_t)rows * pl.nsplit * H;
+          if (pl.nsplit == 1) {
+            CHECK(c.end == 0, "rows %d H %d slots %d: one split carves %zu bytes", rows, H, slots, c.end);
+          } else {
+            CHECK(c.part_ml >= c.part_o + units * 512 * 2, "rows %d H %d slots %d: partials overlap", rows, H, slots);
+            CHECK(c.part_ml % 16 == 0, "rows %d H %d slots %d: (m, n, l, e) not 16-byte aligned", rows, H, slots);
+            CHECK(c.part_ml + units * 16 <= ws, "rows %d H %d slots %d: partials end past %zu", rows, H, slots, ws);
+          }
+        }
   std::printf("checked %ld plans, %d failures\n", n, failures);
   return failures ? 1 : 0;
 }

@@ -169,6 +169,11 @@ def test_attend_validation():
     assert attend(fp4, win, B=0)[0] == L.CSA_OK                   # fp4 entries are accepted
     assert attend(cache(cap=2048, dtype=L.CSA_FP4_E2M1, sb=32, scales=False), win)[0] == L.CSA_EINVAL
     assert attend(kv, cache(cap=160, window=1, stride=1, dtype=L.CSA_FP4_E2M1, sb=32))[0] == L.CSA_ENOTSUP
+    # fp8 entries: scales per 64 channels (or a multiple); finer blocks are not supported
+    rc, msg = attend(cache(cap=2048, dtype=L.CSA_FP8_E4M3, sb=32), win, ws=FAKE, wsb=1 << 40)
+    assert rc == L.CSA_ENOTSUP and "scale_block" in msg
+    assert attend(cache(cap=2048, dtype=L.CSA_FP8_E4M3, sb=64), win, ws=FAKE, wsb=1 << 40)[0] not in (
+        L.CSA_ENOTSUP, L.CSA_EINVAL, L.CSA_EWORKSPACE)
 
 
 def test_workspace_sizes_scale_with_work():

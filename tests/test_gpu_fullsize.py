@@ -127,6 +127,16 @@ def test_v4flash_csa_decode_1m_fp8():
     check_rows(wl, t, meta, step, every_row(wl))
 
 
+def test_v4flash_csa_decode_1m_fp8_peaked_queries():
+    """The Flash fp8 decode with queries scaled by 4 (a sharper softmax over the fp8 cache; the
+    scaling is exact in bf16): attention over the same selection and stored bytes."""
+    wl, t, meta, step = run_step("v4flash_csa_decode_1m_fp8")
+    t["q"].mul_(4.0)
+    step.attend()
+    torch.cuda.synchronize()
+    check_rows(wl, t, meta, step, every_row(wl))
+
+
 def test_v4pro_csa_prefill_4k_on_131k():
     wl, t, meta, step = run_step("v4pro_csa_prefill_4k_on_131k")
     check_new_entry(wl, t, meta, step, 0)

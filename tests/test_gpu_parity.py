@@ -344,9 +344,12 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     ("csa", 4, 64, 64, 600, [600] * 4, False, 200, 128, 200, 0.1, 2.0),               # 256 rows: no split
     ("csa", 4, 1, 64, 6000, [6000, 5000, 512, 100], True, 512, 128, 129, 1 / math.sqrt(512), 4.0),  # CSA2: top-512, fp8
     ("hca", 2, 1, 128, 700, [700, 300], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),
-    # fp8 rows are staged in LDS as bf16 (code x scale rounded): sharper softmax than this
-    # exceeds the bar (CPU emulation of that rounding: 1.1% at scale 1, 5.8% at scale 1 with q x 4)
     ("hca", 1, 2, 128, 64, [64], True, 0, 128, 129, 1 / math.sqrt(512), 4.0),        # fp8, sharper q
+    # fp8 rows at a peaked softmax (scale 1, q x 8): the kernel stages the exact codes and applies
+    # the per-64-channel scales in fp32, so no rounding of code x scale enters the logits
+    ("csa", 2, 1, 64, 3000, [3000, 2000], True, 1024, 128, 129, 1.0, 8.0),
+    ("hca", 2, 1, 128, 700, [700, 300], True, 0, 128, 129, 1.0, 8.0),
+    ("csa", 3, 2, 128, 2500, [2500, 2400, 60], True, 1024, 128, 129, 1.0, 4.0),     # fp8, 128 heads, < k visible
     ("hca", 3, 1, 24, 300, [300, 299, 1], False, 0, 0, 1, 1 / math.sqrt(512), 1.0),   # no window, H < 32
     ("csa", 4, 1, 64, 6000, [6000, 5000, 512, 100], "fp4", 512, 128, 129, 1 / math.sqrt(512), 4.0),  # CSA2, fp4
     ("csa", 2, 3, 64, 900, [900, 40], "fp4", 300, 128, 140, 1 / math.sqrt(512), 1.0),  # fp4, < k visible

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(os.path.dirname(HERE), "compressed_attention_long_amd", "csrc")
 
 
-def test_topk_workspace_carving_fits(tmp_path):
+def test_workspace_carving_fits(tmp_path):
     cxx = shutil.which("g++") or shutil.which("c++")
     if cxx is None:
         pytest.skip("no host C++ compiler")
