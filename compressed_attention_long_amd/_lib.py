@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libcsa.so")
 
 CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EWORKSPACE, CSA_EHIP = 0, -1, -2, -3, -4
 CSA_BF16, CSA_FP8_E4M3, CSA_FP32, CSA_FP4_E2M1 = 0, 1, 2, 3
+CSA_NOALLOC_SCRATCH_BYTES = 32 << 20   # include/csa.h
 
 # Entry points declared in include/csa.h, in declaration order.
 EXPORTS = (
@@ -28,6 +29,7 @@ EXPORTS = (
     "csa_index_topk_compress",
     "csa_attend",
     "csa_attend_workspace_bytes",
+    "csa_attend_noalloc",
     "hca_attend",
     "hca_attend_workspace_bytes",
     "csa_last_error",
@@ -87,6 +89,8 @@ _SIGS = {
     "csa_attend": (_i32, [_vp, _vp, _i32, _i32, _i32, _PC, _vp, _i32, _PC, _i32, _vp, _vp, _i32, _f32,
                           _vp, _i32, _vp, _vp, _sz, _vp]),
     "csa_attend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "csa_attend_noalloc": (_i32, [_vp, _vp, _i32, _i32, _i32, _PC, _vp, _i32, _PC, _i32, _vp, _vp, _i32, _f32,
+                                  _vp, _i32, _vp, _vp]),
     "hca_attend": (_i32, [_vp, _vp, _i32, _i32, _i32, _PC, _PC, _i32, _vp, _vp, _i32, _f32,
                           _vp, _i32, _vp, _vp, _sz, _vp]),
     "hca_attend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -285,6 +289,20 @@ def csa_attend(q: torch.Tensor, q_pos: torch.Tensor, kv: Cache, idx: torch.Tenso
                            softmax_scale, out.data_ptr(), _out_code(out), _ptr(lse), _ptr(workspace), ws_bytes,
                            _stream(stream))
     _check("csa_attend", rc)
+
+
+def csa_attend_noalloc(q: torch.Tensor, q_pos: torch.Tensor, kv: Cache, idx: torch.Tensor, win: Cache, W: int,
+                       sink: torch.Tensor, inv_freq: Optional[torch.Tensor], rope_dim: int, softmax_scale: float,
+                       out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """csa_attend_noalloc: csa_attend with the library's own scratch instead of a workspace."""
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and out.is_contiguous()
+    assert idx.dtype == torch.int32 and idx.is_contiguous()
+    B, Tq, H, _ = q.shape
+    ck, cw = kv.struct(), win.struct()
+    rc = load().csa_attend_noalloc(q.data_ptr(), q_pos.data_ptr(), B, Tq, H, ctypes.byref(ck), idx.data_ptr(),
+                                   idx.shape[-1], ctypes.byref(cw), W, sink.data_ptr(), _ptr(inv_freq), rope_dim,
+                                   softmax_scale, out.data_ptr(), _out_code(out), _ptr(lse), _stream(stream))
+    _check("csa_attend_noalloc", rc)
 
 
 def hca_attend(q: torch.Tensor, q_pos: torch.Tensor, kv: Cache, win: Cache, W: int, sink: torch.Tensor,

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -425,6 +426,53 @@ int csa_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H, const 
                float* lse_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return attend_common(q, q_pos, B, Tq, H, kv, idx, topk, true, win, W, sink, inv_freq, rope_dim, softmax_scale,
                        out, out_dtype, lse_out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- csa_attend without a workspace
+//
+// The split partials of csa_attend_noalloc live in this array: one copy per GPU the library runs
+// on, kept until the process ends.  Host code never uses its name as an address (on the host it
+// is only a stand-in): each device's address is looked up once, with that device current, and
+// kept in g_scratch.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+extern "C" {
+
+int csa_attend_noalloc(const void* q, const int64_t* q_pos, int B, int Tq, int H, const csa_cache_t* kv,
+                       const int32_t* idx, int topk, const csa_cache_t* win, int W, const float* sink,
+                       const double* inv_freq, int rope_dim, float softmax_scale, void* out, int out_dtype,
+                       float* lse_out, hipStream_t stream) {
+  // the scratch this call needs, from its sizes alone (bad sizes are reported by attend_common)
+  size_t need = 0;
+  if (B > 0 && Tq > 0 && H >= 1 && H <= 1024 && topk >= 0 && W >= 0 && (int64_t)B * Tq <= 0x7fffffff)
+    need = csa::attend_workspace(B * Tq, H, topk + W, true);
+  REQUIRE(need <= CSA_NOALLOC_SCRATCH_BYTES, CSA_EWORKSPACE,
+          "this call needs %zu bytes of scratch; the no-allocation entry point holds %u (use csa_attend with a "
+          "workspace)", need, (unsigned)CSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    REQUIRE(e == hipSuccess, CSA_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    REQUIRE(dev >= 0 && dev < kMaxDevices, CSA_ENOTSUP, "device %d: at most %d devices", dev, kMaxDevices);
+    std::call_once(g_scratch_once[dev], [dev] {
+      g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch[dev], HIP_SYMBOL(scratch));
+    });
+    REQUIRE(g_scratch_err[dev] == hipSuccess && g_scratch[dev] != nullptr, CSA_EHIP,
+            "locating the scratch array on device %d failed: %s", dev, hipGetErrorString(g_scratch_err[dev]));
+    ws = g_scratch[dev];
+  }
+  return attend_common(q, q_pos, B, Tq, H, kv, idx, topk, true, win, W, sink, inv_freq, rope_dim, softmax_scale,
+                       out, out_dtype, lse_out, ws, ws ? (size_t)CSA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int hca_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H, const csa_cache_t* kv,

@@ -259,6 +259,29 @@ int csa_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H,
 size_t csa_attend_workspace_bytes(int B, int Tq, int H, int topk, int W);
 
 /*
+ * csa_attend_noalloc — csa_attend for callers that cannot allocate a workspace.
+ *
+ * For code that must not allocate device memory: work captured into a HIP graph, tight serving
+ * loops, harnesses that forbid it.  Same arguments and result as csa_attend, without the
+ * workspace: the split partials live in a scratch array inside the library, one per GPU, of
+ * CSA_NOALLOC_SCRATCH_BYTES bytes, held from the first call on that GPU (with that GPU current)
+ * until the process ends.  Nothing is allocated or freed by the call.
+ *   - CSA_EWORKSPACE when the call needs more scratch than that (csa_attend_workspace_bytes of
+ *     the same arguments is larger), checked on the host before anything is launched;
+ *   - every call on one GPU shares that GPU's array, which keeps the last call's contents:
+ *     calls that overlap on one GPU (other streams, or graph replays in flight together) race
+ *     and must be serialised by the caller;
+ *   - the array is located on the current device: the stream must belong to it.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int csa_attend_noalloc(const void* q, const int64_t* q_pos, int B, int Tq, int H,
+                       const csa_cache_t* kv, const int32_t* idx, int topk,
+                       const csa_cache_t* win, int W, const float* sink,
+                       const double* inv_freq, int rope_dim, float softmax_scale,
+                       void* out, int out_dtype, float* lse_out, hipStream_t stream);
+
+/*
  * hca_attend — as csa_attend, with U = every kv row visible to the query
  * (j < n_valid[b] and position <= p) plus the window rows.
  *

@@ -176,6 +176,18 @@ def test_attend_validation():
         L.CSA_ENOTSUP, L.CSA_EINVAL, L.CSA_EWORKSPACE)
 
 
+def test_attend_noalloc_rejects_calls_beyond_its_scratch():
+    # an fp4 cache with a 20,000-entry selection over 64 query rows needs far more than the
+    # library's scratch: refused on the host, before anything touches a GPU
+    lib = L.load()
+    kv = cache(cap=30000, dtype=L.CSA_FP4_E2M1, sb=32)
+    win = cache(cap=160, window=1, stride=1)
+    assert L.csa_attend_workspace_bytes(64, 1, 128, 20000, 128) > L.CSA_NOALLOC_SCRATCH_BYTES
+    rc = lib.csa_attend_noalloc(FAKE, FAKE, 64, 1, 128, ctypes.byref(kv), FAKE, 20000, ctypes.byref(win), 128,
+                                FAKE, FAKE, 64, 0.04, FAKE, L.CSA_FP32, None, None)
+    assert rc == L.CSA_EWORKSPACE and "scratch" in L.last_error()
+
+
 def test_workspace_sizes_scale_with_work():
     assert L.csa_attend_workspace_bytes(4096, 1, 128, 1024, 128) == 0   # enough rows: no split partials
     a = L.hca_attend_workspace_bytes(16, 1, 128, 8192, 128)
