@@ -55,20 +55,21 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 
 // ---------------------------------------------------------------- scores
 
-constexpr int kIdxTilesPerWave = 32;     // 16 entries per tile
-constexpr int kIdxWaves = 4;
+constexpr int kIdxBlockTiles = 128;      // tiles of 16 entries per block (2,048 entries)
+constexpr int kIdxWaves = 4;             // waves per block of the fused scores + compress launch
 // Score-tile loads in flight per wave (the register ring's depth): 8 when the scores grid has
 // at most kDeepRingBlocks blocks (about one per CU, so each wave must keep more loads in flight:
 // 65K decode fused call 32.8 -> 32.1 us), else 4 (grids of 512 and more, as at 1M, lose with 8).
 constexpr int kDeepRingBlocks = 256;
-constexpr int kIdxEntPerBlock = kIdxWaves * kIdxTilesPerWave * 16;
+constexpr int kIdxEntPerBlock = kIdxBlockTiles * 16;
 
 // One block of the decode scores grid: query row `row` (b * Tq + t), entries from
 // chunk * kIdxEntPerBlock.
-template <int HB, bool FP8, int DEPTH>
+template <int HB, bool FP8, int DEPTH, int NW>
 __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, int chunk) {
+  constexpr int kIdxTilesPerWave = kIdxBlockTiles / NW;
   static_assert(kIdxTilesPerWave % DEPTH == 0, "whole ring rounds stay inside a wave's tiles");
-  __shared__ float sbuf[kIdxWaves][kIdxTilesPerWave * 16];
+  __shared__ float sbuf[NW][kIdxTilesPerWave * 16];
   const int b = row / a.Tq;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
@@ -148,7 +149,12 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
     // staged in LDS: global stores inside the loop would count against vmcnt and stall the ring
     if (g == 0) sbuf[wave][16 * t + n] = sc;
   };
-  for (int t0 = 0; t0 < ntile; t0 += DEPTH) {
+  // The tile loop always runs its full compile-time count (tiles past ntile recompute the last
+  // tile), fully unrolled: with a back edge the compiler waits for every load in flight at the
+  // loop header, which drains the ring once per round.
+  if (ntile > 0) {
+#pragma unroll
+  for (int t0 = 0; t0 < kIdxTilesPerWave; t0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int t = t0 + d;
@@ -187,7 +193,8 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
       tprev = t;
     }
   }
-  if (ntile > 0) finish(prev, prev_scale, tprev);
+  finish(prev, prev_scale, tprev);
+  }
   // write this wave's scores, coalesced; entries past the visible count score -inf
 #pragma unroll
   for (int i = lane; i < kIdxTilesPerWave * 16; i += 64) {
@@ -196,9 +203,9 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
   }
 }
 
-template <int HB, bool FP8, int DEPTH>
-__global__ void __launch_bounds__(256) k_index_scores(IndexArgs a) {
-  index_scores_block<HB, FP8, DEPTH>(a, blockIdx.x, blockIdx.y);
+template <int HB, bool FP8, int DEPTH, int NW>
+__global__ void __launch_bounds__(64 * NW) k_index_scores(IndexArgs a) {
+  index_scores_block<HB, FP8, DEPTH, NW>(a, blockIdx.x, blockIdx.y);
 }
 
 // The same grid with a decode step's compress blocks after it (csa_index_topk_compress): the
@@ -209,7 +216,7 @@ template <int HB, bool FP8, int DEPTH>
 __global__ void __launch_bounds__(256) k_index_scores_compress(IndexArgs a, CompressBatch cb, int n_idx) {
   const int L = blockIdx.x;
   const int rows = a.B * a.Tq;
-  if (L < n_idx) index_scores_block<HB, FP8, DEPTH>(a, L % rows, L / rows);
+  if (L < n_idx) index_scores_block<HB, FP8, DEPTH, kIdxWaves>(a, L % rows, L / rows);
   else compress_batch_block(cb, L - n_idx);
 }
 
@@ -348,12 +355,15 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   const int HB = (a.Hi + 15) / 16;
   const bool f8 = a.key_dtype == CSA_FP8_E4M3;
   const bool deep = (long long)grid.x * grid.y <= kDeepRingBlocks;
+#ifndef CSA_IDX_DEEP_WAVES
+#define CSA_IDX_DEEP_WAVES 4   // 8 waves (two per SIMD at one block per CU) measured slower: 17.9 against 16.7 us at 65K
+#endif
 #define CSA_IDX_LAUNCH(hb)                                                                     \
   if (HB == hb) {                                                                              \
-    if (f8 && deep) hipLaunchKernelGGL((k_index_scores<hb, true, 8>), grid, dim3(256), 0, s, a); \
-    else if (f8) hipLaunchKernelGGL((k_index_scores<hb, true, 4>), grid, dim3(256), 0, s, a);   \
-    else if (deep) hipLaunchKernelGGL((k_index_scores<hb, false, 8>), grid, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((k_index_scores<hb, false, 4>), grid, dim3(256), 0, s, a);          \
+    if (f8 && deep) hipLaunchKernelGGL((k_index_scores<hb, true, 8, CSA_IDX_DEEP_WAVES>), grid, dim3(64 * CSA_IDX_DEEP_WAVES), 0, s, a); \
+    else if (f8) hipLaunchKernelGGL((k_index_scores<hb, true, 4, kIdxWaves>), grid, dim3(256), 0, s, a);   \
+    else if (deep) hipLaunchKernelGGL((k_index_scores<hb, false, 8, CSA_IDX_DEEP_WAVES>), grid, dim3(64 * CSA_IDX_DEEP_WAVES), 0, s, a); \
+    else hipLaunchKernelGGL((k_index_scores<hb, false, 4, kIdxWaves>), grid, dim3(256), 0, s, a);          \
   }
   if (!f8 && a.Tq >= kMqRows && a.Di == 128) {
     const dim3 gmq(a.B * ((a.Tq + kMqRows - 1) / kMqRows));
