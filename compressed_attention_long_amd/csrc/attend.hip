@@ -114,10 +114,21 @@ __device__ __forceinline__ void ring_barrier() {
 // cannot tell the four tile buffers apart, and would wait for every load in flight before any read
 // of any tile buffer.  The ring's waits are explicit instead (wait_tiles before ring_barrier), and
 // the "memory" clobber keeps LDS accesses from moving across the issue.
+// m0 (the LDS base of the load) is a reserved register, so it is saved and restored around the
+// load (the load takes m0 when it issues), with a wait state after each write of it.
 __device__ __forceinline__ void dma_row(const void* src_lane, uint16_t* lds_row) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void*)lds_row;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(src_lane)
-               : "memory", "m0");
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)lds_row;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
+      : "s"(base), "v"(src_lane)
+      : "memory");
 }
 
 // wait until at most k tiles of RPW loads each are outstanding, k in 0..3

@@ -50,30 +50,6 @@ __device__ __forceinline__ f32x2 unpack_f16x2(uint32_t w) {
 __device__ __forceinline__ f32x2 fp8x2_lo(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false); }
 __device__ __forceinline__ f32x2 fp8x2_hi(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true); }
 
-// fp32 -> E4M3FN code, round to nearest even, saturating at +-448 (finite input).
-// Written from the format definition: 1 sign, 4 exponent (bias 7), 3 mantissa bits,
-// subnormal spacing 2^-9, largest finite value 1.75 * 2^8.
-__device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float x) {
-  uint32_t u = __float_as_uint(x);
-  uint32_t sign = (u >> 24) & 0x80u;
-  float a = fminf(fabsf(x), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {                    // below 2^-6: subnormal range, spacing 2^-9
-    float m = rintf(a * 512.0f);          // exact scaling; rintf rounds half to even
-    code = (uint32_t)m;                   // 0..8 (8 == smallest normal, encoded correctly as 1<<3)
-  } else {
-    uint32_t ua = __float_as_uint(a);
-    // keep 3 mantissa bits of the fp32 value with round-to-nearest-even
-    uint32_t lsb = (ua >> 20) & 1u;
-    ua += 0x7ffffu + lsb;
-    uint32_t e = (ua >> 23) - 127 + 7;    // biased e4m3 exponent (1..15)
-    uint32_t m = (ua >> 20) & 7u;
-    code = (e << 3) | m;
-    if (code > 0x7eu) code = 0x7eu;       // saturate (448 = 0x7e)
-  }
-  return code == 0 ? 0u : (code | sign);
-}
-
 // fp32 -> OCP E2M1 code (4 bits), round to nearest even on the E2M1 grid, saturating at
 // +-6; written from the format definition: 1 sign, 2 exponent (bias 1), 1 mantissa bit,
 // magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (the grid step is 0.5 below 2, 1 below 4, 2 above).

@@ -203,10 +203,14 @@ __device__ __forceinline__ void finish_row(const PoolState& p, const CompressArg
     float scale = amax / 448.0f;
     uint32_t lo = 0, hi = 0;
     if (scale > 0.f) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_fp8_e4m3(e[i] / scale) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= f32_to_fp8_e4m3(e[4 + i] / scale) << (8 * i);
+      // codes: round to nearest even of e / scale, by gfx950's converter (OCP E4M3FN), on e times
+      // the fp32 reciprocal of the scale (within an fp32 ulp of the quotient; |e / scale| <= 448, so
+      // nothing saturates)
+      const float inv = 1.0f / scale;
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(e[0] * inv, e[1] * inv, 0u, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(e[2] * inv, e[3] * inv, lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(e[4] * inv, e[5] * inv, 0u, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(e[6] * inv, e[7] * inv, hi, true);
     }
     u32x2 w;
     w[0] = lo;

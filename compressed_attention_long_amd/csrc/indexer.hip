@@ -845,7 +845,11 @@ hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
     const dim3 grid(rows);
     if (a.cap <= 4096) hipLaunchKernelGGL((k_topk_reg<1024, 4>), grid, dim3(1024), 0, s, a);
     else if (a.cap <= 8192) hipLaunchKernelGGL((k_topk_reg<1024, 8>), grid, dim3(1024), 0, s, a);
-    else if (a.cap <= 16384) hipLaunchKernelGGL((k_topk_reg<1024, 16>), grid, dim3(1024), 0, s, a);
+#ifndef CSA_TOPK16K_T
+#define CSA_TOPK16K_T 1024
+#endif
+    else if (a.cap <= 16384)
+      hipLaunchKernelGGL((k_topk_reg<CSA_TOPK16K_T, 16384 / CSA_TOPK16K_T>), grid, dim3(CSA_TOPK16K_T), 0, s, a);
     else if (a.cap <= 32768) hipLaunchKernelGGL((k_topk_reg<1024, 32>), grid, dim3(1024), 0, s, a);
     else if (a.cap <= 49152) hipLaunchKernelGGL((k_topk_reg<1024, 48>), grid, dim3(1024), 0, s, a);
     else hipLaunchKernelGGL((k_topk_reg<1024, 64>), grid, dim3(1024), 0, s, a);

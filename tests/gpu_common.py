@@ -138,8 +138,9 @@ def check_fp8_rows(codes_g: np.ndarray, scales: np.ndarray, ref: np.ndarray, bou
     y = np.where(s_full > 0, ref / safe, 0.0)
     mag = np.abs(O.fp8_e4m3_decode(codes_g))
     sign = np.where(codes_g & 0x80, -1.0, 1.0)
-    # the kernel divides its fp32 value by its scale in fp32: one more relative rounding
-    tol = bound / safe * (1 + 1e-6) + 2.0 * U32 * np.abs(y)
+    # the kernel multiplies its fp32 value by the fp32 reciprocal of its scale: two more relative
+    # roundings (of the reciprocal and of the product)
+    tol = bound / safe * (1 + 1e-6) + 3.0 * U32 * np.abs(y)
     return check_codes_against_grid(mag, sign, y, tol, "fp8", what)
 
 
