@@ -36,111 +36,9 @@
 //  * several splits of the row set run in parallel when the query rows alone cannot
 //    fill the GPU; their (max, sums, normalised fp16 output) partials are merged by
 //    k_attend_combine.  With one split the kernel normalises, rotates and stores.
-#include "common.hpp"
-#include "internal.hpp"
+#include "attend_dev.hpp"
 
 namespace csa {
-
-constexpr int kD = 512;             // channels (head dim)
-// bf16 per LDS row: 1056 B, so consecutive rows start 8 banks apart (no bank conflicts for the
-// scores' 16-byte row reads or the transposing reads of P V at this pitch).
-constexpr int kPitch = 528;
-constexpr int kTR = kAttTile;       // rows per tile
-constexpr float kRescale = 8.f;     // lazy-rescale threshold (log2 units)
-
-// Block shape: NP wave pairs, 16 heads each.
-template <int NP>
-struct AttShape {
-  static constexpr int HPB = 16 * NP;     // heads per block
-  static constexpr int NW = 2 * NP;       // waves
-  static constexpr int NT = 64 * NW;      // threads
-  static constexpr int RPW = kTR / NW;    // rows of a tile each wave moves
-};
-
-__device__ __forceinline__ int visible_rows_att(int64_t qp, int64_t pos0, int window, int stride,
-                                                int n_valid, int cap) {
-  int nv = min(max(n_valid, 0), cap);
-  int64_t num = qp - pos0 - (window - 1);
-  if (num < 0) return 0;
-  return (int)min((int64_t)nv, num / stride + 1);
-}
-
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
-
-// Reductions over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane groups holding one head) with
-// the gfx950 lane-swap permutes, no LDS round trip.
-__device__ __forceinline__ float max_lane_groups(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const uint32_t v = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_lane_groups(float x) {
-  const uint32_t u = __float_as_uint(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t v = __float_as_uint(y);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Hardware exp2 (v_exp_f32): results below 2^-126 flush to zero, which softmax weights tolerate.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Wait until at most N vector-memory loads of this wave are outstanding (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima = no wait).  Loads
-// complete in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-// Workgroup barrier for the tile ring.  __syncthreads() is a release fence plus the barrier, and
-// the fence waits for every LDS write of the wave, the DMA loads into LDS included: no tile could
-// stay in flight across it.  Here the waits are explicit instead: this wave's own LDS stores
-// (lgkmcnt(0)) before the barrier, and (by the caller, with wait_tiles) the DMA of exactly the
-// tiles the next step reads.  The "memory" clobber keeps the compiler from moving LDS accesses
-// across the barrier; it still counts the DMA loads that are in flight for every later LDS read.
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));   // lgkmcnt(0)
-  asm volatile("s_barrier" ::: "memory");
-}
-
-// One 1 KB row from global memory into LDS (16 bytes per lane, lane i at lds_row + 16 i) by the
-// direct global-to-LDS load, issued through inline asm: the compiler's own tracking of these loads
-// cannot tell the four tile buffers apart, and would wait for every load in flight before any read
-// of any tile buffer.  The ring's waits are explicit instead (wait_tiles before ring_barrier), and
-// the "memory" clobber keeps LDS accesses from moving across the issue.
-// m0 (the LDS base of the load) is a reserved register, so it is saved and restored around the
-// load (the load takes m0 when it issues), with a wait state after each write of it.
-__device__ __forceinline__ void dma_row(const void* src_lane, uint16_t* lds_row) {
-  const uint32_t base = (uint32_t)(uintptr_t)(lds_void*)lds_row;
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0"
-      : "=&s"(saved)
-      : "s"(base), "v"(src_lane)
-      : "memory");
-}
-
-// wait until at most k tiles of RPW loads each are outstanding, k in 0..3
-template <int RPW>
-__device__ __forceinline__ void wait_tiles(int k) {
-  switch (k) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<RPW>(); break;
-    case 2: wait_vmcnt<2 * RPW>(); break;
-    default: wait_vmcnt<3 * RPW>(); break;
-  }
-}
 
 // ---------------------------------------------------------------- grouped kernel (bf16 caches)
 //
@@ -397,19 +295,21 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
     const int buf = bcur + grp;
     const uint16_t* tl = cur + grp * T * kPitch;
 
-    // S^T = K Q^T for rows 16kb + [0,16) of the tile
+    // S^T = K Q^T for rows 16kb + [0,16) of the tile: chunk by chunk over the row blocks, so that
+    // the KB accumulation chains interleave; the lo parts of the rotated chunks are zero without
+    // rotation and add nothing
     constexpr int KB = T / 16;
     f32x4 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* rp = &tl[(16 * kb + n) * kPitch + 8 * g];
+    for (int kb = 0; kb < KB; ++kb) sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* rp0 = &tl[n * kPitch + 8 * g];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp + 32 * c);
+    for (int c = 0; c < 16; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(rp0 + 16 * kb * kPitch + 32 * c);
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sacc[kb], 0, 0, 0);
-        if (c >= 14 && q_split)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[c - 14], sacc[kb], 0, 0, 0);
+        if (c >= 14) sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[c - 14], sacc[kb], 0, 0, 0);
       }
     }
     // online softmax over this tile's rows 16kb + 4g + i (lane's head n)
@@ -1149,19 +1049,22 @@ __global__ void __launch_bounds__(AttShape<NP>::NT) k_attend(AttendArgs a) {
 // weights as they entered the split's P V product), lse = M + log2(2^(sink - M) + sum l_s
 // 2^(m_s - M)) with the exact sums l_s; then rotate back and store.  A block of 256 lanes merges 4
 // (row, head) pairs, 8 channels per lane; splits are merged online, four per round, so that a
-// round's (max, sum) and output loads are all in flight together.
+// round's (max, sum) and output loads are all in flight together.  The (cos, sin) table of the
+// row's position is built by the whole wave, one frequency per lane, while the loads are in
+// flight.
 constexpr int kCombineHeads = 4;
 __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArgs a) {
+  __shared__ f32x2 rtab[kCombineHeads][kD / 2];
   const int rows = a.B * a.Tq;
   // blocks in the order of the attention grid's XCD ranges: a row's merge runs on the XCD that
   // wrote its partials
-  const int rh = (int)xcd_remap(blockIdx.x, gridDim.x) * kCombineHeads + (threadIdx.x >> 6);   // row * H + head
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rh = (int)xcd_remap(blockIdx.x, gridDim.x) * kCombineHeads + wave;   // row * H + head
   if (rh >= rows * a.H) return;
   const int row = rh / a.H, head = rh % a.H;
-  const int d0 = (threadIdx.x & 63) * 8;
-  const int64_t p = a.q_pos[row];
-  const float sink2 = a.sink[head] * kLog2e;
+  const int d0 = lane * 8;
   const int64_t base = (int64_t)row * a.nsplit * a.H + head;        // partial (row, s, head) = base + s * H
+  const float sink2 = a.sink[head] * kLog2e;
   // online merge, 4 splits per round: each round's (max, sum) and output loads go out together
   float M = sink2, Z = 1.f, Zo = 1.f;   // relative to 2^M
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1179,17 +1082,25 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
       // read once: nontemporal loads keep them from displacing other lines
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.part_o + pr * kD + d0));
     }
+    if (s0 == 0 && a.rope_dim > 0) {
+      const int64_t p = a.q_pos[row];
+      for (int i = lane; i < a.rope_dim / 2; i += kWave) {
+        float cs, sn;
+        rope_cs(p, a.inv_freq[i], cs, sn);
+        rtab[wave][i] = f32x2{cs, -sn};   // rotation by -q_pos: same cosine, negated sine
+      }
+    }
     float Mn = M;
 #pragma unroll
     for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, ms[u]);
-    const float r = exp2f(M - Mn);
+    const float r = fast_exp2(M - Mn);
     Z *= r;
     Zo *= r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= r;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float w = exp2f(ms[u] - Mn);   // 0 for the padding of a partial round
+      const float w = fast_exp2(ms[u] - Mn);   // 0 for the padding of a partial round
       Z += ls[u] * w;
       Zo += ns[u] * w;
       const float wo = ldexpf(ns[u] * w, (int)es[u]);
@@ -1211,11 +1122,10 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
     for (int k2 = 0; k2 < 4; ++k2) {
       const int d = d0 + 2 * k2;
       if (d >= rot0) {
-        float cs, sn;
-        rope_cs(-p, a.inv_freq[(d - rot0) >> 1], cs, sn);
+        const f32x2 t2 = rtab[wave][(d - rot0) >> 1];
         const float x0 = o[2 * k2], x1 = o[2 * k2 + 1];
-        o[2 * k2] = x0 * cs - x1 * sn;
-        o[2 * k2 + 1] = x0 * sn + x1 * cs;
+        o[2 * k2] = x0 * t2[0] - x1 * t2[1];
+        o[2 * k2 + 1] = x0 * t2[1] + x1 * t2[0];
       }
     }
   }
