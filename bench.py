@@ -337,7 +337,8 @@ def compressor_bulk(torch, reps=3):
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_bytes_csa_decode_65k.md")
 
 
-CALL_SOURCES = {"attend": ("attend.hip",), "index": ("indexer.hip", "compress_dev.hpp"),
+CALL_SOURCES = {"attend": ("attend.hip", "attend_dev.hpp", "workspace.hpp"),
+                "index": ("indexer.hip", "compress_dev.hpp", "workspace.hpp"),
                 "compress": ("compress.hip", "compress_dev.hpp")}
 
 
@@ -612,8 +613,9 @@ def main():
     dom = max((k for k in calls if k != "index_compress"), key=lambda k: calls[k]["ms"])
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if dom == "attend" or (dom == "index" and wl.Tq >= 16):
-        kern = ("csa_attend (k_attend + k_attend_combine)" if wl.mode == "csa" else "hca_attend") if dom == "attend" \
-            else "csa_index_topk (k_index_scores_mq + top-k)"
+        att_k = "k_attend_grp" if wl.kv_dtype == "bf16" else "k_attend"
+        kern = (f"{'csa_attend' if wl.mode == 'csa' else 'hca_attend'} ({att_k} + k_attend_combine)" if dom == "attend"
+                else "csa_index_topk (k_index_scores_mq + top-k)")
         intensity = costs[f"{dom}_flops"] / costs[f"{dom}_bytes"]
         roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom), "kernel": kern,
