@@ -51,25 +51,29 @@ namespace csa {
 // current one is consumed.  Scores and outputs are transposed as in the pair kernel below; the
 // rotated query dims are carried as bf16 hi + lo; the sink joins once (epilogue or merge); lazy
 // rescaling; weights rounded to bf16 for P V and normalised by their own sum.
-constexpr int kAttWaves = 8;
-constexpr int kAttThreads = kAttWaves * 64;
-constexpr int kStepRows = 64;       // rows staged per step (one tile per group); two steps in LDS
-
-template <int HPB>
+// W waves per block, each moving 8 rows of every step: a step stages 8 W rows
+template <int HPB, int W>
 struct AttCfg {
+  static constexpr int SR = 8 * W;               // rows staged per step (one tile per group)
   static constexpr int GW = HPB / 16;            // waves per tile group
-  static constexpr int NG = kAttWaves / GW;      // tile groups
-  static constexpr int T = kStepRows / NG;       // rows per tile
-  static constexpr int RPT = T / 8;              // rows of each tile a wave moves per step
+  static constexpr int NG = W / GW;              // tile groups
+  static constexpr int T = SR / NG;              // rows per tile
+  static constexpr int RPT = T / W;              // rows of each tile a wave moves per step
   static_assert(T == kAttGroupTile64 * HPB / 64, "tile rows must match the plan's");
 };
 
-// Grouped kernel (bf16 caches); HPB: the block shape (AttCfg).
-template <bool CSA, int HPB>
-__global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
+// Grouped kernel (bf16 caches); HPB, W: the block shape (AttCfg).  W = 4: one group of four
+// waves (64 heads), a block small enough in LDS that two run on a CU.
+template <bool CSA, int HPB, int W>
+__global__ void __launch_bounds__(64 * W, 2) k_attend_grp(AttendArgs a) {
   constexpr bool QKV = false;
   constexpr int kRowB = 2 * kD;
-  constexpr int GW = AttCfg<HPB>::GW, NG = AttCfg<HPB>::NG, T = AttCfg<HPB>::T, RPT = AttCfg<HPB>::RPT;
+  using Cfg = AttCfg<HPB, W>;
+  constexpr int kAttWaves = W, kStepRows = Cfg::SR;
+  constexpr int GW = Cfg::GW, NG = Cfg::NG, T = Cfg::T, RPT = Cfg::RPT;
+  // the block's query rows go through the second tile half when they fit there, else (W = 4)
+  // straight into registers
+  constexpr bool kQInLds = HPB <= kStepRows;
   // Two halves of tile buffers as two objects: one step's tiles are read from one half while
   // the next step's stream into the other, and separate objects let the compiler see that the
   // LDS reads never touch the half in flight (it then does not wait for those loads).  Group
@@ -106,7 +110,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
   auto pair_idx = [&](int pr) -> int {
     const int k = lane & 7;
     const int t = NG * pr + k / RPT;
-    const int slot = s0 + t * T + wave + 8 * (k % RPT);
+    const int slot = s0 + t * T + wave + W * (k % RPT);
     int j = -1;
     if (CSA && lane < 8 && slot < s0 + a.slots_per_split && slot < a.topk) j = idxrow[slot];
     return j;
@@ -114,8 +118,14 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
   const int idx0 = pair_idx(0);
   int idx_next = pair_idx(1);
   // the block's HPB query rows (1 KB each) go straight into the second tile half, row h at
-  // h kPitch, once for both tile groups; wave w moves rows w, w + 8, ...
-  {
+  // h kPitch, once for all tile groups; wave w moves rows w, w + W, ...  (W = 4: each wave's own
+  // 16 heads into registers instead, raw; rotated below)
+  u32x4 qraw[kQInLds ? 1 : 16];
+  if constexpr (!kQInLds) {
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + min(head, a.H - 1)) * kD + 8 * g;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qh + 32 * c);
+  } else {
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q) + (int64_t)row * a.H * (2 * kD);
 #pragma unroll
     for (int i = 0; i < HPB / kAttWaves; ++i) {
@@ -160,7 +170,7 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
   auto pair_rows = [&](int pr, int j) -> PairRows {
     const int k = lane & 7;
     const int t = NG * pr + k / RPT;
-    const int slot = s0 + t * T + wave + 8 * (k % RPT);
+    const int slot = s0 + t * T + wave + W * (k % RPT);
     int r = -1;
     if (lane < 8 && t < ntile && slot < s1) {
       if (slot >= n_ent) r = -2 - (int)(r_lo + (slot - n_ent));
@@ -176,12 +186,12 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
   auto mark_pair = [&](int pr, const PairRows& pr_rows, int bnxt) {
     if (lane < 8) {
       const int t = NG * pr + lane / RPT;
-      if (t < ntile) tvalid[bnxt + lane / RPT][wave + 8 * (lane % RPT)] = pr_rows.r != -1;
+      if (t < ntile) tvalid[bnxt + lane / RPT][wave + W * (lane % RPT)] = pr_rows.r != -1;
     }
   };
   // LDS address of lane-k row of a step in a half
   auto row_dst = [&](uint16_t* half, int k) -> uint16_t* {
-    return half + ((k / RPT) * T + wave + 8 * (k % RPT)) * kPitch;
+    return half + ((k / RPT) * T + wave + W * (k % RPT)) * kPitch;
   };
   auto issue_row = [&](int pr, const PairRows& pr_rows, int k, uint16_t* half) {
     const int t = NG * pr + k / RPT;
@@ -237,10 +247,10 @@ __global__ void __launch_bounds__(kAttThreads, 2) k_attend_grp(AttendArgs a) {
   bf16x8 qlo[2];
   {
     const int rot0 = kD - a.rope_dim;
-    const uint16_t* qs = tbB + (hw * 16 + n) * kPitch + 8 * g;
+    const uint16_t* qs = tbB + (kQInLds ? (hw * 16 + n) * kPitch + 8 * g : 0);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qs + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = !head_ok ? u32x4{0u, 0u, 0u, 0u} : (kQInLds ? *reinterpret_cast<const u32x4*>(qs + 32 * c) : qraw[c]);
       u32x4 lo = {0u, 0u, 0u, 0u};
       if (32 * c + 32 > rot0 && a.rope_dim > 0) {
 #pragma unroll
@@ -1161,10 +1171,10 @@ static void launch_attend_pairs(const AttendArgs& a, dim3 grid, hipStream_t s) {
   }
 }
 
-template <int HPB>
+template <int HPB, int W>
 static void launch_attend_groups(const AttendArgs& a, dim3 grid, hipStream_t s) {
-  if (a.csa_mode != 0) hipLaunchKernelGGL((k_attend_grp<true, HPB>), grid, dim3(kAttThreads), 0, s, a);
-  else hipLaunchKernelGGL((k_attend_grp<false, HPB>), grid, dim3(kAttThreads), 0, s, a);
+  if (a.csa_mode != 0) hipLaunchKernelGGL((k_attend_grp<true, HPB, W>), grid, dim3(64 * W), 0, s, a);
+  else hipLaunchKernelGGL((k_attend_grp<false, HPB, W>), grid, dim3(64 * W), 0, s, a);
 }
 
 hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
@@ -1176,9 +1186,11 @@ hipError_t launch_attend(const AttendArgs& a0, hipStream_t s) {
   const int HG = (a.H + pl.hpb - 1) / pl.hpb;
   const long long blocks = (long long)rows * HG * a.nsplit;
   const dim3 grid((unsigned)blocks);
-  if (pl.kind == kAttGroups) {
-    if (pl.hpb == 64) launch_attend_groups<64>(a, grid, s);
-    else launch_attend_groups<32>(a, grid, s);
+  if (pl.kind == kAttGroups4) {
+    launch_attend_groups<64, 4>(a, grid, s);
+  } else if (pl.kind == kAttGroups) {
+    if (pl.hpb == 64) launch_attend_groups<64, 8>(a, grid, s);
+    else launch_attend_groups<32, 8>(a, grid, s);
   } else {
     if (pl.hpb == 64) launch_attend_pairs<4>(a, grid, s);
     else launch_attend_pairs<2>(a, grid, s);

@@ -81,7 +81,7 @@ inline size_t topk_workspace(int rows, int cap, int k) {
 // output channels, 64 rows per step, 32- or 16-row tiles) and the wave-pair kernel for quantized
 // caches (pairs of waves sharing 16 heads, 32-row tiles through a four-buffer ring, fp8 scales
 // applied in fp32).
-constexpr int kAttGroups = 0, kAttPairs = 1;
+constexpr int kAttGroups = 0, kAttPairs = 1, kAttGroups4 = 2;   // kernels: grouped (8 or 4 waves), wave pairs
 constexpr int kAttGroupTile64 = 32;    // grouped kernel: rows per tile with 64 heads per block
 constexpr int kAttTile = 32;           // wave-pair kernel: rows per tile
 constexpr int kAttIdxMax = 1280;       // top-k indices of one split held in LDS (a multiple of 64)
@@ -91,7 +91,7 @@ constexpr int kAttTargetBlocks = 256;  // split until the grid has about this ma
 constexpr int kAttBf16 = 0, kAttFp8 = 1, kAttFp4 = 2;
 
 struct AttendPlan {
-  int kind;     // kAttGroups or kAttPairs
+  int kind;     // kAttGroups, kAttGroups4 or kAttPairs
   int hpb;      // heads per block (64 or 32)
   int nsplit;   // splits of each query row's row set
   int sps;      // rows per split (whole tiles)
@@ -101,13 +101,14 @@ struct AttendPlan {
 // blocks, at least two tiles per split, at most `idx_max` slots per split (0: no limit); the
 // per-split count is rounded up to whole tiles.  slot_cap = the longest row set (top-k or visible
 // entries, plus the window).
-inline AttendPlan attend_plan_for(int kind, int hpb, int tile, int idx_max, int rows, int H, int slot_cap) {
+inline AttendPlan attend_plan_for(int kind, int hpb, int tile, int idx_max, int rows, int H, int slot_cap,
+                                  int target = kAttTargetBlocks) {
   AttendPlan pl{};
   pl.kind = kind;
   pl.hpb = hpb;
   const long long HG = (H + hpb - 1) / hpb;
   const long long base = (long long)rows * HG;
-  long long ns = (kAttTargetBlocks + base - 1) / base;
+  long long ns = (target + base - 1) / base;
   const long long max_ns = ((long long)slot_cap + 2 * tile - 1) / (2 * tile);
   if (ns > max_ns) ns = max_ns;
   if (ns < 1) ns = 1;
@@ -131,6 +132,11 @@ inline AttendPlan attend_plan_for(int kind, int hpb, int tile, int idx_max, int 
 // registers of the larger shape's second pair).
 inline AttendPlan attend_plan(int rows, int H, int slot_cap, bool csa, int kv_kind) {
   if (kv_kind == kAttBf16) {
+    // 64 heads in 4-wave blocks, two per CU (their phases drift apart: prefill 1.85 -> 1.61 ms),
+    // where the query rows alone fill two blocks per CU, so that no split is added (with splits
+    // the extra partials cost what the kernel gains: HCA 1M even, 65K decode +4 us)
+    const AttendPlan p4 = attend_plan_for(kAttGroups4, 64, kAttGroupTile64, 0, rows, H, slot_cap, 2 * kAttTargetBlocks);
+    if (p4.nsplit == 1 && (long long)rows * ((H + 63) / 64) >= 2 * kAttTargetBlocks) return p4;
     const AttendPlan p64 = attend_plan_for(kAttGroups, 64, kAttGroupTile64, 0, rows, H, slot_cap);
     const long long blocks64 = (long long)rows * ((H + 63) / 64) * p64.nsplit;
     return blocks64 < kAttTargetBlocks ? attend_plan_for(kAttGroups, 32, kAttGroupTile64 / 2, 0, rows, H, slot_cap)

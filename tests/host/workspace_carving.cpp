@@ -92,8 +92,11 @@ int main() {
           const AttendPlan pl = attend_plan(rows, H, slots, csa != 0, kind);
           CHECK(kind != kAttFp8 || pl.hpb == 32, "rows %d H %d slots %d: fp8 plan with %d heads per block", rows, H,
                 slots, pl.hpb);
-          CHECK((kind == kAttBf16) == (pl.kind == kAttGroups), "rows %d H %d slots %d: kernel kind", rows, H, slots);
-          const int tile = pl.kind == kAttGroups ? (pl.hpb == 64 ? kAttGroupTile64 : kAttGroupTile64 / 2) : kAttTile;
+          CHECK((kind == kAttBf16) == (pl.kind == kAttGroups || pl.kind == kAttGroups4), "rows %d H %d slots %d: kernel kind",
+                rows, H, slots);
+          CHECK(pl.kind != kAttGroups4 || (pl.hpb == 64 && pl.nsplit == 1), "rows %d H %d slots %d: 4-wave plan", rows, H,
+                slots);
+          const int tile = pl.kind != kAttPairs ? (pl.hpb == 64 ? kAttGroupTile64 : kAttGroupTile64 / 2) : kAttTile;
           CHECK(pl.hpb == 32 || pl.hpb == 64, "rows %d H %d slots %d: %d heads per block", rows, H, slots, pl.hpb);
           CHECK(pl.nsplit >= 1 && pl.sps >= tile && pl.sps % tile == 0,
                 "rows %d H %d slots %d: %d splits of %d", rows, H, slots, pl.nsplit, pl.sps);

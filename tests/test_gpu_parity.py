@@ -342,6 +342,9 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     ("csa", 2, 3, 64, 900, [900, 40], True, 300, 128, 140, 1 / math.sqrt(512), 1.0),   # fp8 KV, < k visible
     ("csa", 1, 1, 16, 500, [500], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),        # window only
     ("csa", 4, 64, 64, 600, [600] * 4, False, 200, 128, 200, 0.1, 2.0),               # 256 rows: no split
+    # 512 rows x 128 heads: the 4-wave block shape (two blocks per CU, no split)
+    ("csa", 4, 128, 128, 600, [600, 599, 400, 300], False, 200, 128, 256, 0.1, 2.0),
+    ("hca", 2, 256, 128, 300, [300, 250], False, 0, 128, 384, 1 / math.sqrt(512), 1.0),
     ("csa", 4, 1, 64, 6000, [6000, 5000, 512, 100], True, 512, 128, 129, 1 / math.sqrt(512), 4.0),  # CSA2: top-512, fp8
     ("hca", 2, 1, 128, 700, [700, 300], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),
     ("hca", 1, 2, 128, 64, [64], True, 0, 128, 129, 1 / math.sqrt(512), 4.0),        # fp8, sharper q
