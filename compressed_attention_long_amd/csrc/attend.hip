@@ -1078,31 +1078,29 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
   // online merge, 4 splits per round: each round's (max, sum) and output loads go out together
   float M = sink2, Z = 1.f, Zo = 1.f;   // relative to 2^M
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < a.nsplit; s0 += 4) {
+  // one round: four splits' (max, sums, e) and output slices, issued together; a round's loads go
+  // out before the previous round is merged (two rounds in flight)
+  struct Round {
     u32x4 v[4];
     float ms[4], ns[4], ls[4], es[4];
+  };
+  auto load_round = [&](int s0, Round& R) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t pr = base + (int64_t)min(s0 + u, a.nsplit - 1) * a.H;
       const f32x4 ml = *reinterpret_cast<const f32x4*>(a.part_ml + 4 * pr);
-      ms[u] = s0 + u < a.nsplit ? ml[0] : kNegBig;
-      ns[u] = ml[1];
-      ls[u] = ml[2];
-      es[u] = ml[3];
+      R.ms[u] = s0 + u < a.nsplit ? ml[0] : kNegBig;
+      R.ns[u] = ml[1];
+      R.ls[u] = ml[2];
+      R.es[u] = ml[3];
       // read once: nontemporal loads keep them from displacing other lines
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.part_o + pr * kD + d0));
+      R.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.part_o + pr * kD + d0));
     }
-    if (s0 == 0 && a.rope_dim > 0) {
-      const int64_t p = a.q_pos[row];
-      for (int i = lane; i < a.rope_dim / 2; i += kWave) {
-        float cs, sn;
-        rope_cs(p, a.inv_freq[i], cs, sn);
-        rtab[wave][i] = f32x2{cs, -sn};   // rotation by -q_pos: same cosine, negated sine
-      }
-    }
+  };
+  auto merge_round = [&](const Round& R) {
     float Mn = M;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, ms[u]);
+    for (int u = 0; u < 4; ++u) Mn = fmaxf(Mn, R.ms[u]);
     const float r = fast_exp2(M - Mn);
     Z *= r;
     Zo *= r;
@@ -1110,18 +1108,35 @@ __global__ void __launch_bounds__(64 * kCombineHeads) k_attend_combine(AttendArg
     for (int i = 0; i < 8; ++i) o[i] *= r;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float w = fast_exp2(ms[u] - Mn);   // 0 for the padding of a partial round
-      Z += ls[u] * w;
-      Zo += ns[u] * w;
-      const float wo = ldexpf(ns[u] * w, (int)es[u]);
+      const float w = fast_exp2(R.ms[u] - Mn);   // 0 for the padding of a partial round
+      Z += R.ls[u] * w;
+      Zo += R.ns[u] * w;
+      const float wo = ldexpf(R.ns[u] * w, (int)R.es[u]);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x2 hh = unpack_f16x2(v[u][k]);
+        const f32x2 hh = unpack_f16x2(R.v[u][k]);
         o[2 * k] += wo * hh[0];
         o[2 * k + 1] += wo * hh[1];
       }
     }
     M = Mn;
+  };
+  Round R0, R1;
+  load_round(0, R0);
+  if (a.rope_dim > 0) {
+    const int64_t p = a.q_pos[row];
+    for (int i = lane; i < a.rope_dim / 2; i += kWave) {
+      float cs, sn;
+      rope_cs(p, a.inv_freq[i], cs, sn);
+      rtab[wave][i] = f32x2{cs, -sn};   // rotation by -q_pos: same cosine, negated sine
+    }
+  }
+  for (int s0 = 0; s0 < a.nsplit; s0 += 8) {
+    if (s0 + 4 < a.nsplit) load_round(s0 + 4, R1);
+    merge_round(R0);
+    if (s0 + 4 >= a.nsplit) break;
+    if (s0 + 8 < a.nsplit) load_round(s0 + 8, R0);
+    merge_round(R1);
   }
   const float inv = Zo > 0.f ? 1.f / Zo : 0.f;
 #pragma unroll
