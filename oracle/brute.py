@@ -121,3 +121,31 @@ def hca_step(kv, z, pos0, q, q_pos, sink, W, scale, freqs, window, stride):
     rows += [rotate(kv[i], pos0 + i, freqs) for i in range(len(kv))
              if q_pos - W < pos0 + i <= q_pos]
     return attend(q, q_pos, rows, sink, scale, freqs)
+
+
+def out_projection(o, wa, wb):
+    """Grouped low-rank output projection with explicit loops (tiny sizes only).
+    o: T x H x D nested lists; wa: G x R x (H/G * D); wb: hidden x (G * R).  Returns y: T x hidden."""
+    T, H, D = len(o), len(o[0]), len(o[0][0])
+    G, R = len(wa), len(wa[0])
+    hg = H // G
+    y = []
+    for t in range(T):
+        cat = []
+        for g in range(G):
+            flat = []
+            for h in range(g * hg, (g + 1) * hg):
+                flat.extend(o[t][h])
+            for r in range(R):
+                acc = 0.0
+                for k, x in enumerate(flat):
+                    acc += wa[g][r][k] * x
+                cat.append(acc)
+        row = []
+        for j in range(len(wb)):
+            acc = 0.0
+            for k, x in enumerate(cat):
+                acc += wb[j][k] * x
+            row.append(acc)
+        y.append(row)
+    return y

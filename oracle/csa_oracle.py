@@ -29,7 +29,8 @@ the definition states.  Sources (page title, then section):
 * "DeepSeek-V4-Pro" (model atlas), Raw config fields: head_dim 512,
   qk_rope_head_dim 64, index_n_heads 64, index_head_dim 128, index_topk 1024,
   sliding_window 128, num_attention_heads 128, num_key_value_heads 1,
-  compress_rope_theta 160000, compress_ratios 4 (CSA) and 128 (HCA).
+  compress_rope_theta 160000, compress_ratios 4 (CSA) and 128 (HCA); for the output side,
+  o_groups 16, o_lora_rank 1024 and hidden_size 7168.
 
 Readings where the pages are silent are listed beside the function that takes
 them (pairing of rotated dims, position of an entry, window edge, tie order,
@@ -448,3 +449,34 @@ def hca_query(q, q_pos, entries, entry_pos, win, win_pos, sink, scale, inv_freq,
     wm = window_rows(win_pos, q_pos, W)
     X = np.concatenate([np.asarray(entries, np.float64)[vis], np.asarray(win, np.float64)[wm]], 0)
     return attend(q, q_pos, X, sink, scale, inv_freq)
+
+
+# --------------------------------------------------------------------------
+# Grouped low-rank output projection (after attention)
+# --------------------------------------------------------------------------
+
+O_GROUPS = 16
+O_LORA_RANK = 1024
+HIDDEN = 7168
+
+
+def out_projection(o, wa, wb):
+    """The attention output of a token, projected back to the hidden size through grouped low-rank
+    factors ("DeepSeek-V4-Pro" model atlas, Raw config fields o_groups 16, o_lora_rank 1024,
+    hidden_size 7168; the fields alone are given, the reading below is the plainest one they
+    support): the heads' outputs (after the inverse rotation) are cut into G groups of H / G
+    consecutive heads; group g's H/G * D values go through its own down factor
+    wa[g] (R x (H/G) D) to R values; the G * R values, concatenated in group order, go through
+    the up factor wb (hidden x G R).
+
+    o: [T, H, D]; wa: [G, R, (H/G) D]; wb: [hidden, G R].  Returns (y [T, hidden], z [T, G, R])."""
+    o = np.asarray(o, np.float64)
+    wa = np.asarray(wa, np.float64)
+    wb = np.asarray(wb, np.float64)
+    T, H, D = o.shape
+    G, R, Kg = wa.shape
+    assert H % G == 0 and Kg == (H // G) * D and wb.shape[1] == G * R
+    xg = o.reshape(T, G, Kg)                      # group g = heads g H/G .. (g + 1) H/G - 1
+    z = np.einsum("tgk,grk->tgr", xg, wa)         # each group through its own down factor
+    y = z.reshape(T, G * R) @ wb.T                # concatenated, through the up factor
+    return y, z

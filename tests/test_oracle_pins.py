@@ -35,6 +35,8 @@ def test_oracle_constants_are_the_pages():
     assert (O.CSA_WINDOW, O.CSA_STRIDE) == (g["csa_window"]["value"], g["csa_stride"]["value"])
     assert O.HCA_WINDOW == O.HCA_STRIDE == g["hca_window"]["value"]
     assert g["csa_layers"]["value"] + g["hca_layers"]["value"] == g["num_hidden_layers"]["value"]
+    assert (O.O_GROUPS, O.O_LORA_RANK, O.HIDDEN) == (g["o_groups"]["value"], g["o_lora_rank"]["value"],
+                                                     g["hidden_size"]["value"])
 
 
 def test_entry_counts_golden():
@@ -577,3 +579,69 @@ def test_fp4_pack_order():
     p = O.fp4_pack(c)
     assert list(p[0]) == [0x21, 0x43, 0x0F]
     assert np.array_equal(O.fp4_unpack(p), c)
+
+
+# ---------------------------------------------------------------- grouped low-rank output projection
+
+def _proj_case(T=3, H=8, D=6, G=4, R=5, hidden=7, seed=11):
+    r = np.random.default_rng(seed)
+    return r.normal(size=(T, H, D)), r.normal(size=(G, R, (H // G) * D)), r.normal(size=(hidden, G * R))
+
+
+def test_out_projection_matches_brute_force_loops():
+    o, wa, wb = _proj_case()
+    y, _ = O.out_projection(o, wa, wb)
+    yb = np.array(brute.out_projection(o.tolist(), wa.tolist(), wb.tolist()))
+    assert np.allclose(y, yb, rtol=1e-12, atol=1e-12)
+
+
+def test_out_projection_identity_down_factors_give_the_flat_output():
+    # closed form: with wa[g] the identity (R = H/G * D) the rank-R codes are the group's own
+    # values, head after head, and y is wb applied to the whole flattened output
+    T, H, D, G = 2, 6, 4, 3
+    o, _, _ = _proj_case(T, H, D, G, 8, 5)
+    wa = np.stack([np.eye(8) for _ in range(G)])
+    wb = np.random.default_rng(3).normal(size=(5, G * 8))
+    y, z = O.out_projection(o, wa, wb)
+    assert np.array_equal(z.reshape(T, H, D), o)
+    assert np.allclose(y, o.reshape(T, H * D) @ wb.T, rtol=1e-13, atol=1e-13)
+
+
+def test_out_projection_group_of_a_head_is_its_block_of_consecutive_heads():
+    # zeroing the heads of group g changes only that group's codes, and y by exactly wb's block g
+    o, wa, wb = _proj_case()
+    G, R = wa.shape[:2]
+    hg = o.shape[1] // G
+    y, z = O.out_projection(o, wa, wb)
+    for g in range(G):
+        o2 = o.copy()
+        o2[:, g * hg:(g + 1) * hg] = 0.0
+        y2, z2 = O.out_projection(o2, wa, wb)
+        keep = [x for x in range(G) if x != g]
+        assert np.array_equal(z2[:, keep], z[:, keep])
+        assert np.all(z2[:, g] == 0.0)
+        assert np.allclose(y - y2, z[:, g] @ wb[:, g * R:(g + 1) * R].T, rtol=1e-12, atol=1e-12)
+
+
+def test_out_projection_consistent_group_permutation_changes_nothing():
+    o, wa, wb = _proj_case()
+    G, R = wa.shape[:2]
+    hg = o.shape[1] // G
+    perm = np.array([2, 0, 3, 1])
+    o2 = np.concatenate([o[:, p * hg:(p + 1) * hg] for p in perm], 1)
+    wb2 = np.concatenate([wb[:, p * R:(p + 1) * R] for p in perm], 1)
+    y, _ = O.out_projection(o, wa, wb)
+    y2, _ = O.out_projection(o2, wa[perm], wb2)
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-12)
+
+
+def test_out_projection_one_group_is_two_matrix_products():
+    # G = 1 reduces to the plain product wb (wa x), checked with torch's matmul in fp64
+    o, _, _ = _proj_case(G=1)
+    r = np.random.default_rng(5)
+    wa = r.normal(size=(1, 5, o.shape[1] * o.shape[2]))
+    wb = r.normal(size=(7, 5))
+    y, _ = O.out_projection(o, wa, wb)
+    x = torch.tensor(o.reshape(o.shape[0], -1))
+    ref = torch.tensor(wb) @ (torch.tensor(wa[0]) @ x.T)
+    assert np.allclose(y, ref.T.numpy(), rtol=1e-12, atol=1e-12)
