@@ -280,6 +280,46 @@ def time_reuse(wl, steps_n, warmup, torch, min_cache_bytes=4 << 30):
     return ms
 
 
+def out_projection_bench(torch, T=32, reps=50):
+    """csa_out_proj at the 65K decode batch (32 tokens; 128 heads x 512 -> 16 groups x rank 1,024 ->
+    hidden 7,168, atlas Raw config fields o_groups, o_lora_rank, hidden_size), synthetic bf16
+    factors, the bf16 attention output the decode step writes.  Not part of the timed step (the
+    pages' attention path ends at the attention output); reported as its own HBM-bound call: the
+    factors (2 B per element) are read once per call, the tokens' activations are small."""
+    from compressed_attention_long_amd import _lib as ops
+    dev = "cuda"
+    H, D, G, R, hidden = 128, 512, 16, 1024, 7168
+    g = torch.Generator(device=dev)
+    g.manual_seed(777)
+    o = torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    wa = (torch.randn((G, R, (H // G) * D), generator=g, device=dev, dtype=torch.float32) / 64.0).to(torch.bfloat16)
+    wb = (torch.randn((hidden, G * R), generator=g, device=dev, dtype=torch.float32) / 128.0).to(torch.bfloat16)
+    y = torch.empty((T, hidden), dtype=torch.bfloat16, device=dev)
+    ws = ops.workspace(ops.csa_out_proj_workspace_bytes(T, G, R, hidden), dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ops.csa_out_proj(o, wa, wb, y, ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        ops.csa_out_proj(o, wa, wb, y, ws)
+    samples = []
+    with torch.cuda.stream(s):
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            graph.replay()
+            e1.record(s)
+            e1.synchronize()
+            samples.append(e0.elapsed_time(e1))
+    ms = sum(samples) / len(samples)
+    nbytes = (wa.numel() + wb.numel()) * 2 + o.numel() * 2 + y.numel() * 2 + 2 * T * G * R * 4
+    flops = 2 * T * (H * D * R + G * R * hidden)
+    return {"tokens": T, "ms": ms, "stats": stats(samples), "bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
+            "shape": "o [32, 128, 512] bf16; wa [16, 1024, 4096] bf16; wb [7168, 16384] bf16; y bf16"}
+
+
 def compressor_bulk(torch, reps=3):
     """csa_compress over whole raw streams (the compressor's HBM benchmark): kv and pooling
     logits read once, entries written once.  Inputs tile one seeded 64K-token random block
@@ -562,6 +602,7 @@ def main():
                     help="comma-separated extra workloads measured into 'extra' ('none' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compressor-bulk", action="store_true")
+    ap.add_argument("--no-out-proj", action="store_true", help="skip the output projection's own timing")
     ap.add_argument("--no-achievable", action="store_true", help="skip the measured HBM / GEMM ceilings")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--pmc-probe", action="store_true",
@@ -671,6 +712,9 @@ def main():
             e2.update({"reuse_ms_per_step": tr, "reuse_layers_per_computed": w2.reuse, "layer_avg_ms": avg,
                        "tokens_per_s_layer_avg": w2.B * w2.Tq / (avg / 1e3)})
         extra[name] = e2
+    if not args.no_out_proj:
+        print("[bench] output projection (decode batch)", file=sys.stderr, flush=True)
+        extra["out_projection"] = out_projection_bench(torch)
     if not args.no_compressor_bulk:
         print("[bench] compressor over whole raw streams", file=sys.stderr, flush=True)
         extra["compressor_bulk"] = compressor_bulk(torch)

@@ -32,6 +32,8 @@ EXPORTS = (
     "csa_attend_noalloc",
     "hca_attend",
     "hca_attend_workspace_bytes",
+    "csa_out_proj",
+    "csa_out_proj_workspace_bytes",
     "csa_last_error",
     "csa_abi_version",
 )
@@ -94,6 +96,8 @@ _SIGS = {
     "hca_attend": (_i32, [_vp, _vp, _i32, _i32, _i32, _PC, _PC, _i32, _vp, _vp, _i32, _f32,
                           _vp, _i32, _vp, _vp, _sz, _vp]),
     "hca_attend_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "csa_out_proj": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _sz, _vp]),
+    "csa_out_proj_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "csa_last_error": (ctypes.c_char_p, []),
     "csa_abi_version": (_i32, []),
 }
@@ -317,6 +321,24 @@ def hca_attend(q: torch.Tensor, q_pos: torch.Tensor, kv: Cache, win: Cache, W: i
                            sink.data_ptr(), _ptr(inv_freq), rope_dim, softmax_scale, out.data_ptr(),
                            _out_code(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check("hca_attend", rc)
+
+
+def csa_out_proj_workspace_bytes(T: int, G: int, R: int, hidden: int) -> int:
+    return int(load().csa_out_proj_workspace_bytes(T, G, R, hidden))
+
+
+def csa_out_proj(o: torch.Tensor, wa: torch.Tensor, wb: torch.Tensor, y: torch.Tensor,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """csa_out_proj: o [T, H, D] (fp32 or bf16), wa bf16 [G, R, (H/G) D], wb bf16 [hidden, G R] -> y [T, hidden]."""
+    assert o.is_contiguous() and wa.is_contiguous() and wb.is_contiguous() and y.is_contiguous()
+    assert wa.dtype == torch.bfloat16 and wb.dtype == torch.bfloat16
+    T, H, D = o.shape
+    G, R, _ = wa.shape
+    hidden = wb.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().csa_out_proj(o.data_ptr(), _out_code(o), T, H, D, G, wa.data_ptr(), R, wb.data_ptr(), hidden,
+                             y.data_ptr(), _out_code(y), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("csa_out_proj", rc)
 
 
 def workspace(nbytes: int, device) -> Optional[torch.Tensor]:

@@ -430,6 +430,60 @@ int csa_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H, const 
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- output projection
+
+extern "C" {
+
+static size_t out_proj_z_bytes(int T, int G, int R) { return ((size_t)T * G * R * sizeof(float) + 255) / 256 * 256; }
+
+size_t csa_out_proj_workspace_bytes(int T, int G, int R, int hidden) {
+  if (T <= 0 || G <= 0 || R <= 0 || hidden <= 0) return 0;
+  return out_proj_z_bytes(T, G, R) + (size_t)csa::kOutSplit * T * hidden * sizeof(float);
+}
+
+int csa_out_proj(const void* o, int o_dtype, int T, int H, int D, int G, const void* wa, int R, const void* wb,
+                 int hidden, void* y, int y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  REQUIRE(T >= 0, CSA_EINVAL, "T must be >= 0 (got %d)", T);
+  if (T == 0) return ok();
+  REQUIRE(o && wa && wb && y, CSA_EINVAL, "o, wa, wb and y must be non-NULL");
+  REQUIRE(H >= 1 && D >= 1 && G >= 1 && R >= 1 && hidden >= 1, CSA_EINVAL,
+          "H, D, G, R and hidden must be >= 1 (got %d, %d, %d, %d, %d)", H, D, G, R, hidden);
+  REQUIRE(H % G == 0, CSA_EINVAL, "H (%d) must be a multiple of G (%d)", H, G);
+  const long long Kg = (long long)(H / G) * D;
+  REQUIRE(Kg % 32 == 0, CSA_ENOTSUP, "(H / G) * D must be a multiple of 32 (got %lld)", Kg);
+  REQUIRE(R % 64 == 0, CSA_ENOTSUP, "R must be a multiple of 64 (got %d)", R);
+  REQUIRE(hidden % 32 == 0, CSA_ENOTSUP, "hidden must be a multiple of 32 (got %d)", hidden);
+  REQUIRE((long long)G * R <= (1LL << 30) && Kg <= (1LL << 30), CSA_EINVAL, "factor shapes too large");
+  REQUIRE(o_dtype == CSA_FP32 || o_dtype == CSA_BF16, CSA_ENOTSUP, "o_dtype must be FP32 or BF16");
+  REQUIRE(y_dtype == CSA_FP32 || y_dtype == CSA_BF16, CSA_ENOTSUP, "y_dtype must be FP32 or BF16");
+  REQUIRE(aligned(o, 16) && aligned(wa, 16) && aligned(wb, 16) && aligned(y, 16), CSA_EINVAL,
+          "o, wa, wb and y must be 16-byte aligned");
+  const size_t need = csa_out_proj_workspace_bytes(T, G, R, hidden);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, CSA_EWORKSPACE, "workspace of %zu bytes needed (got %zu)",
+          need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), CSA_EINVAL, "workspace must be 256-byte aligned");
+  csa::OutProjArgs a{};
+  a.o = o;
+  a.o_dtype = o_dtype;
+  a.T = T;
+  a.H = H;
+  a.D = D;
+  a.G = G;
+  a.R = R;
+  a.hidden = hidden;
+  a.wa = wa;
+  a.wb = wb;
+  a.z = static_cast<float*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + out_proj_z_bytes(T, G, R));
+  a.y = y;
+  a.y_dtype = y_dtype;
+  const hipError_t e = csa::launch_out_proj(a, stream);
+  REQUIRE(e == hipSuccess, CSA_EHIP, "output projection launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
 // ---------------------------------------------------------------- csa_attend without a workspace
 //
 // The split partials of csa_attend_noalloc live in this array: one copy per GPU the library runs

@@ -83,6 +83,31 @@ struct AttendArgs {
   float* part_ml;         // [rows, nsplit, H, 4]: reference max, normaliser n, exact sum, e
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+// C = A B^T for the output projection: A element (m, k) of group g at A + g a_gstride + m lda + k
+// (fp32 or bf16 elements), B (bf16) rows of K contiguous elements, C fp32 or bf16
+struct GemmArgs {
+  const void* A;
+  int64_t lda, a_gstride;
+  const uint16_t* B;
+  int64_t ldb, b_gstride;
+  void* C;
+  int64_t ldc, c_gstride;
+  int M, N, K;
+  int ksplit;           // K ranges of equal length; > 1: C holds fp32 partials, range r at C + r p_stride
+  int64_t p_stride;
+};
+constexpr int kOutSplit = 4;   // K ranges of the output projection's second product
+struct OutProjArgs {
+  const void* o;      // [T, H, D], o_dtype CSA_FP32 or CSA_BF16
+  int o_dtype, T, H, D, G, R, hidden;
+  const void* wa;     // bf16 [G, R, (H / G) D]
+  const void* wb;     // bf16 [hidden, G R]
+  float* z;           // fp32 [T, G R] (workspace)
+  float* part;        // fp32 [kOutSplit, T, hidden] (workspace): the second product's partials
+  void* y;            // [T, hidden], y_dtype CSA_FP32 or CSA_BF16
+  int y_dtype;
+};
+hipError_t launch_out_proj(const OutProjArgs& a, hipStream_t s);
 // the plan's name for a cache storage code
 inline int att_kind(int dtype) { return dtype == CSA_FP8_E4M3 ? kAttFp8 : (dtype == CSA_FP4_E2M1 ? kAttFp4 : kAttBf16); }
 

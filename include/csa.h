@@ -297,6 +297,35 @@ int hca_attend(const void* q, const int64_t* q_pos, int B, int Tq, int H,
 
 size_t hca_attend_workspace_bytes(int B, int Tq, int H, int cap, int W);
 
+/*
+ * csa_out_proj — grouped low-rank output projection of the attention output.
+ *
+ * Source: "DeepSeek-V4-Pro" model atlas, Raw config fields o_groups (16), o_lora_rank (1024) and
+ * hidden_size (7168); the fields alone are given, and the plainest reading they support is taken:
+ * the H heads' outputs (after the inverse rotation, as csa_attend / hca_attend write them) form G
+ * groups of H / G consecutive heads; group g's (H / G) * D values go through its own down factor,
+ * the G * R codes, concatenated in group order, through one up factor:
+ *     z[t, g, r] = sum_k o[t, g (H / G) D + k] * wa[g, r, k]        (k < (H / G) D)
+ *     y[t, j]    = sum_{g, r} z[t, g, r] * wb[j, g R + r]
+ *
+ *   o          device [T, H, D], o_dtype CSA_FP32 or CSA_BF16 (16-byte aligned)
+ *   wa         device bf16 [G, R, (H / G) D] (each code's weights contiguous; 16-byte aligned)
+ *   wb         device bf16 [hidden, G R] (each output's weights contiguous; 16-byte aligned)
+ *   y          device [T, hidden], y_dtype CSA_FP32 or CSA_BF16 (16-byte aligned)
+ *   workspace  at least csa_out_proj_workspace_bytes(T, G, R, hidden) bytes (the fp32 codes z and
+ *              the second product's partial sums), 256-byte aligned; its contents need not be kept
+ *              between calls
+ * Products of fp32 inputs (o, and the codes z) enter as bf16 hi + lo parts (about 16 bits);
+ * sums are fp32 in a fixed order (results are deterministic).  Requires H a multiple of G,
+ * (H / G) D a multiple of 32, R a multiple of 64, hidden a multiple of 32 (CSA_ENOTSUP otherwise).
+ * T = 0 is a no-op.  Errors as for the other calls; nothing is launched on failure.
+ */
+int csa_out_proj(const void* o, int o_dtype, int T, int H, int D, int G,
+                 const void* wa, int R, const void* wb, int hidden,
+                 void* y, int y_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t csa_out_proj_workspace_bytes(int T, int G, int R, int hidden);
+
 /* Thread-local description of the last failure (empty string after success). */
 const char* csa_last_error(void);
 

@@ -209,3 +209,33 @@ def test_rotary_tables_agree_with_the_oracle():
                                O.yarn_inv_freq(160000.0, 64, 16.0, 65536), rtol=1e-14, atol=0)
     assert abs(rope.yarn_logit_scale(16.0) - O.yarn_logit_scale(16.0)) < 1e-15
     assert rope.yarn_logit_scale(1.0) == 1.0
+
+
+def out_proj(o=FAKE, o_dt=L.CSA_BF16, T=32, H=128, D=512, G=16, wa=FAKE, R=1024, wb=FAKE, hidden=7168, y=FAKE,
+             y_dt=L.CSA_FP32, ws=FAKE, ws_bytes=None):
+    lib = L.load()
+    if ws_bytes is None:
+        ws_bytes = lib.csa_out_proj_workspace_bytes(T, G, R, hidden)
+    return rc_msg(lib.csa_out_proj(o, o_dt, T, H, D, G, wa, R, wb, hidden, y, y_dt, ws, ws_bytes, None))
+
+
+def test_out_proj_validation():
+    lib = L.load()
+    assert lib.csa_out_proj_workspace_bytes(32, 16, 1024, 7168) == 32 * 16 * 1024 * 4 + 4 * 32 * 7168 * 4
+    assert lib.csa_out_proj_workspace_bytes(3, 2, 65, 32) == 1792 + 4 * 3 * 32 * 4   # codes: 1560 B, 256-aligned
+    assert lib.csa_out_proj_workspace_bytes(0, 16, 1024, 7168) == 0
+    assert out_proj(T=0, o=None) == (L.CSA_OK, "")                # nothing to do, nothing launched
+    assert out_proj(o=None)[0] == L.CSA_EINVAL
+    assert out_proj(wb=None)[0] == L.CSA_EINVAL
+    rc, msg = out_proj(G=12)
+    assert rc == L.CSA_EINVAL and "multiple of G" in msg           # 128 heads do not split in 12 groups
+    assert out_proj(D=6)[0] == L.CSA_ENOTSUP                      # (H / G) D = 48: not a multiple of 32
+    assert out_proj(R=1000)[0] == L.CSA_ENOTSUP
+    assert out_proj(hidden=7000)[0] == L.CSA_ENOTSUP
+    assert out_proj(o_dt=7)[0] == L.CSA_ENOTSUP
+    assert out_proj(y_dt=L.CSA_FP8_E4M3)[0] == L.CSA_ENOTSUP
+    assert out_proj(wa=FAKE + 8)[0] == L.CSA_EINVAL               # misaligned
+    assert out_proj(ws=None)[0] == L.CSA_EWORKSPACE
+    rc, msg = out_proj(ws_bytes=1024)
+    assert rc == L.CSA_EWORKSPACE and "5767168" in msg
+    assert out_proj(ws=FAKE + 64)[0] == L.CSA_EINVAL              # workspace not 256-byte aligned
