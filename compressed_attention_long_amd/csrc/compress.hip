@@ -5,6 +5,12 @@
 namespace csa {
 
 // grid: (ceil(n_new / run), B); block: groups of C/8 lanes, one run of rows per group.
+// MODE (a separate kernel each, so that each path gets its own register allocation):
+// kOverlapRegs, kOverlap (window = 2 stride, runs of rows walking the raw stream once; the
+// first keeps a block of tokens in registers ahead of the pooling), kPerRow (every row its own
+// window).
+enum { kOverlapRegs = 0, kOverlap = 1, kPerRow = 2 };
+template <int MODE>
 __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
   const int lanes = a.C / 8;
   const int groups = blockDim.x / lanes;
@@ -20,11 +26,11 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
   const uint16_t* lg = a.logits ? reinterpret_cast<const uint16_t*>(a.logits) + (int64_t)b * a.ld_seq
                                 : nullptr;
   const RopeIn ri = rope_in(a, b, c0);
-  if (a.window == 2 * a.stride && a.run > 1 && a.stride <= kB) {
+  if constexpr (MODE == kOverlapRegs) {
     // Overlapping rows: entry i = block i + block i+1 (blocks of `stride` tokens).  The
     // loads of block i + 2 are issued before block i + 1 is pooled.
     const int st = a.stride;
-    PoolState prev, cur, both;
+    PoolState prev, cur;
     RawBlock r0, r1;
     load_block(r0, kv, lg, a.ld_tok, first * st, st, c0);
     load_block(r1, kv, lg, a.ld_tok, (first + 1) * st, st, c0);
@@ -34,12 +40,12 @@ __global__ void __launch_bounds__(256) k_compress(CompressArgs a) {
       if (i + 1 < last) load_block(r0, kv, lg, a.ld_tok, (i + 2) * st, st, c0);
       pool_reset(cur);
       pool_regs(cur, r1, st);
-      pool_merge(both, prev, cur);
-      finish_row(both, a, rope_trig(a, ri, a.first_row + i, c0), b, a.first_row + i, c0);
+      pool_merge(prev, prev, cur);   // in place: element by element
+      finish_row(prev, a, rope_trig(a, ri, a.first_row + i, c0), b, a.first_row + i, c0);
       prev = cur;
       r1 = r0;
     }
-  } else if (a.window == 2 * a.stride && a.run > 1) {
+  } else if constexpr (MODE == kOverlap) {
     PoolState prev, cur, both;
     pool_reset(prev);
     pool_block(prev, kv, lg, a.ld_tok, first * a.stride, a.stride, c0);
@@ -85,7 +91,7 @@ hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   // long windows, or few rows (a decode step): the one-launch kernel with a single call
   if (batch_layout(a) >= 0) return launch_compress_batch(&a, 1, s);
   const int lanes = a.C / 8;
-  const int groups = 256 / lanes;
+  const int groups = max(128, lanes) / lanes;   // blocks of 128 lanes (measured faster than 256)
   // Long runs amortise the extra leading block of overlapping windows; short runs keep
   // enough blocks in flight for small calls.
   int run = 1;
@@ -96,7 +102,12 @@ hipError_t launch_compress(const CompressArgs& a0, hipStream_t s) {
   a.run = run;
   const int runs = (a.n_new + run - 1) / run;
   dim3 grid((runs + groups - 1) / groups, a.B);
-  hipLaunchKernelGGL(k_compress, grid, dim3(groups * lanes), 0, s, a);
+  if (a.window == 2 * a.stride && a.run > 1 && a.stride <= kB)
+    hipLaunchKernelGGL(k_compress<kOverlapRegs>, grid, dim3(groups * lanes), 0, s, a);
+  else if (a.window == 2 * a.stride && a.run > 1)
+    hipLaunchKernelGGL(k_compress<kOverlap>, grid, dim3(groups * lanes), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_compress<kPerRow>, grid, dim3(groups * lanes), 0, s, a);
   return hipGetLastError();
 }
 

