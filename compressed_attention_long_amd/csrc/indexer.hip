@@ -468,7 +468,7 @@ struct SelShared {
   alignas(16) int cidx[kCandMax + 4];
   alignas(16) uint8_t flag[T * NPT];         // selection flags by entry, for the ordered numbering
   int cnt[NPT * W];
-  uint32_t red[2 * W];
+  uint32_t red[3 * W];
   int ccount, bstar, above, bcnt, total;
   uint32_t TK;
   int I;
@@ -592,13 +592,29 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
       if (ok(i)) { klo = min(klo, key[i]); khi = max(khi, key[i]); }
+    // A lower bound of the k-th largest key: split the lanes into aligned groups of G lanes,
+    // G the largest power of two (<= 64) with G k <= T, so that there are at least k groups.
+    // Each group's largest key is a different entry, so at least k entries hold a key >= the
+    // smallest of those maxima, and keys below it can be left out of every round (a group
+    // without an entry has maximum 0: no bound).  For k > T there is no bound.
+    uint32_t lb = 0u;
+    if (k <= T) {
+      uint32_t gm = khi;   // this lane's largest key (0 without an entry)
+      for (int m = 1; m < 64 && 2 * m * k <= T; m <<= 1) gm = max(gm, (uint32_t)__shfl_xor((int)gm, m, 64));
+      lb = wave_reduce_u32<false>(gm);
+    }
     klo = wave_reduce_u32<false>(klo);
     khi = wave_reduce_u32<true>(khi);
-    if (lane == 0) { sh.red[wave] = klo; sh.red[W + wave] = khi; }
+    if (lane == 0) { sh.red[wave] = klo; sh.red[W + wave] = khi; sh.red[2 * W + wave] = lb; }
     for (int b = tid; b < kTopkBins + kTopkBins / 32; b += T) sh.hist[b] = 0;
     __syncthreads();
 #pragma unroll
-    for (int w2 = 0; w2 < W; ++w2) { klo = min(klo, sh.red[w2]); khi = max(khi, sh.red[W + w2]); }
+    for (int w2 = 0; w2 < W; ++w2) {
+      klo = min(klo, sh.red[w2]);
+      khi = max(khi, sh.red[W + w2]);
+      lb = min(lb, sh.red[2 * W + w2]);
+    }
+    klo = max(klo, lb);
     int above = 0, cnt = 0;
     for (int round = 0; round < 3 && klo < khi; ++round) {
       const uint32_t range = khi - klo;
@@ -707,14 +723,18 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
   return sel_ranks_contig<T, NPT>(sh, f, emit);
 }
 
-// Scores of entries j < n starting at s, read once with coalesced loads (index clamped into
-// the range; entries past n get key 0).
+// Scores of entries j < lim starting at s, read once with coalesced loads (index clamped
+// into the range).  The loads go out before the visible count is known (lim is the row's
+// allocation), so their latency overlaps that of the count's inputs.
 template <int T, int NPT>
-__device__ __forceinline__ void load_score_keys(const float* s, int n, uint32_t (&key)[NPT]) {
-  const int last = max(n - 1, 0);
-  float v[NPT];
+__device__ __forceinline__ void load_scores(const float* s, int lim, float (&v)[NPT]) {
+  const int last = max(lim - 1, 0);
 #pragma unroll
   for (int i = 0; i < NPT; ++i) v[i] = s[min(i * T + (int)threadIdx.x, last)];
+}
+// their keys, entries j >= n (not visible) key 0
+template <int T, int NPT>
+__device__ __forceinline__ void score_keys(const float (&v)[NPT], int n, uint32_t (&key)[NPT]) {
 #pragma unroll
   for (int i = 0; i < NPT; ++i) key[i] = i * T + (int)threadIdx.x < n ? okey(v[i]) : 0u;
 }
@@ -726,10 +746,12 @@ __global__ void __launch_bounds__(T) k_topk_reg(IndexArgs a) {
   const int row = blockIdx.x;
   const int b = row / a.Tq;
   const int k = a.topk;
+  float v[NPT];
+  load_scores<T, NPT>(a.scores + (int64_t)row * a.cap, min(a.cap, T * NPT), v);   // cap <= T NPT here
   const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   int32_t* out = a.idx_out + (int64_t)row * k;
   uint32_t key[NPT];
-  load_score_keys<T, NPT>(a.scores + (int64_t)row * a.cap, nvis, key);
+  score_keys<T, NPT>(v, nvis, key);
   const int tot = select_keys<T, NPT>(sh, key, nvis, k, [&](int j, int pos) {
     if (pos < k) out[pos] = j;
   });
@@ -747,11 +769,13 @@ __global__ void __launch_bounds__(T) k_topk_chunk(IndexArgs a) {
   const int row = blockIdx.x, pch = blockIdx.y, P = gridDim.y;
   const int b = row / a.Tq;
   const int k = a.topk;
-  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   const int base = pch * a.chunk;
+  float v[NPT];
+  load_scores<T, NPT>(a.scores + (int64_t)row * a.cap + base, min(a.cap - base, a.chunk), v);
+  const int nvis = visible_rows(a.q_pos[row], a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   const int n = min(max(nvis - base, 0), a.chunk);
   uint32_t key[NPT];
-  load_score_keys<T, NPT>(a.scores + (int64_t)row * a.cap + base, n, key);
+  score_keys<T, NPT>(v, n, key);
   const int64_t slot0 = ((int64_t)row * P + pch) * k;
   const float* srow = a.scores + (int64_t)row * a.cap + base;
   const int tot = select_keys<T, NPT>(sh, key, n, k, [&](int j, int pos) {
