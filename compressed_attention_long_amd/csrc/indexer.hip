@@ -457,23 +457,34 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Shared state of one selection by a block of T lanes holding NPT keys each.  The histogram
-// has one padding word per 32 bins so that wave 0 can read 32 consecutive bins per lane
-// without bank conflicts.
+// f(Ic<I>{}) for I = B .. E - 1, each I a compile-time constant
+template <int V>
+struct Ic {
+  static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Shared state of one selection by a block of T lanes holding NPT keys each.
 template <int T, int NPT>
 struct SelShared {
   static constexpr int W = T / 64;
-  uint32_t hist[kTopkBins + kTopkBins / 32];
+  alignas(16) uint32_t hist[kTopkBins];
   alignas(16) uint32_t ckey[kCandMax + 4];   // + 4: padding for 16-byte reads of the tail
   alignas(16) int cidx[kCandMax + 4];
-  alignas(16) uint8_t flag[T * NPT];         // selection flags by entry, for the ordered numbering
+  alignas(16) uint8_t flag[64 % NPT == 0 ? 16 : T * NPT];   // selection flags by entry (byte path)
+  uint64_t flagw[64 % NPT == 0 ? NPT * (T / 64) : 1];        // the same as the waves' ballots
   int cnt[NPT * W];
   uint32_t red[3 * W];
   int ccount, bstar, above, bcnt, total;
   uint32_t TK;
   int I;
 };
-__device__ __forceinline__ int hslot(int b) { return b + (b >> 5); }
 
 // Number the flagged entries (i, t) -- entry j = i * T + t, flag = bit i of `bits` -- in
 // ascending j: per-(i, wave) counts, one in-order exclusive scan of them by wave 0, then each
@@ -520,23 +531,45 @@ __device__ __forceinline__ int sel_ranks(SelShared<T, NPT>& sh, uint64_t bits, E
   return sh.total;
 }
 
-// The same numbering through LDS, thread-contiguous: the flags are stored by entry, thread t
-// reads back entries [t NPT, (t + 1) NPT) (one 16-byte read per 16 entries), the per-thread
-// counts are scanned across the block (a wave scan plus the wave totals), and each thread
-// numbers its own entries in order: emit(j, number) with j the entry.  Two barriers and no
-// per-index ballot rounds.  Returns the total.
-template <int T, int NPT, class Emit>
-__device__ __forceinline__ int sel_ranks_contig(SelShared<T, NPT>& sh, uint64_t bits, Emit&& emit) {
+// The same numbering through LDS, thread-contiguous, of the selected entries (sel(i): the wave's
+// lane mask of its entries i * T + t that are selected): the flags go to LDS, thread t reads back
+// those of entries [t NPT, (t + 1) NPT), the per-thread counts are scanned across the block (a
+// wave scan plus the wave totals), and each thread numbers its own entries in order:
+// emit(j, number) with j the entry.  Two barriers and no per-index ballot rounds.  Returns the
+// total.  When NPT divides 64 the flags are the waves' ballots, one 64-bit word per (index i,
+// wave): entries [t NPT, (t + 1) NPT) are NPT consecutive bits of one word.  Otherwise they are
+// stored as one byte per entry and read back 4 or 16 at a time.
+template <int T, int NPT, class Sel, class Emit>
+__device__ __forceinline__ int sel_ranks_contig(SelShared<T, NPT>& sh, Sel&& sel, Emit&& emit) {
   constexpr int W = T / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int i = 0; i < NPT; ++i) sh.flag[i * T + tid] = (uint8_t)((bits >> i) & 1u);
-  __syncthreads();
   uint64_t m = 0;
   auto take4 = [](uint32_t w) -> uint32_t {   // four 0/1 bytes -> four bits
     return (w & 1u) | ((w >> 7) & 2u) | ((w >> 14) & 4u) | ((w >> 21) & 8u);
   };
-  if constexpr (NPT % 16 == 0) {
+  if constexpr (64 % NPT == 0) {
+    uint32_t mlo = 0u, mhi = 0u;   // lane i < NPT: the wave's ballot of index i
+    static_for<0, NPT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const uint64_t bl = sel(i);
+      // v_writelane: the wave-uniform word into lane i (a lane-select compare and two
+      // conditional moves per index otherwise); the lane is an inline constant
+      uint32_t lo = mlo, hi = mhi;
+      asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(lo) : "s"((uint32_t)bl), "i"(i));
+      asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(hi) : "s"((uint32_t)(bl >> 32)), "i"(i));
+      mlo = lo;
+      mhi = hi;
+    });
+    if (lane < NPT) sh.flagw[lane * W + wave] = ((uint64_t)mhi << 32) | mlo;
+    __syncthreads();
+    const int j0 = tid * NPT;             // entry j0 = i T + t0: lanes t0 .. t0 + NPT - 1 of index i
+    const int t0 = j0 % T;
+    const uint64_t wd = sh.flagw[(j0 / T) * W + (t0 >> 6)];
+    m = NPT == 64 ? wd : (wd >> (t0 & 63)) & ((1ull << (NPT & 63)) - 1ull);
+  } else if constexpr (NPT % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) sh.flag[i * T + tid] = (uint8_t)((sel(i) >> lane) & 1u);
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < NPT / 16; ++q) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(&sh.flag[tid * NPT + 16 * q]);
@@ -544,6 +577,9 @@ __device__ __forceinline__ int sel_ranks_contig(SelShared<T, NPT>& sh, uint64_t 
       for (int e = 0; e < 4; ++e) m |= (uint64_t)take4(w[e]) << (16 * q + 4 * e);
     }
   } else {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) sh.flag[i * T + tid] = (uint8_t)((sel(i) >> lane) & 1u);
+    __syncthreads();
 #pragma unroll
     for (int q = 0; q < NPT / 4; ++q)
       m |= (uint64_t)take4(*reinterpret_cast<const uint32_t*>(&sh.flag[tid * NPT + 4 * q])) << (4 * q);
@@ -606,7 +642,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
     klo = wave_reduce_u32<false>(klo);
     khi = wave_reduce_u32<true>(khi);
     if (lane == 0) { sh.red[wave] = klo; sh.red[W + wave] = khi; sh.red[2 * W + wave] = lb; }
-    for (int b = tid; b < kTopkBins + kTopkBins / 32; b += T) sh.hist[b] = 0;
+    for (int b = tid; b < kTopkBins; b += T) sh.hist[b] = 0;
     __syncthreads();
 #pragma unroll
     for (int w2 = 0; w2 < W; ++w2) {
@@ -619,9 +655,12 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
     for (int round = 0; round < 3 && klo < khi; ++round) {
       const uint32_t range = khi - klo;
       const int shift = max(0, 32 - __clz((int)range) - 11);
+      // keys in [klo, khi] (klo > 0: no entry's key 0 is in range), as one unsigned compare
 #pragma unroll
-      for (int i = 0; i < NPT; ++i)
-        if (ok(i) && key[i] >= klo && key[i] <= khi) atomicAdd(&sh.hist[hslot((key[i] - klo) >> shift)], 1u);
+      for (int i = 0; i < NPT; ++i) {
+        const uint32_t d = key[i] - klo;
+        if (d <= range) atomicAdd(&sh.hist[d >> shift], 1u);
+      }
       __syncthreads();
       {
         // thread t owns bins 2047 - BPT t - e (e < BPT): the bins in descending key order.
@@ -630,13 +669,13 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
         int c[BPT], sum = 0;
 #pragma unroll
         for (int e = 0; e < BPT; ++e) {
-          c[e] = (int)sh.hist[hslot(kTopkBins - 1 - (BPT * tid + e))];
+          c[e] = (int)sh.hist[kTopkBins - 1 - (BPT * tid + e)];
           sum += c[e];
         }
         const int incl = wave_incl_scan(sum);
         if (lane == 63) sh.red[wave] = (uint32_t)incl;   // the min/max scratch is free by now
 #pragma unroll
-        for (int e = 0; e < BPT; ++e) sh.hist[hslot(kTopkBins - 1 - (BPT * tid + e))] = 0;   // next round
+        for (int e = 0; e < BPT; ++e) sh.hist[kTopkBins - 1 - (BPT * tid + e)] = 0;   // next round
         __syncthreads();
         if (tid == 0) sh.ccount = 0;   // for the candidate collection below; unused within rounds
         int pre = incl - sum;
@@ -683,7 +722,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
       // the last histogram round, between its barriers.
 #pragma unroll
       for (int i = 0; i < NPT; ++i) {
-        const bool c = ok(i) && key[i] >= klo && key[i] <= khi;
+        const bool c = key[i] - klo <= khi - klo;   // klo > 0: keys of entries only
         const uint64_t m = __ballot(c);
         if (m == 0) continue;
         int base = 0;
@@ -715,12 +754,15 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
       I = sh.I;
     }
   }
-  // ascending compaction: selected entries numbered in index order
-  uint64_t f = 0;
-#pragma unroll
-  for (int i = 0; i < NPT; ++i)
-    f |= (uint64_t)(ok(i) && (take_all || key[i] > TK || (key[i] == TK && jof(i) <= I))) << i;
-  return sel_ranks_contig<T, NPT>(sh, f, emit);
+  // ascending compaction: selected entries numbered in index order.  The test is taken on the
+  // compares' lane masks, without branches (every vector operation per key here costs the block
+  // a wave instruction per 64 keys).
+  if (take_all) { TK = 0u; I = -1; }   // then key > 0, i.e. every entry, is selected
+  auto sel = [&](int i) -> uint64_t {
+    return __builtin_amdgcn_ballot_w64(key[i] > TK) |
+           (__builtin_amdgcn_ballot_w64(key[i] == TK) & __builtin_amdgcn_ballot_w64(jof(i) <= I));
+  };
+  return sel_ranks_contig<T, NPT>(sh, sel, emit);
 }
 
 // Scores of entries j < lim starting at s, read once with coalesced loads (index clamped
