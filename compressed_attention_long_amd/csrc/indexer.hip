@@ -415,8 +415,9 @@ constexpr int kCandMax = 512;
 
 // Order-preserving map of fp32 bit patterns onto uint32.
 __device__ __forceinline__ uint32_t okey(float v) {
-  uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(v);
+  // negative: all bits flipped; otherwise the sign bit set (branch-free: three operations)
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // The selection holds a row (or a chunk of one) in registers, read once with coalesced loads:
@@ -627,7 +628,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
     uint32_t klo = 0xffffffffu, khi = 0u;
 #pragma unroll
     for (int i = 0; i < NPT; ++i)
-      if (ok(i)) { klo = min(klo, key[i]); khi = max(khi, key[i]); }
+      { klo = min(klo, key[i] - 1u); khi = max(khi, key[i]); }   // key 0 (no entry): -1 wraps to the top
     // A lower bound of the k-th largest key: split the lanes into aligned groups of G lanes,
     // G the largest power of two (<= 64) with G k <= T, so that there are at least k groups.
     // Each group's largest key is a different entry, so at least k entries hold a key >= the
@@ -650,7 +651,7 @@ __device__ __forceinline__ int select_keys(SelShared<T, NPT>& sh, const uint32_t
       khi = max(khi, sh.red[W + w2]);
       lb = min(lb, sh.red[2 * W + w2]);
     }
-    klo = max(klo, lb);
+    klo = max(klo + 1u, lb);   // the smallest key (see the minimum above)
     int above = 0, cnt = 0;
     for (int round = 0; round < 3 && klo < khi; ++round) {
       const uint32_t range = khi - klo;
