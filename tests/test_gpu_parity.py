@@ -16,7 +16,7 @@ from compressed_attention_long_amd import _lib as ops
 from compressed_attention_long_amd.rope import rope_inv_freq, yarn_inv_freq
 from oracle import csa_oracle as O
 
-from gpu_common import (check_attention, check_bf16_rows, check_fp4_rows, check_fp8_rows, check_lse, check_scores,
+from gpu_common import (ATT_TOL, LSE_TOL, check_attention, check_bf16_rows, check_fp4_rows, check_fp8_rows, check_lse, check_scores,
                         check_topk, lse_tolerance, np64, oracle_rows_csa, oracle_rows_hca, pool_error_bound,
                         score_error_bound, stored_rows)
 
@@ -444,6 +444,69 @@ def test_attend_workspace_reused_across_calls():
         ref = call(n, ops.workspace(ops.csa_attend_workspace_bytes(n, 1, H, topk, W), DEV))
         torch.cuda.synchronize()
         assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"{n} rows"
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_attend_same_row_across_split_plans(mode):
+    """One query row attended alone and as each row of a 32-row batch of its copies.  The plans
+    differ: alone, the row set is cut into many short splits of 32-head blocks (36 for CSA);
+    in the batch, into a few long splits of 64-head blocks (4).  Both match the oracle, they agree
+    with each other to the same bar, and the batch's copies are equal bit for bit."""
+    B, H, W = 32, 128, 128
+    csa = mode == "csa"
+    cap, topk = (4000, 1024) if csa else (1200, 0)
+    window, stride = (8, 4) if csa else (128, 128)
+    d = ci.Draw(17, "cpu")
+    q1 = d.normal((1, 1, H, 512), std=2 / math.sqrt(512))
+    sink = d.normal((H,), dtype=torch.float32)
+    kv1 = d.normal((1, cap, 512))
+    win1 = d.normal((1, W, 512))
+    qp = (cap - 1) * stride + window           # every entry visible (pos0 0)
+    idx1 = None
+    if csa:
+        rng = np.random.default_rng(17)
+        idx1 = torch.from_numpy(np.sort(rng.choice(cap, topk, replace=False)).astype(np.int32).reshape(1, 1, topk))
+    fg, fo = inv_freq_pair(64)
+    scale = 1 / math.sqrt(512)
+
+    def call(n):
+        rep = lambda x: x.expand(n, *x.shape[1:]).contiguous().to(DEV)
+        kv = ops.Cache(rep(kv1), torch.full((n,), cap, dtype=torch.int32, device=DEV),
+                       torch.zeros(n, dtype=torch.int64, device=DEV), window, stride)
+        win = ops.Cache(rep(win1), torch.full((n,), W, dtype=torch.int32, device=DEV),
+                        torch.full((n,), qp - W + 1, dtype=torch.int64, device=DEV), 1, 1)
+        q_pos = torch.full((n, 1), qp, dtype=torch.int64, device=DEV)
+        out = torch.empty((n, 1, H, 512), dtype=torch.float32, device=DEV)
+        lse = torch.empty((n, 1, H), dtype=torch.float32, device=DEV)
+        if csa:
+            ws = ops.workspace(ops.csa_attend_workspace_bytes(n, 1, H, topk, W), DEV)
+            ops.csa_attend(rep(q1), q_pos, kv, rep(idx1), win, W, sink.to(DEV), fg, 64, scale, out, lse, ws)
+        else:
+            ws = ops.workspace(ops.hca_attend_workspace_bytes(n, 1, H, cap, W), DEV)
+            ops.hca_attend(rep(q1), q_pos, kv, win, W, sink.to(DEV), fg, 64, scale, out, lse, ws)
+        torch.cuda.synchronize()
+        return np64(out), lse.cpu().numpy()
+
+    print(f"case {mode} one row vs {B} copies", flush=True)
+    o1, l1 = call(1)
+    oB, lB = call(B)
+    for b in range(1, B):
+        assert np.array_equal(oB[b], oB[0]) and np.array_equal(lB[b], lB[0]), f"copy {b} differs"
+    wpos = qp - W + 1 + np.arange(W)
+    if csa:
+        X = oracle_rows_csa(np64(kv1[0]), idx1.numpy()[0, 0], np64(win1[0]), wpos, qp, W, cap)
+    else:
+        ent_pos = O.entry_positions(0, cap, window, stride)
+        X = oracle_rows_hca(np64(kv1[0]), ent_pos, np64(win1[0]), wpos, qp, W)
+    o_ora, l_ora = O.attend(np64(q1[0, 0]), qp, X, np64(sink), scale, fo)
+    check_attention(o1[0, 0], o_ora, "one row")
+    check_attention(oB[0, 0], o_ora, "batch row")
+    # the plans round different weights to bf16 (each split has its own reference maximum), so
+    # the two outputs are held to the oracle's bar between them; lse uses the exact fp32 sums
+    rms = float(np.sqrt((o_ora ** 2).mean()))
+    diff = float(np.abs(o1 - oB[:1]).max())
+    assert diff <= ATT_TOL * rms, f"plans differ by {diff / rms:.2e} x RMS"
+    assert float(np.abs(l1 - lB[:1]).max()) <= LSE_TOL
 
 
 # ---------------------------------------------------------------- tiny decode from raw tokens
