@@ -61,23 +61,34 @@ constexpr int kIdxWaves = 4;             // waves per block of the fused scores 
 // at most kDeepRingBlocks blocks (about one per CU, so each wave must keep more loads in flight:
 // 65K decode fused call 32.8 -> 32.1 us), else 4 (grids of 512 and more, as at 1M, lose with 8).
 constexpr int kDeepRingBlocks = 256;
-constexpr int kIdxEntPerBlock = kIdxBlockTiles * 16;
 
-// One block of the decode scores grid: query row `row` (b * Tq + t), entries from
-// chunk * kIdxEntPerBlock.
-template <int HB, bool FP8, int DEPTH, int NW>
-__device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, int chunk) {
-  constexpr int kIdxTilesPerWave = kIdxBlockTiles / NW;
+// Tiles of 16 entries in a decode scores block's chunk: 128 for one query row per block; 64 when
+// a block holds a sequence's 2 or 4 rows (each wave then scores a whole row's share of the chunk,
+// and twice the blocks run two per CU).
+constexpr int scores_chunk_tiles(int tq) { return tq == 1 ? kIdxBlockTiles : kIdxBlockTiles / 2; }
+
+// One block of the decode scores grid: entries from chunk * 16 scores_chunk_tiles(TQ) for TQ query rows
+// row0 .. row0 + TQ - 1.  TQ = 1: the block's waves split the chunk for one row.  TQ = Tq > 1
+// (several query tokens per sequence): the block holds all of a sequence's rows, NW / TQ waves
+// per row, so its waves read the same key tiles at about the same time and the keys cross
+// from memory once per sequence instead of once per row (the other waves' loads hit the cache).
+template <int HB, bool FP8, int DEPTH, int NW, int TQ = 1>
+__device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row0, int chunk) {
+  static_assert(NW % TQ == 0, "whole waves per row");
+  constexpr int WPR = NW / TQ;                               // waves per row
+  constexpr int CT = scores_chunk_tiles(TQ);                 // tiles of the block's chunk
+  constexpr int kIdxTilesPerWave = CT / WPR;
   static_assert(kIdxTilesPerWave % DEPTH == 0, "whole ring rounds stay inside a wave's tiles");
   __shared__ float sbuf[NW][kIdxTilesPerWave * 16];
-  const int b = row / a.Tq;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, in an SGPR
+  const int row = row0 + wave / WPR;
+  const int b = row / a.Tq;
   const int n = lane & 15, g = lane >> 4;
   const int64_t qp = a.q_pos[row];
   const int nvis = visible_rows(qp, a.pos0[b], a.window, a.stride, a.n_valid[b], a.cap);
   float* srow = a.scores + (int64_t)row * a.cap;
-  const int base = chunk * kIdxEntPerBlock + wave * (kIdxTilesPerWave * 16);
+  const int base = chunk * (CT * 16) + (wave % WPR) * (kIdxTilesPerWave * 16);
 
   // query fragments: A operand, row = head (hb*16 + n), k = 8g + i <-> channel 32g + 8s + i
   bf16x8 qf[HB][4];
@@ -203,22 +214,27 @@ __device__ __forceinline__ void index_scores_block(const IndexArgs& a, int row, 
   }
 }
 
-template <int HB, bool FP8, int DEPTH, int NW>
+// grid (rows / TQ, chunks): block x takes rows TQ x .. TQ x + TQ - 1
+template <int HB, bool FP8, int DEPTH, int NW, int TQ>
 __global__ void __launch_bounds__(64 * NW) k_index_scores(IndexArgs a) {
-  index_scores_block<HB, FP8, DEPTH, NW>(a, blockIdx.x, blockIdx.y);
+  index_scores_block<HB, FP8, DEPTH, NW, TQ>(a, TQ * blockIdx.x, blockIdx.y);
 }
 
 // The same grid with a decode step's compress blocks after it (csa_index_topk_compress): the
 // compressor writes only the KV and window caches, which the scores do not read, so its
 // short, latency-bound blocks run beside the scores blocks instead of in a launch of their
 // own.  Blocks [0, n_idx) are the scores grid in launch order (row fastest).
-template <int HB, bool FP8, int DEPTH>
+template <int HB, bool FP8, int DEPTH, int TQ>
 __global__ void __launch_bounds__(256) k_index_scores_compress(IndexArgs a, CompressBatch cb, int n_idx) {
   const int L = blockIdx.x;
-  const int rows = a.B * a.Tq;
-  if (L < n_idx) index_scores_block<HB, FP8, DEPTH, kIdxWaves>(a, L % rows, L / rows);
+  const int units = a.B * a.Tq / TQ;
+  if (L < n_idx) index_scores_block<HB, FP8, DEPTH, kIdxWaves, TQ>(a, TQ * (L % units), L / units);
   else compress_batch_block(cb, L - n_idx);
 }
+
+// Query rows per scores block: a sequence's Tq rows when Tq is 2 or 4 (whole waves per row),
+// else one.
+static inline int scores_rows_per_block(int Tq) { return (Tq == 2 || Tq == 4) ? Tq : 1; }
 
 // ---------------------------------------------------------------- scores, many query rows
 
@@ -351,20 +367,21 @@ __global__ void __launch_bounds__(kMqWaves * 64, 1) k_index_scores_mq(IndexArgs 
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   const int rows = a.B * a.Tq;
-  dim3 grid(rows, (a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
+  const int tq = scores_rows_per_block(a.Tq);
+  const int cent = 16 * scores_chunk_tiles(tq);
+  dim3 grid(rows / tq, (a.cap + cent - 1) / cent);
   const int HB = (a.Hi + 15) / 16;
   const bool f8 = a.key_dtype == CSA_FP8_E4M3;
   const bool deep = (long long)grid.x * grid.y <= kDeepRingBlocks;
-#ifndef CSA_IDX_DEEP_WAVES
-#define CSA_IDX_DEEP_WAVES 4   // 8 waves (two per SIMD at one block per CU) measured slower: 17.9 against 16.7 us at 65K
-#endif
-#define CSA_IDX_LAUNCH(hb)                                                                     \
-  if (HB == hb) {                                                                              \
-    if (f8 && deep) hipLaunchKernelGGL((k_index_scores<hb, true, 8, CSA_IDX_DEEP_WAVES>), grid, dim3(64 * CSA_IDX_DEEP_WAVES), 0, s, a); \
-    else if (f8) hipLaunchKernelGGL((k_index_scores<hb, true, 4, kIdxWaves>), grid, dim3(256), 0, s, a);   \
-    else if (deep) hipLaunchKernelGGL((k_index_scores<hb, false, 8, CSA_IDX_DEEP_WAVES>), grid, dim3(64 * CSA_IDX_DEEP_WAVES), 0, s, a); \
-    else hipLaunchKernelGGL((k_index_scores<hb, false, 4, kIdxWaves>), grid, dim3(256), 0, s, a);          \
+  // 8 waves (two per SIMD at one block per CU) measured slower: 17.9 against 16.7 us at 65K
+#define CSA_IDX_LAUNCH_TQ(hb, TQ)                                                                              \
+  if (HB == hb && tq == TQ) {                                                                                 \
+    if (f8 && deep) hipLaunchKernelGGL((k_index_scores<hb, true, 8, kIdxWaves, TQ>), grid, dim3(256), 0, s, a); \
+    else if (f8) hipLaunchKernelGGL((k_index_scores<hb, true, 4, kIdxWaves, TQ>), grid, dim3(256), 0, s, a);    \
+    else if (deep) hipLaunchKernelGGL((k_index_scores<hb, false, 8, kIdxWaves, TQ>), grid, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((k_index_scores<hb, false, 4, kIdxWaves, TQ>), grid, dim3(256), 0, s, a);          \
   }
+#define CSA_IDX_LAUNCH(hb) CSA_IDX_LAUNCH_TQ(hb, 1) CSA_IDX_LAUNCH_TQ(hb, 2) CSA_IDX_LAUNCH_TQ(hb, 4)
   if (!f8 && a.Tq >= kMqRows && a.Di == 128) {
     const dim3 gmq(a.B * ((a.Tq + kMqRows - 1) / kMqRows));
 #define CSA_IDX_MQ(hb) \
@@ -375,6 +392,7 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t s) {
   }
   CSA_IDX_LAUNCH(1) CSA_IDX_LAUNCH(2) CSA_IDX_LAUNCH(3) CSA_IDX_LAUNCH(4)
 #undef CSA_IDX_LAUNCH
+#undef CSA_IDX_LAUNCH_TQ
   return hipGetLastError();
 }
 
@@ -392,18 +410,22 @@ hipError_t launch_index_scores_compress(const IndexArgs& a, const CompressArgs* 
     }
     return launch_index_scores(a, s);
   }
-  const long long n_idx = (long long)rows * ((a.cap + kIdxEntPerBlock - 1) / kIdxEntPerBlock);
+  const int tq = scores_rows_per_block(a.Tq);
+  const int cent = 16 * scores_chunk_tiles(tq);
+  const long long n_idx = (long long)(rows / tq) * ((a.cap + cent - 1) / cent);
   const dim3 grid((unsigned)(n_idx + total));
   const bool deep = n_idx <= kDeepRingBlocks;
-#define CSA_IDX_FUSED(hb)                                                                                           \
-  if (HB == hb) {                                                                                                   \
-    if (f8 && deep) hipLaunchKernelGGL((k_index_scores_compress<hb, true, 8>), grid, dim3(256), 0, s, a, cb, (int)n_idx); \
-    else if (f8) hipLaunchKernelGGL((k_index_scores_compress<hb, true, 4>), grid, dim3(256), 0, s, a, cb, (int)n_idx);    \
-    else if (deep) hipLaunchKernelGGL((k_index_scores_compress<hb, false, 8>), grid, dim3(256), 0, s, a, cb, (int)n_idx); \
-    else hipLaunchKernelGGL((k_index_scores_compress<hb, false, 4>), grid, dim3(256), 0, s, a, cb, (int)n_idx);          \
+#define CSA_IDX_FUSED_TQ(hb, TQ)                                                                                        \
+  if (HB == hb && tq == TQ) {                                                                                         \
+    if (f8 && deep) hipLaunchKernelGGL((k_index_scores_compress<hb, true, 8, TQ>), grid, dim3(256), 0, s, a, cb, (int)n_idx); \
+    else if (f8) hipLaunchKernelGGL((k_index_scores_compress<hb, true, 4, TQ>), grid, dim3(256), 0, s, a, cb, (int)n_idx);    \
+    else if (deep) hipLaunchKernelGGL((k_index_scores_compress<hb, false, 8, TQ>), grid, dim3(256), 0, s, a, cb, (int)n_idx); \
+    else hipLaunchKernelGGL((k_index_scores_compress<hb, false, 4, TQ>), grid, dim3(256), 0, s, a, cb, (int)n_idx);          \
   }
+#define CSA_IDX_FUSED(hb) CSA_IDX_FUSED_TQ(hb, 1) CSA_IDX_FUSED_TQ(hb, 2) CSA_IDX_FUSED_TQ(hb, 4)
   CSA_IDX_FUSED(1) CSA_IDX_FUSED(2) CSA_IDX_FUSED(3) CSA_IDX_FUSED(4)
 #undef CSA_IDX_FUSED
+#undef CSA_IDX_FUSED_TQ
   return hipGetLastError();
 }
 
