@@ -940,6 +940,8 @@ hipError_t launch_topk(const IndexArgs& a0, hipStream_t s) {
     else if (a.cap <= 16384)
       hipLaunchKernelGGL((k_topk_reg<CSA_TOPK16K_T, 16384 / CSA_TOPK16K_T>), grid, dim3(CSA_TOPK16K_T), 0, s, a);
     else if (a.cap <= 32768) hipLaunchKernelGGL((k_topk_reg<1024, 32>), grid, dim3(1024), 0, s, a);
+    // a 131K-token prefix plus a 4,096-token chunk: 33,791 entries
+    else if (a.cap <= 36864) hipLaunchKernelGGL((k_topk_reg<1024, 36>), grid, dim3(1024), 0, s, a);
     else if (a.cap <= 49152) hipLaunchKernelGGL((k_topk_reg<1024, 48>), grid, dim3(1024), 0, s, a);
     else hipLaunchKernelGGL((k_topk_reg<1024, 64>), grid, dim3(1024), 0, s, a);
     return hipGetLastError();

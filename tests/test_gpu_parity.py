@@ -181,6 +181,7 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (1, 16, 40, 1300, [1290], False, 64, "causal"),            # multi-row kernel, heads not a multiple of 16
     (1, 1, 64, 140000, [140000], True, 512, "end"),            # CSA2 selection: top-512 of a long row (chunked)
     (1, 128, 4, 40000, [40000], True, 256, "end"),             # 128 rows, one block each: 48 entries per lane
+    (1, 128, 4, 34000, [33900], True, 1024, "causal"),         # 128 rows, one block each: 36 entries per lane
     (1, 128, 4, 60000, [59000], False, 512, "end"),            # 128 rows, one block each: 64 entries per lane
     # a sequence's 2 or 4 query rows in one scores block (one key pass per sequence)
     (3, 4, 64, 20000, [20000, 19990, 7], True, 1024, "end"),   # 4 rows per block, fp8, two-stage, < k visible
