@@ -44,8 +44,9 @@ def kv_row_bytes(wl):
 def algorithmic_costs(wl):
     """Bytes / flops each C-ABI call of one step must move / do at minimum.
 
-    indexer: each visible key once (Di bytes fp8 + 4-byte scale, or 2*Di bf16), the
-             indexer queries and weights, the selected indices.
+    indexer: each visible key once per sequence (Di bytes fp8 + 4-byte scale, or 2*Di bf16;
+             a sequence's query tokens all score the same keys), the indexer queries and
+             weights, the selected indices.
     attend:  each attended row once per query token (1 KB bf16, 512 B + 32 B scales fp8,
              256 B + 64 B scales fp4; window rows bf16), q in (bf16) and out (bf16); flops
              4 * H * rows * 512 per token.
@@ -57,7 +58,7 @@ def algorithmic_costs(wl):
     kv_row_b = kv_row_bytes(wl)
     c = {}
     if wl.mode == "csa":
-        c["index_bytes"] = rows * (E * key_b + wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4)
+        c["index_bytes"] = wl.B * E * key_b + rows * (wl.Hi * wl.Di * 2 + wl.Hi * 4 + wl.topk * 4)
         c["index_flops"] = rows * E * wl.Hi * wl.Di * 2
         ent_rows = wl.topk
     else:
@@ -649,14 +650,15 @@ def main():
             d["TFLOP_per_s"] = costs[f"{name}_flops"] / (t_ms * 1e-3) / 1e12
             d["mfma_frac"] = d["TFLOP_per_s"] / BF16_PEAK_TFLOPS
         calls[name] = d
-    # dominant call of the step.  Attention (and a prefill chunk's indexer) is a dense contraction:
-    # its roofline is bf16 MFMA; the decode indexer and the compressor stream HBM.
+    # dominant call of the step.  Attention (and the indexer of several query tokens per sequence,
+    # whose keys cross HBM once per sequence) is a dense contraction: its roofline is bf16 MFMA;
+    # the one-token decode indexer and the compressor stream HBM.
     dom = max((k for k in calls if k != "index_compress"), key=lambda k: calls[k]["ms"])
     ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if dom == "attend" or (dom == "index" and wl.Tq >= 16):
+    if dom == "attend" or (dom == "index" and wl.Tq > 1):
         att_k = "k_attend_grp" if wl.kv_dtype == "bf16" else "k_attend"
         kern = (f"{'csa_attend' if wl.mode == 'csa' else 'hca_attend'} ({att_k} + k_attend_combine)" if dom == "attend"
-                else "csa_index_topk (k_index_scores_mq + top-k)")
+                else f"csa_index_topk ({'k_index_scores_mq' if wl.Tq >= 16 else 'k_index_scores'} + top-k)")
         intensity = costs[f"{dom}_flops"] / costs[f"{dom}_bytes"]
         roof = {"bound": "mfma", "achieved": calls[dom]["TFLOP_per_s"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": calls[dom]["mfma_frac"], "traffic": measured_traffic(wl.name, dom), "kernel": kern,
@@ -697,14 +699,14 @@ def main():
         if w2.mode == "csa":
             e2["index_ms"] = cg2["index"]
             e2["index_stats"] = t2["calls_stats"]["index"]
-            if w2.Tq >= 16:
-                # a prefill chunk's scores are a contraction over keys held in LDS for 16 query rows:
-                # reported against bf16 MFMA (keys cross HBM about once per chunk, not once per row)
+            if w2.Tq > 1:
+                # several query tokens per sequence score the same keys, which cross HBM once per
+                # sequence (prefill: once per chunk): a contraction, reported against bf16 MFMA with
+                # its HBM rate beside
                 e2["index_TFLOP_per_s"] = c2["index_flops"] / (cg2["index"] * 1e-3) / 1e12
                 e2["index_mfma_frac"] = e2["index_TFLOP_per_s"] / BF16_PEAK_TFLOPS
-            else:
-                e2["index_GB_per_s"] = c2["index_bytes"] / (cg2["index"] * 1e-3) / 1e9
-                e2["index_hbm_frac"] = e2["index_GB_per_s"] / HBM_PEAK_GBS
+            e2["index_GB_per_s"] = c2["index_bytes"] / (cg2["index"] * 1e-3) / 1e9
+            e2["index_hbm_frac"] = e2["index_GB_per_s"] / HBM_PEAK_GBS
             e2["index_compress_ms"] = cg2["index_compress"]
         if w2.reuse > 0:
             tr = time_reuse(w2, max(10, args.steps // 2), args.warmup, torch)
