@@ -187,6 +187,7 @@ def _keys_cache(B, cap, fp8, seed, n_valid, pos0, window=8, stride=4):
     (3, 4, 64, 20000, [20000, 19990, 7], True, 1024, "end"),   # 4 rows per block, fp8, two-stage, < k visible
     (2, 4, 64, 5000, [5000, 4000], False, 512, "causal"),      # 4 rows per block, bf16, different counts per row
     (2, 2, 24, 3000, [3000, 2999], True, 300, "causal"),       # 2 rows per block, heads not a multiple of 16
+    (4, 4, 40, 70000, [70000, 69000, 30000, 900], False, 1024, "end"),  # 4 rows per block, bf16, 276-block grid (4-deep ring), two-stage
 ])
 def test_index_topk_parity(B, Tq, Hi, cap, n_valid, fp8, topk, qpos_of):
     d = ci.Draw(200 + cap, "cpu")
