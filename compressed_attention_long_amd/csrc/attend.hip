@@ -541,7 +541,7 @@ __global__ void __launch_bounds__(AttShape<NP>::NT) k_attend(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t tb2[kTR * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t tb3[kTR * kPitch];
   __shared__ __attribute__((aligned(16))) int32_t idxl[CSA ? kAttIdxMax : 4];   // the split's top-k indices
-  __shared__ __attribute__((aligned(16))) uint32_t pbuf[2][NP][2][kWave][2];   // weights P (bf16), by parity
+  __shared__ __attribute__((aligned(16))) float pbuf[2][NP][2][kWave][4];   // weights P (fp32), by parity
   __shared__ float mref[2][NP][2][16];          // the producing wave's reference of those weights
   __shared__ __attribute__((aligned(4))) uint8_t tvalid[4][kTR];
   __shared__ f32x2 rtab[kD / 2];                // (cos, sin) of q_pos * inv_freq[i], fp64-evaluated
@@ -776,17 +776,18 @@ __global__ void __launch_bounds__(AttShape<NP>::NT) k_attend(AttendArgs a) {
 
   // ---- online softmax state.  Lane (n, g) of a wave works for head n.  Two references per
   // wave, both integers in log2 units, so that moving weights between them is an exact
-  // power-of-two scaling of bf16 values:
+  // power-of-two scaling:
   //  * m_own, for the weights of this wave's own rows (16h .. 16h + 15 of each tile): it starts
   //    at the first tile's maximum (rounded up) and moves only when a tile's maximum exceeds it
-  //    by more than kRescale, so a dominant row gets weight 2^(s - m_own) <= 1 exactly rounded;
-  //    l_own sums those weights in fp32 (for lse);
+  //    by more than kRescale, so weights stay below 2^kRescale; l_own sums them in fp32 (for lse);
   //  * m_acc, for this wave's P V accumulators, which take the weights of both waves of the
   //    pair, each rescaled from its producer's reference by an exact power of two; it moves
-  //    lazily the same way.  n_acc sums the weights exactly as they enter the product (bf16)
-  //    and normalises the output, so the rounding of a dominant weight cancels between
-  //    numerator and denominator.  Both waves of a pair see the same weights and references,
-  //    so they hold the same m_acc and n_acc.
+  //    lazily the same way.  The weights pass between the waves in fp32 and enter the P V
+  //    product as bf16 hi + lo (fp8 rows: weight x row scale), so they keep about 16 bits
+  //    instead of 8: with 8, a flat softmax over a few hundred rows puts the largest output
+  //    error near 1 % of the output's RMS.  n_acc sums the weights and normalises the output.
+  //    Both waves of a pair see the same weights and references, so they hold the same m_acc
+  //    and n_acc.
   // The sink joins once, in the epilogue or in the split merge.
   float m_own = kNegBig, l_own = 0.f;
   float m_acc = kNegBig, n_acc = 0.f;
@@ -845,7 +846,7 @@ __global__ void __launch_bounds__(AttShape<NP>::NT) k_attend(AttendArgs a) {
       pv[i] = sv[i] > kNegBig ? fast_exp2(sv[i] - m_own) : 0.f;
       l_own += pv[i];
     }
-    *reinterpret_cast<u32x2*>(&pbuf[par][p][h][lane][0]) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+    *reinterpret_cast<f32x4*>(&pbuf[par][p][h][lane][0]) = f32x4{pv[0], pv[1], pv[2], pv[3]};
     if (g == 0) mref[par][p][h][n] = m_own;
   };
   // 2^k for an integer k (exact); 0 far below the range
@@ -870,33 +871,34 @@ __global__ void __launch_bounds__(AttShape<NP>::NT) k_attend(AttendArgs a) {
       }
       m_acc = m_new;
     }
-    // the producers' weights on this wave's reference: exact power-of-two rescaling of bf16
+    // the producers' weights on this wave's reference: exact power-of-two rescaling
     const float f0 = pow2i(r0 - m_acc), f1 = pow2i(r1 - m_acc);
-    const u32x2 pa = *reinterpret_cast<const u32x2*>(&pbuf[par][p][0][lane][0]);
-    const u32x2 pb = *reinterpret_cast<const u32x2*>(&pbuf[par][p][1][lane][0]);
     float w[8];
+    {
+      const f32x4 pa = *reinterpret_cast<const f32x4*>(&pbuf[par][p][0][lane][0]);
+      const f32x4 pb = *reinterpret_cast<const f32x4*>(&pbuf[par][p][1][lane][0]);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      w[2 * k] = bf16lo_to_f32(pa[k]) * f0;
-      w[2 * k + 1] = bf16hi_to_f32(pa[k]) * f0;
-      w[4 + 2 * k] = bf16lo_to_f32(pb[k]) * f1;
-      w[4 + 2 * k + 1] = bf16hi_to_f32(pb[k]) * f1;
+      for (int i = 0; i < 4; ++i) { w[i] = pa[i] * f0; w[4 + i] = pb[i] * f1; }
     }
     n_acc += ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
     const int L = lane & 15;
     const uint16_t* v0p = buf + (4 * g + (L >> 2)) * kPitch + 256 * h + 4 * (L & 3);
     const uint16_t* v1p = buf + (16 + 4 * g + (L >> 2)) * kPitch + 256 * h + 4 * (L & 3);
     if constexpr (!F8) {
-      u32x4 pw;
+      u32x4 pw, pl;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) pw[k] = pack_bf16x2(w[2 * k], w[2 * k + 1]);   // exact
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+      for (int k = 0; k < 4; ++k) {
+        pw[k] = pack_bf16x2(w[2 * k], w[2 * k + 1]);
+        pl[k] = pack_bf16x2(w[2 * k] - bf16lo_to_f32(pw[k]), w[2 * k + 1] - bf16hi_to_f32(pw[k]));
+      }
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pw), pfl = __builtin_bit_cast(bf16x8, pl);
 #pragma unroll
       for (int db = 0; db < 16; ++db) {
         const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0p + 16 * db));
         const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1p + 16 * db));
         const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pfl, acc[db], 0, 0, 0);
       }
     } else {
 #pragma unroll

@@ -178,12 +178,17 @@ def check_scores(s_gpu: np.ndarray, s_ora: np.ndarray, vis: np.ndarray, what: st
 
 
 def lse_tolerance(q: np.ndarray, q_pos: int, X: np.ndarray, scale: float, inv_freq: np.ndarray) -> np.ndarray:
-    """Per-head lse bar: LSE_TOL + 512 u * scale * max_u sum_c |q'_c x_uc| (see the module docstring)."""
+    """Per-head lse bar: LSE_TOL + 512 u * scale * max_u sum_c |q'_c x_uc| (see the module docstring).
+
+    With more than 64 rotated dims the rotated query channels below 448 are rounded to
+    bf16 (unit roundoff 2^-8) before the product: those channels add 2^-8 |q'_c x_uc|."""
     qr = O.rope(q, q_pos, inv_freq)
     if X.shape[0] == 0:
         return np.full(q.shape[0], LSE_TOL)
     D = q.shape[-1]
-    return LSE_TOL + D * U32 * abs(scale) * (np.abs(qr) @ np.abs(X).T).max(axis=1)
+    w = np.full(D, D * U32)
+    w[D - 2 * len(inv_freq):D - 64] += 2.0 ** -8
+    return LSE_TOL + abs(scale) * ((np.abs(qr) * w) @ np.abs(X).T).max(axis=1)
 
 
 def check_lse(lse_gpu: np.ndarray, lse_ora: np.ndarray, tol: np.ndarray, what: str = ""):

@@ -49,6 +49,9 @@ def inv_freq_pair(R=64, yarn=False):
     (8, 4, "fp8", 2, 333, 0, 64),        # fp8 cache, per-64 scales
     (128, 128, "fp8", 1, 5, 2, 64),
     (8, 4, "bf16", 1, 50, 0, 0),         # no rotation
+    (8, 4, "bf16", 2, 77, 1, 128),       # wider rotations
+    (128, 128, "fp8", 2, 5, 0, 512),
+    (2, 2, "fp4", 2, 300, 2, 2),
     (8, 4, "bf16", 2, 37, 3, "yarn"),    # the model's table (YaRN 16 over 65,536), positions near 1M
     (128, 128, "fp8", 2, 5, 0, "yarn"),
     (1, 1, "bf16", 2, 60, 1, "yarn"),
@@ -269,7 +272,7 @@ def test_topk_clustered_scores():
 # ---------------------------------------------------------------- attention
 
 def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, qmul, seed, out_dtype="fp32",
-                 win_start=None, kv_gain=None, pos_base=1, yarn=False):
+                 win_start=None, kv_gain=None, pos_base=1, yarn=False, R=64):
     d = ci.Draw(seed, "cpu")
     q = d.normal((B, Tq, H, 512), std=qmul / math.sqrt(512))
     sink = d.normal((H,), dtype=torch.float32)
@@ -303,7 +306,7 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
     win = ops.Cache(wt.to(DEV), torch.tensor([win_cap] * B, dtype=torch.int32, device=DEV),
                     torch.tensor(wpos0, dtype=torch.int64, device=DEV), 1, 1)
     q_pos = torch.tensor(qp, dtype=torch.int64, device=DEV)
-    fg, fo = inv_freq_pair(64, yarn)
+    fg, fo = inv_freq_pair(R, yarn) if R else (None, np.zeros(0))
     odt = torch.float32 if out_dtype == "fp32" else torch.bfloat16
     out = torch.empty((B, Tq, H, 512), dtype=odt, device=DEV)
     lse = torch.empty((B, Tq, H), dtype=torch.float32, device=DEV)
@@ -318,10 +321,10 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
                 idx_np[b, t, :take] = np.sort(rng.choice(nvis, size=take, replace=False))
         idx = torch.from_numpy(idx_np).to(DEV)
         ws = ops.workspace(ops.csa_attend_workspace_bytes(B, Tq, H, topk, W), DEV)
-        ops.csa_attend(q.to(DEV), q_pos, kv, idx, win, W, sink.to(DEV), fg, 64, scale, out, lse, ws)
+        ops.csa_attend(q.to(DEV), q_pos, kv, idx, win, W, sink.to(DEV), fg, R, scale, out, lse, ws)
     else:
         ws = ops.workspace(ops.hca_attend_workspace_bytes(B, Tq, H, cap, W), DEV)
-        ops.hca_attend(q.to(DEV), q_pos, kv, win, W, sink.to(DEV), fg, 64, scale, out, lse, ws)
+        ops.hca_attend(q.to(DEV), q_pos, kv, win, W, sink.to(DEV), fg, R, scale, out, lse, ws)
     torch.cuda.synchronize()
     og, lg = np64(out), lse.cpu().numpy()
     worst = 0.0
@@ -395,6 +398,22 @@ def test_attend_parity_yarn_near_1m(mode, cap, n_valid, topk):
     pos_base = 1048576 - cap * (4 if mode == "csa" else 128) - 2000
     _attend_case(mode, 2, 1, 128, cap, n_valid, False, topk, 128, 129, scale, 1.0, seed=61, pos_base=pos_base,
                  yarn=True)
+
+
+@pytest.mark.parametrize("mode,B,Tq,H,cap,n_valid,fp8,topk,R", [
+    ("csa", 2, 1, 128, 3000, [3000, 2000], False, 1024, 0),     # no rotation: the query is used as stored
+    ("csa", 2, 1, 128, 3000, [3000, 2000], True, 1024, 2),      # one rotated pair
+    ("csa", 2, 1, 128, 3000, [3000, 2000], False, 1024, 128),   # rotated dims below 448 (bf16 query part)
+    ("csa", 4, 64, 64, 600, [600] * 4, False, 200, 512),        # every dim rotated, multi-row block
+    ("csa", 4, 128, 128, 600, [600, 599, 400, 300], True, 200, 96),
+    ("hca", 2, 1, 128, 700, [700, 300], False, 0, 0),
+    ("hca", 2, 256, 128, 300, [300, 250], "fp4", 0, 256),
+])
+def test_attend_parity_rope_widths(mode, B, Tq, H, cap, n_valid, fp8, topk, R):
+    """Rotated widths other than the model's 64: none, one pair, and wider ones whose
+    rotated channels reach below 448 (the query part there is carried in bf16)."""
+    _attend_case(mode, B, Tq, H, cap, n_valid, fp8, topk, 128, 129 if Tq == 1 else 256, 1 / math.sqrt(512),
+                 2.0, seed=800 + R + Tq, R=R)
 
 
 def test_attend_window_cut_by_stream_start():
