@@ -16,7 +16,7 @@
 //  * scores are computed transposed, S^T = K Q^T (M = rows, N = heads, K = channels):
 //    wave h of a pair scores rows 16h .. 16h + 15 of a tile for its pair's heads, so every
 //    accumulator lane belongs to one head;
-//  * the two waves of a pair exchange their tiles' maxima and their softmax weights P
+//  * the two waves of a pair exchange their tiles' maxima and their softmax weights P (fp32)
 //    through LDS; then each computes O^T = V^T P^T (M = channels, N = heads, K = rows) over
 //    all 32 rows for half the channels (wave h: channels 256h .. 256h + 255), so each wave
 //    holds 64 accumulator registers instead of 128 and a block of eight waves covers 64
@@ -29,8 +29,9 @@
 //  * bf16 rows reach LDS by direct DMA; fp8 and fp4 entry rows go through registers.  fp4
 //    codes times their power-of-two scale are exact in bf16.  fp8 rows are staged as their
 //    exact codes and the per-64-channel scales are applied in fp32: to the scores per
-//    channel block, and to the weights per channel block in P V, carried as bf16 hi + lo
-//    parts so that the scaled weights keep about 16 bits;
+//    channel block, and to the weights per channel block in P V;
+//  * the weights enter P V as bf16 hi + lo parts (fp8 rows: weight x row scale), so they
+//    keep about 16 bits;
 //  * the sink joins the denominator once, in the epilogue (one split) or the split merge;
 //  * lazy rescaling: the reference maximum moves only when a tile exceeds it by 2^8;
 //  * several splits of the row set run in parallel when the query rows alone cannot
