@@ -372,6 +372,12 @@ def _attend_case(mode, B, Tq, H, cap, n_valid, kv_fp8, topk, W, win_cap, scale, 
      1 / math.sqrt(512), 2.0),
     ("hca", 8, 1, 128, 2000, [2000, 1999, 1500, 1000, 800, 700, 600, 500], False, 0, 128, 129,
      1 / math.sqrt(512), 2.0),
+    # the largest top-k the indexer returns (4,096): bf16 with 256 heads; fp8 over several splits
+    # whose staged index lists stay within the per-split limit
+    ("csa", 1, 1, 256, 6000, [6000], False, 4096, 128, 129, 1 / math.sqrt(512), 1.0),
+    ("csa", 2, 1, 64, 6000, [6000, 5000], True, 4096, 128, 129, 1 / math.sqrt(512), 4.0),
+    ("hca", 1, 2, 1024, 300, [300], False, 0, 128, 129, 1 / math.sqrt(512), 1.0),       # the largest head count
+    ("csa", 1, 1, 1000, 2000, [2000], "fp4", 1024, 128, 129, 1 / math.sqrt(512), 1.0),  # heads not a multiple of 64
 ])
 def test_attend_parity(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul):
     _attend_case(mode, B, Tq, H, cap, n_valid, fp8, topk, W, win_cap, scale, qmul, seed=400 + cap + H)
