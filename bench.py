@@ -611,8 +611,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs the path on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU sharding is described in DESIGN.md, not implemented)"}))
+        print(json.dumps({"error": "the library runs the path on one GPU only; --gpus must be 1 "
+                                   "(sharding across GPUs is not implemented)"}))
         sys.exit(2)
 
     import torch

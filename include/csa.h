@@ -50,7 +50,7 @@ extern "C" {
 /* Status codes. */
 #define CSA_OK          0
 #define CSA_EINVAL     -1   /* null pointer, bad size, misaligned pointer, topk > capacity ... */
-#define CSA_ENOTSUP    -2   /* a dtype or shape combination this build does not implement */
+#define CSA_ENOTSUP    -2   /* a dtype or shape combination the library does not implement */
 #define CSA_EWORKSPACE -3   /* workspace missing or smaller than *_workspace_bytes() */
 #define CSA_EHIP       -4   /* a kernel launch reported a HIP error */
 
