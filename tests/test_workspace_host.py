@@ -17,13 +17,21 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(os.path.dirname(HERE), "compressed_attention_long_amd", "csrc")
 
 
-def test_workspace_carving_fits(tmp_path):
+@pytest.mark.parametrize("sanitize", [False, True])
+def test_workspace_carving_fits(tmp_path, sanitize):
+    """The plan sweep, built plain and with the host compiler's address and undefined-behaviour
+    sanitizers (host code only: the driver includes no device code)."""
     cxx = shutil.which("g++") or shutil.which("c++")
     if cxx is None:
         pytest.skip("no host C++ compiler")
     exe = tmp_path / "carving"
-    subprocess.run([cxx, "-std=c++17", "-O1", "-Wall", "-I", CSRC, os.path.join(HERE, "host", "workspace_carving.cpp"),
-                    "-o", str(exe)], check=True)
+    flags = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"] if sanitize else []
+    build = subprocess.run([cxx, "-std=c++17", "-O1", "-Wall", *flags, "-I", CSRC,
+                            os.path.join(HERE, "host", "workspace_carving.cpp"), "-o", str(exe)],
+                           capture_output=True, text=True)
+    if sanitize and build.returncode != 0:
+        pytest.skip("the host compiler cannot build with sanitizers here: " + build.stderr[-300:])
+    assert build.returncode == 0, build.stderr[-4000:]
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout[-4000:]
     assert "0 failures" in r.stdout
